@@ -1,0 +1,39 @@
+"""CPU oracle for the branch-parallel scoring path -- TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, obviously correct NumPy float64 statement of what the path
+computes: the proposal-tree pack, tree-masked GQA attention with RoPE at
+semantic positions, predecessor-row readout and the E2E-TV surrogate with its
+gradient. It shares no code with the HIP library and imports nothing from it;
+the only shared module is ``specgen`` (seeded inputs, no method arithmetic).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package. The product path never calls it.
+
+Sources, cited by page title and section throughout:
+  * [SpecOPD paper page] "SpecOPD: Branch-Parallel On-Policy Distillation for
+    Speculative Decoding" (thelatestinai.com paper page): abstract and the
+    captions of Figures 2, 3, 4 and 13.
+  * [SpecOPD notes page] "SpecOPD: independent supervision branches and
+    acceptance-prefix optimization" (daiwk auto-research notes): sections
+    "Equations", "Inputs and code mapping" and "Checks, negative controls,
+    and limits".
+
+Every function here is pinned by a ``-m "not gpu"`` test against something
+other than itself (a hand-worked example, a closed form, brute force, a library
+routine or finite differences); none is "parity unpinned".
+"""
+from .pack_ref import pack_ref, parents_ref, visible_ref, visible_intervals_ref  # noqa: F401
+from .attn_ref import (  # noqa: F401
+    brute_force_branch_ref,
+    causal_attn_ref,
+    readout_ref,
+    rope_ref,
+    tree_attn_ref,
+)
+from .e2etv_ref import (  # noqa: F401
+    e2etv_coef_ref,
+    e2etv_grad_ref,
+    e2etv_loss_ref,
+    e2etv_ref,
+    e2etv_row_stats_ref,
+)
