@@ -1,0 +1,240 @@
+/*
+ * spec_tree.h -- C ABI of the branch-parallel scoring path (MI355X / gfx950).
+ *
+ * Three calls make up the path, each enqueued on the caller's HIP stream:
+ *   spec_tree_pack      proposal-tree packer (host checks + device expand)
+ *   spec_tree_attn_fwd  tree-masked GQA attention, RoPE at semantic positions,
+ *                       optional predecessor-row readout
+ *   spec_e2etv_fwd_bwd  E2E-TV overlap, prefix-product loss and its gradient
+ *                       with respect to the draft logits
+ *
+ * Sources, cited by page title and section:
+ *   [SpecOPD paper page]  "SpecOPD: Branch-Parallel On-Policy Distillation for
+ *                         Speculative Decoding" (thelatestinai.com paper page)
+ *   [SpecOPD notes page]  "SpecOPD: independent supervision branches and
+ *                         acceptance-prefix optimization" (daiwk auto-research
+ *                         notes)
+ *
+ * Conventions shared by every call
+ *   - All pointers named d_* are device pointers; h_* are host pointers.
+ *   - The caller allocates and owns every buffer. The library never allocates
+ *     or frees device memory; scratch memory comes from a caller workspace.
+ *     Passing d_mem / d_work == NULL is a size query: the call validates what
+ *     it can, writes the byte count and returns SPEC_OK without touching the
+ *     GPU (no HIP call at all).
+ *   - All device work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     default stream). There is no host synchronisation inside any call
+ *     except that spec_tree_pack's small host-to-device copy reads its host
+ *     staging before returning. Device buffers must stay valid until the
+ *     enqueued work completes.
+ *   - Arguments are checked before anything is enqueued; on any error nothing
+ *     is launched and spec_last_error() describes the problem (thread-local).
+ *   - Tensors are dense and row-major. Device buffers must be 16-byte aligned.
+ *   - The library holds no state between calls; calls on different streams
+ *     may run concurrently as long as their buffers are disjoint.
+ */
+#ifndef SPEC_TREE_H
+#define SPEC_TREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_TREE_ABI_VERSION 1
+#define SPEC_MAX_BRANCH_LEN 64 /* largest supported branch width W_b */
+
+typedef enum spec_status {
+  SPEC_OK = 0,
+  SPEC_ERR_INVALID_ARG = 1, /* a NULL / misaligned pointer or an out-of-range value */
+  SPEC_ERR_UNSUPPORTED = 2, /* a valid request outside what the kernels implement */
+  SPEC_ERR_WORKSPACE = 3,   /* the workspace / layout buffer is too small */
+  SPEC_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} spec_status;
+
+typedef enum spec_dtype {
+  SPEC_F32 = 0,  /* IEEE binary32 */
+  SPEC_BF16 = 1  /* bfloat16 (upper half of a binary32) */
+} spec_dtype;
+
+typedef void *spec_stream; /* a hipStream_t */
+
+/*
+ * Packed proposal-tree layout, filled by spec_tree_pack.
+ *
+ * Packed order (rows and columns of the tree mask share it, [SpecOPD paper
+ * page, Figure 3]): tree by tree; inside a tree the trunk rows 0..T-1 first,
+ * then the tree's branches in ascending anchor order (ties keep the caller's
+ * order), each branch's rows y_{b,1}..y_{b,W_b-1} in depth order. The terminal
+ * sample y_{b,W_b} has no row ([SpecOPD paper page, Figure 3]: terminal
+ * samples use predecessor readouts and need no query rows), so
+ *   N = n_rows  = sum_t T_t + sum_b (W_b - 1)
+ *   R = n_steps = sum_b W_b   (supervised steps = E2E-TV rows).
+ * Supervised steps stay in caller branch order: branch b's steps are
+ * step_off[b] .. step_off[b+1]-1, step i (1-based) at step_off[b] + i - 1.
+ *
+ * Every device pointer points into the caller's d_mem buffer; all arrays are
+ * int32. "local" anchors are zero-based trunk indices of the branch's tree
+ * ([SpecOPD notes page, "Inputs and code mapping"]).
+ */
+typedef struct spec_tree_layout {
+  /* host scalars */
+  int32_t n_trees;
+  int32_t n_branches;      /* B */
+  int32_t max_branch_len;  /* max_b W_b (0 when B == 0) */
+  int32_t max_pos;         /* largest semantic position of any row */
+  int64_t n_rows;          /* N */
+  int64_t n_steps;         /* R */
+  int32_t n_attn_items;    /* query blocks in attn_items */
+  int32_t reserved0;
+
+  /* per tree */
+  int32_t *tree_off;        /* [n_trees+1] first packed row of each tree; last = N */
+  /* per packed row [N] */
+  int32_t *row_tree;        /* tree index */
+  int32_t *row_branch;      /* branch index b, -1 for trunk rows */
+  int32_t *row_anchor;      /* local anchor a_b, -1 for trunk rows */
+  int32_t *row_pos;         /* semantic position: j for trunk token j, a_b+i for y_{b,i} */
+  int32_t *row_depth;       /* 0 for trunk rows, i for y_{b,i} */
+  int32_t *row_trunk_hi;    /* last visible trunk row (packed index): itself, or tree_off+a_b */
+  int32_t *row_branch_lo;   /* first visible own-branch row; r+1 (empty) for trunk rows */
+  /* per branch [B] (caller order) */
+  int32_t *branch_tree;
+  int32_t *branch_anchor;   /* local anchor a_b */
+  int32_t *branch_len;      /* W_b */
+  int32_t *branch_off;      /* packed row of y_{b,1} (for W_b == 1: the next packed row) */
+  int32_t *step_off;        /* [B+1] exclusive prefix sum of W_b */
+  int32_t *branch_order;    /* [B] branch indices in packed order */
+  /* per supervised step [R] */
+  int32_t *step_branch;     /* branch of the step */
+  int32_t *step_pred_row;   /* packed row whose output predicts the step's sample */
+  int32_t *step_sample_row; /* packed row of the sample y_{b,i}; -1 for the terminal sample */
+  /* library-internal attention schedule [n_attn_items * 8] */
+  int32_t *attn_items;
+} spec_tree_layout;
+
+/*
+ * spec_tree_pack -- build the packed proposal tree.
+ *
+ * Defines: [SpecOPD paper page, Figure 2] (a shared reference trunk with
+ * sampled continuations attached at their anchors), [SpecOPD paper page,
+ * Figure 3] (one packed order; each row sees itself and its ancestors;
+ * terminal samples need no query row) and [SpecOPD notes page, "Equations"]
+ * (histories h_{b,i} = (x_{<=a_b}, y_{b,<i}); the anchor row predicts y_{b,1},
+ * the row of y_{b,i-1} predicts y_{b,i}; semantic position a_b + i).
+ *
+ * Arguments (all host arrays are read before the call returns):
+ *   n_trees       >= 1 trees packed back to back.
+ *   h_trunk_len   [n_trees] trunk length T_t >= 1.
+ *   h_n_branches  [n_trees] branches per tree (>= 0); B = their sum.
+ *   h_anchor      [B] local zero-based anchor, 0 <= a_b < T_t, tree t's
+ *                 branches consecutive, trees in order.
+ *   h_branch_len  [B] branch width 1 <= W_b <= SPEC_MAX_BRANCH_LEN.
+ *   d_mem         device buffer of *mem_bytes bytes for the layout arrays, or
+ *                 NULL for a size query (then only the scalars and *mem_bytes
+ *                 are written).
+ *   mem_bytes     in: size of d_mem; out: bytes required.
+ *   layout        out: scalars always; device pointers when d_mem != NULL.
+ * Errors: SPEC_ERR_INVALID_ARG for NULL required pointers or out-of-range
+ * values (N and R must fit in int32), SPEC_ERR_WORKSPACE when *mem_bytes is
+ * too small, SPEC_ERR_HIP when the copy or the expand kernel fails to enqueue.
+ */
+spec_status spec_tree_pack(int32_t n_trees, const int32_t *h_trunk_len,
+                           const int32_t *h_n_branches, const int32_t *h_anchor,
+                           const int32_t *h_branch_len, void *d_mem, size_t *mem_bytes,
+                           spec_tree_layout *layout, spec_stream stream);
+
+/*
+ * spec_tree_attn_fwd -- tree-masked GQA attention over a packed tree.
+ *
+ * Defines: [SpecOPD paper page, Figure 3] (packed queries share the trunk K/V
+ * under a tree mask restricting each row to itself and its ancestors) and
+ * [SpecOPD notes page, "Equations"] (only the reference prefix through the
+ * anchor and the branch's own predecessors are visible; RoPE uses the
+ * semantic position a_b + i, not the packed offset; the readout for step
+ * (b,i) is the output row of its predecessor, never the sample's own row).
+ *
+ * For packed row r and query head h (KV head g = h / (Hq/Hkv)):
+ *   O[r,h] = sum_{c in vis(r)} softmax_c(scale * <rope(q[r,h], pos r), rope(k[c,g], pos c)>) v[c,g]
+ *   vis(r) = [tree_off[t], row_trunk_hi[r]]  U  [row_branch_lo[r], r]
+ * RoPE is rotate-half: dimension j pairs with j + D/2 at angle
+ * pos * rope_base^(-2j/D). Accumulation is float32; O is rounded to the input
+ * dtype (round-to-nearest-even for bf16).
+ *
+ * Arguments:
+ *   layout        from spec_tree_pack (device arrays must be resident).
+ *   n_heads_q     Hq >= 1; n_heads_kv: Hkv >= 1 with Hq % Hkv == 0.
+ *   head_dim      D in {32, 64, 128}.
+ *   dtype         SPEC_BF16 (MFMA path) or SPEC_F32 (exact float32 path).
+ *   d_q           [N, Hq, D]; d_k, d_v: [N, Hkv, D], pre-RoPE, dtype `dtype`.
+ *   rope_base     > 0 (e.g. 10000).
+ *   softmax_scale <= 0 selects 1/sqrt(D).
+ *   d_out         [N, Hq, D] dtype, written for every packed row.
+ *   d_readout     optional [R, Hq, D] dtype: readout[s] = O[step_pred_row[s]].
+ *   d_work        workspace of *work_bytes bytes, or NULL for a size query.
+ * Data precondition (not checked): Q, K, V are finite.
+ * Errors: SPEC_ERR_INVALID_ARG, SPEC_ERR_UNSUPPORTED (head_dim / dtype / GQA
+ * ratio outside the kernels), SPEC_ERR_WORKSPACE, SPEC_ERR_HIP.
+ */
+spec_status spec_tree_attn_fwd(const spec_tree_layout *layout, int32_t n_heads_q,
+                               int32_t n_heads_kv, int32_t head_dim, spec_dtype dtype,
+                               const void *d_q, const void *d_k, const void *d_v,
+                               float rope_base, float softmax_scale, void *d_out,
+                               void *d_readout, void *d_work, size_t *work_bytes,
+                               spec_stream stream);
+
+/*
+ * spec_e2etv_fwd_bwd -- E2E-TV surrogate, loss and gradient w.r.t. the draft.
+ *
+ * Defines: [SpecOPD notes page, "Equations"]
+ *   alpha_s = sum_v min(q_s(v), p_s(v))          (full vocabulary)
+ *   L = 1 - inv_norm * sum_b sum_{j=1..W_b} prod_{i<=j} alpha_{b,i}
+ * with q = softmax(draft row), p = softmax(teacher row); samples and teacher
+ * are held fixed when differentiating, and teacher mass outside the draft
+ * support is kept, never renormalised. [SpecOPD notes page, "Inputs and code
+ * mapping"]: logits are aligned by history (row s = step s of the layout),
+ * low precision is promoted to float32, inactive draft support may be NaN,
+ * the teacher must be finite.
+ *
+ * Gradient written (float32): grad[s,u] = c_s * q_s(u) * (1[q_s(u) < p_s(u)] - S_s)
+ * with S_s = sum_{v: q_s(v) < p_s(v)} q_s(v) and c_s = dL/d alpha_s =
+ * -inv_norm * A_{b,i-1} * G_{b,i} (prefix products A, suffix sums G).
+ *
+ * Arguments:
+ *   layout        from spec_tree_pack (uses n_steps, n_branches, step_off).
+ *   vocab         V >= 1.
+ *   logit_dtype   SPEC_BF16 or SPEC_F32.
+ *   d_draft       [R, V] draft logits z; NaN or -inf mean inactive support (q = 0).
+ *   d_teacher     [R, V] teacher logits y, all finite.
+ *   inv_norm      <= 0 selects 1/R; otherwise used as given (e.g. a
+ *                 normaliser computed across ranks).
+ *   d_alpha       [R] float32 out.
+ *   d_loss        [1] float32 out.
+ *   d_grad        optional [R, V] float32 out (NULL: forward only).
+ *   d_work        workspace of *work_bytes bytes, or NULL for a size query.
+ * Data preconditions (not checked; violations give NaN): teacher finite, at
+ * least one active draft entry per row.
+ * Errors: SPEC_ERR_INVALID_ARG, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP.
+ */
+spec_status spec_e2etv_fwd_bwd(const spec_tree_layout *layout, int64_t vocab,
+                               spec_dtype logit_dtype, const void *d_draft,
+                               const void *d_teacher, float inv_norm, float *d_alpha,
+                               float *d_loss, float *d_grad, void *d_work, size_t *work_bytes,
+                               spec_stream stream);
+
+/* Human-readable name of a status code (static string). */
+const char *spec_status_string(spec_status status);
+
+/* Description of the last error raised on the calling thread ("" if none). */
+const char *spec_last_error(void);
+
+/* SPEC_TREE_ABI_VERSION of the loaded library. */
+int32_t spec_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_TREE_H */

@@ -23,3 +23,19 @@ def golden():
         with open(os.path.join(GOLDEN, name)) as f:
             return json.load(f)
     return load
+
+
+def _gpu_ready():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def pytest_collection_modifyitems(config, items):
+    gpu_items = [it for it in items if "gpu" in it.keywords]
+    if gpu_items and not _gpu_ready():
+        skip = pytest.mark.skip(reason="no GPU visible to torch")
+        for it in gpu_items:
+            it.add_marker(skip)

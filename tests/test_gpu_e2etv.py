@@ -1,0 +1,145 @@
+"""GPU parity: spec_e2etv_fwd_bwd against the float64 oracle."""
+import numpy as np
+import pytest
+
+from _util import (ALPHA_RTOL, LOSS_ATOL, LOSS_RTOL, Case, check_grad_rows, from_device, say,
+                   to_device, widen)
+from oracle import e2etv_coef_ref, e2etv_grad_ref, e2etv_loss_ref, e2etv_ref, e2etv_row_stats_ref
+from specgen import CONFIGS, gen_logit_rows, small_config
+
+pytestmark = pytest.mark.gpu
+
+
+def _pack(s):
+    import tree_attention_spec_amd as tas
+    return tas.spec_tree_pack(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"])
+
+
+def _run(tree, z, y, inv_norm=0.0, grad=True):
+    import torch
+    import tree_attention_spec_amd as tas
+    a, l, g = tas.spec_e2etv_fwd_bwd(tree, z, y, inv_norm=inv_norm, grad=grad)
+    torch.cuda.synchronize()
+    return a, l, g
+
+
+def _full_compare(case, z, y, inv_norm=None):
+    tree = _pack(case.s)
+    a, l, g = _run(tree, to_device(z), to_device(y), inv_norm or 0.0)
+    zz, yy = widen(z), widen(y)
+    alpha, S, _, _, q, p = e2etv_row_stats_ref(zz, yy)
+    L = e2etv_loss_ref(alpha, case.lay["step_off"], inv_norm)
+    c = e2etv_coef_ref(alpha, case.lay["step_off"], inv_norm)
+    gref = e2etv_grad_ref(q, p, S, c)
+    ga, gl, gg = from_device(a), float(l.item()), from_device(g)
+    arel = np.max(np.abs(ga - alpha) / np.maximum(alpha, 1e-30))
+    lerr = abs(gl - L)
+    gw, nt = check_grad_rows(gg, gref, q, p)
+    say("  alpha rel %.2e, L %.8f vs %.8f, grad rel %.2e (%d near-ties skipped)" % (arel, gl, L, gw, nt))
+    assert arel <= ALPHA_RTOL
+    assert lerr <= max(LOSS_RTOL * abs(L), LOSS_ATOL)
+    assert gw <= 1e-4
+    return ga, gl, gg
+
+
+def test_e2etv_teaching_example(golden):
+    """The pages' teaching pair, through the GPU (vocab 3, -inf draft entry)."""
+    say("e2etv parity: teaching example")
+    gt = golden("teaching_example.json")
+    with np.errstate(divide="ignore"):
+        z = np.log(np.array([gt["draft_probs"]], np.float64)).astype(np.float32)
+        y = np.log(np.array([gt["teacher_probs"]], np.float64)).astype(np.float32)
+    tree = _pack(dict(trunk_len=np.array([4]), n_branches=np.array([1]), anchors=np.array([2], np.int32),
+                      branch_len=np.array([1], np.int32)))
+    a, l, g = _run(tree, to_device(z), to_device(y))
+    assert abs(float(l.item()) - gt["loss"]) < 1e-6
+    assert abs(float(a.item()) - gt["alpha"][0]) < 1e-6
+    assert float(g[0, 2].item()) == 0.0
+
+
+def test_e2etv_tiny_f32():
+    say("e2etv parity: tiny fp32")
+    case = Case(CONFIGS["tiny"])
+    z, y = case.logits()
+    _full_compare(case, z, y)
+
+
+def test_e2etv_equal_and_nan():
+    import torch
+    say("e2etv: q == p and NaN padding")
+    case = Case(small_config("tiny", branches=3, width=5, vocab=1000))
+    z, y = case.logits()
+    tree = _pack(case.s)
+    zt = to_device(z)
+    a, l, g = _run(tree, zt, zt.clone())
+    assert torch.allclose(a, torch.ones_like(a), atol=2e-6, rtol=0)
+    assert abs(float(l.item())) < 2e-6
+    assert torch.count_nonzero(g).item() == 0
+    zn = z.copy()
+    zn[:, 900:] = np.nan
+    zi = z.copy()
+    zi[:, 900:] = -np.inf
+    a1, l1, g1 = _run(tree, to_device(zn), to_device(y))
+    a2, l2, g2 = _run(tree, to_device(zi), to_device(y))
+    assert torch.equal(a1, a2) and torch.equal(l1, l2) and torch.equal(g1, g2)
+    assert torch.count_nonzero(g1[:, 900:]).item() == 0
+    _full_compare(case, zn, y)
+
+
+@pytest.mark.parametrize("vocab", [151936, 50000, 4097])
+def test_e2etv_bf16_rows(vocab):
+    """Variable widths, full vocabulary rows, vector and scalar tails."""
+    say("e2etv parity: bf16 vocab %d" % vocab)
+    cfg = small_config("stress", trunk=500, branches=9, width=16, vocab=vocab)
+    case = Case(cfg)
+    z, y = case.logits()
+    _full_compare(case, z, y)
+    _full_compare(case, z, y, inv_norm=0.01)
+
+
+def test_e2etv_forward_only_and_determinism():
+    import torch
+    case = Case(small_config("gqa8b", trunk=300, branches=5, width=16, vocab=151936))
+    z, y = case.logits()
+    tree = _pack(case.s)
+    zt, yt = to_device(z), to_device(y)
+    a1, l1, g1 = _run(tree, zt, yt)
+    a2, l2, g2 = _run(tree, zt, yt)
+    a3, l3, g3 = _run(tree, zt, yt, grad=False)
+    assert g3 is None
+    assert torch.equal(a1, a2) and torch.equal(l1, l2) and torch.equal(g1, g2)
+    assert torch.equal(a1, a3) and torch.equal(l1, l3)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["gqa8b", "long", "batched", "stress"])
+def test_e2etv_workload_sampled(name):
+    """Full-size workloads; sampled rows for alpha and the gradient, L from all alphas."""
+    import torch
+    say("e2etv parity: %s full size, sampled rows" % name)
+    case = Case(CONFIGS[name])
+    tree = _pack(case.s)
+    z, y = case.logits()
+    zt, yt = to_device(z), to_device(y)
+    case.drop_logits()
+    del z, y
+    a, l, g = _run(tree, zt, yt)
+    del zt, yt
+    R = case.R
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, R - 1], rng.choice(R, size=10, replace=False)]))
+    zs, ys = gen_logit_rows(case.cfg, R, rows)
+    alpha, S, _, _, q, p = e2etv_row_stats_ref(zs.astype(np.float64), ys.astype(np.float64))
+    ga = from_device(a)
+    arel = np.max(np.abs(ga[rows] - alpha) / alpha)
+    # L and c from the GPU's alphas (checked on the sampled rows above)
+    L = e2etv_loss_ref(ga, case.lay["step_off"])
+    c = e2etv_coef_ref(ga, case.lay["step_off"])[rows]
+    gref = e2etv_grad_ref(q, p, S, c)
+    gg = from_device(g[torch.from_numpy(rows).cuda()])
+    gw, nt = check_grad_rows(gg, gref, q, p)
+    say("  alpha rel %.2e, L %.7f vs %.7f, grad rel %.2e (%d near-ties)" % (arel, l.item(), L, gw, nt))
+    assert arel <= ALPHA_RTOL
+    assert abs(l.item() - L) <= max(LOSS_RTOL * abs(L), LOSS_ATOL)
+    assert gw <= 1e-4
+    assert torch.isfinite(g).all()

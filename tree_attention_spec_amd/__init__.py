@@ -1,0 +1,204 @@
+"""Branch-parallel scoring path on MI355X: Python binding of libspec_tree.so.
+
+The three calls mirror the C ABI in ``include/spec_tree.h`` and do argument
+marshalling only: torch provides device memory and the current HIP stream,
+every step of the path runs in the library's HIP kernels.
+
+    tree = spec_tree_pack(trunk_len, n_branches, anchors, branch_len, device="cuda")
+    out, readout = spec_tree_attn_fwd(tree, q, k, v, rope_base=10000.0)
+    alpha, loss, grad = spec_e2etv_fwd_bwd(tree, draft_logits, teacher_logits)
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch  # loads the HIP runtime the library binds to; keep before the library
+
+from . import _lib
+from ._lib import (LAYOUT_ARRAYS, SPEC_BF16, SPEC_F32, SPEC_MAX_BRANCH_LEN, SpecError,  # noqa: F401
+                   spec_tree_layout)
+
+__all__ = ["spec_tree_pack", "spec_tree_pack_query", "spec_tree_attn_fwd", "spec_e2etv_fwd_bwd",
+           "PackedTree", "SpecError", "library"]
+
+_LIB = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libspec_tree.so (raises ImportError if it is not built)."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _lib.load()
+    return _LIB
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int64).astype(np.int32))
+
+
+def _iptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if a.size else None
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SPEC_BF16
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    raise TypeError("tensors must be bfloat16 or float32, got %s" % t.dtype)
+
+
+class PackedTree:
+    """A packed proposal tree: the layout struct plus the device buffer it points into."""
+
+    def __init__(self, layout: spec_tree_layout, mem: torch.Tensor):
+        self.layout = layout
+        self.mem = mem
+
+    n_trees = property(lambda s: s.layout.n_trees)
+    n_branches = property(lambda s: s.layout.n_branches)
+    n_rows = property(lambda s: s.layout.n_rows)
+    n_steps = property(lambda s: s.layout.n_steps)
+    max_branch_len = property(lambda s: s.layout.max_branch_len)
+    max_pos = property(lambda s: s.layout.max_pos)
+    n_attn_items = property(lambda s: s.layout.n_attn_items)
+    device = property(lambda s: s.mem.device)
+
+    def arrays(self) -> dict:
+        """Device int32 views of every layout array, by name."""
+        base = self.mem.data_ptr()
+        words = self.mem.view(torch.int32)
+        out = {}
+        for name, length in LAYOUT_ARRAYS.items():
+            ptr = ctypes.cast(getattr(self.layout, name), ctypes.c_void_p).value
+            n = int(length(self.layout))
+            if ptr is None or n == 0:
+                out[name] = torch.zeros(0, dtype=torch.int32, device=self.mem.device)
+                continue
+            off = (ptr - base) // 4
+            out[name] = words[off:off + n]
+        return out
+
+
+def spec_tree_pack_query(trunk_len, n_branches, anchors, branch_len):
+    """Size query (no GPU work): returns (layout scalars, bytes of the device buffer)."""
+    lib = library()
+    T, nb, a, w = _i32(trunk_len), _i32(n_branches), _i32(anchors), _i32(branch_len)
+    layout = spec_tree_layout()
+    nbytes = ctypes.c_size_t(0)
+    _lib.check(lib, lib.spec_tree_pack(len(T), _iptr(T), _iptr(nb), _iptr(a), _iptr(w), None,
+                                       ctypes.byref(nbytes), ctypes.byref(layout), None))
+    return layout, nbytes.value
+
+
+def spec_tree_pack(trunk_len, n_branches, anchors, branch_len, device=None, mem=None) -> PackedTree:
+    """Pack proposal trees on ``device``; ``mem`` may supply a reusable uint8 buffer."""
+    lib = library()
+    device = torch.device(device if device is not None else "cuda")
+    T, nb, a, w = _i32(trunk_len), _i32(n_branches), _i32(anchors), _i32(branch_len)
+    _, need = spec_tree_pack_query(T, nb, a, w)
+    if mem is None or mem.numel() < need:
+        mem = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    layout = spec_tree_layout()
+    nbytes = ctypes.c_size_t(mem.numel())
+    _lib.check(lib, lib.spec_tree_pack(len(T), _iptr(T), _iptr(nb), _iptr(a), _iptr(w),
+                                       ctypes.c_void_p(mem.data_ptr()), ctypes.byref(nbytes),
+                                       ctypes.byref(layout), ctypes.c_void_p(_stream(device))))
+    return PackedTree(layout, mem)
+
+
+def _attn_call(tree, hq, hkv, D, dt, q, k, v, rope_base, scale, out, readout, work):
+    lib = library()
+    nbytes = ctypes.c_size_t(work.numel() if work is not None else 0)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    return lib.spec_tree_attn_fwd(ctypes.byref(tree.layout), hq, hkv, D, dt, ptr(q), ptr(k), ptr(v),
+                                  float(rope_base), float(scale), ptr(out), ptr(readout), ptr(work),
+                                  ctypes.byref(nbytes),
+                                  ctypes.c_void_p(_stream(q.device)) if q is not None else None), nbytes.value
+
+
+def attn_work_bytes(tree, n_heads_q, n_heads_kv, head_dim, dtype) -> int:
+    lib = library()
+    nbytes = ctypes.c_size_t(0)
+    dt = SPEC_BF16 if dtype == torch.bfloat16 else SPEC_F32
+    _lib.check(lib, lib.spec_tree_attn_fwd(ctypes.byref(tree.layout), n_heads_q, n_heads_kv, head_dim,
+                                           dt, None, None, None, 10000.0, 0.0, None, None, None,
+                                           ctypes.byref(nbytes), None))
+    return nbytes.value
+
+
+def spec_tree_attn_fwd(tree: PackedTree, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                       rope_base: float = 10000.0, softmax_scale: float = 0.0, readout: bool = True,
+                       out: torch.Tensor = None, readout_out: torch.Tensor = None,
+                       work: torch.Tensor = None):
+    """Tree attention. q [N,Hq,D], k/v [N,Hkv,D] (bf16 or fp32, contiguous, on the GPU).
+
+    Returns (out [N,Hq,D], readout [R,Hq,D] or None).
+    """
+    N, hq, D = q.shape
+    hkv = k.shape[1]
+    if k.shape != (N, hkv, D) or v.shape != (N, hkv, D) or N != tree.n_rows:
+        raise ValueError("q/k/v shapes do not match the packed tree")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k and v must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share a dtype")
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    if readout and readout_out is None:
+        readout_out = torch.empty((tree.n_steps, hq, D), dtype=q.dtype, device=q.device)
+    if not readout:
+        readout_out = None
+    if work is None:
+        work = torch.empty(max(attn_work_bytes(tree, hq, hkv, D, q.dtype), 256), dtype=torch.uint8,
+                           device=q.device)
+    st, _ = _attn_call(tree, hq, hkv, D, dt, q, k, v, rope_base, softmax_scale, out, readout_out, work)
+    _lib.check(library(), st)
+    return out, readout_out
+
+
+def e2etv_work_bytes(tree, vocab, dtype) -> int:
+    lib = library()
+    nbytes = ctypes.c_size_t(0)
+    dt = SPEC_BF16 if dtype == torch.bfloat16 else SPEC_F32
+    _lib.check(lib, lib.spec_e2etv_fwd_bwd(ctypes.byref(tree.layout), vocab, dt, None, None, 0.0,
+                                           None, None, None, None, ctypes.byref(nbytes), None))
+    return nbytes.value
+
+
+def spec_e2etv_fwd_bwd(tree: PackedTree, draft: torch.Tensor, teacher: torch.Tensor,
+                       inv_norm: float = 0.0, grad: bool = True, alpha_out=None, loss_out=None,
+                       grad_out=None, work: torch.Tensor = None):
+    """E2E-TV over logits [R, V]. Returns (alpha [R] fp32, loss [1] fp32, grad [R,V] fp32 or None)."""
+    R, V = draft.shape
+    if teacher.shape != (R, V) or R != tree.n_steps:
+        raise ValueError("draft/teacher must be [n_steps, vocab]")
+    if not (draft.is_contiguous() and teacher.is_contiguous()) or draft.dtype != teacher.dtype:
+        raise ValueError("draft and teacher must be contiguous and share a dtype")
+    dt = _dtype_code(draft)
+    dev = draft.device
+    if alpha_out is None:
+        alpha_out = torch.empty(R, dtype=torch.float32, device=dev)
+    if loss_out is None:
+        loss_out = torch.empty(1, dtype=torch.float32, device=dev)
+    if grad and grad_out is None:
+        grad_out = torch.empty((R, V), dtype=torch.float32, device=dev)
+    if not grad:
+        grad_out = None
+    if work is None:
+        work = torch.empty(max(e2etv_work_bytes(tree, V, draft.dtype), 256), dtype=torch.uint8,
+                           device=dev)
+    lib = library()
+    nbytes = ctypes.c_size_t(work.numel())
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    _lib.check(lib, lib.spec_e2etv_fwd_bwd(ctypes.byref(tree.layout), V, dt, ptr(draft), ptr(teacher),
+                                           float(inv_norm), ptr(alpha_out), ptr(loss_out),
+                                           ptr(grad_out), ptr(work), ctypes.byref(nbytes),
+                                           ctypes.c_void_p(_stream(dev))))
+    return alpha_out, loss_out, grad_out

@@ -1,0 +1,180 @@
+// C ABI entry points for attention and E2E-TV: argument checks, workspace
+// sizing and dispatch. The pack entry point lives with its kernels.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "common.h"
+
+namespace spec {
+
+namespace {
+thread_local char g_last_error[512] = {0};
+}
+
+spec_status fail(spec_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+void clear_error() { g_last_error[0] = 0; }
+
+spec_status hip_fail(hipError_t e, const char *what) {
+  return fail(SPEC_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
+}
+
+namespace {
+
+spec_status check_layout(const spec_tree_layout *L, bool need_device) {
+  if (!L) return fail(SPEC_ERR_INVALID_ARG, "layout must be non-NULL");
+  if (L->n_trees < 1 || L->n_rows < 1 || L->n_steps < 0 || L->n_branches < 0)
+    return fail(SPEC_ERR_INVALID_ARG, "layout scalars are not those of a packed tree");
+  if (need_device && (!L->tree_off || !L->row_pos || !L->row_trunk_hi || !L->row_branch_lo ||
+                      !L->step_off || !L->step_pred_row || !L->attn_items))
+    return fail(SPEC_ERR_INVALID_ARG, "layout device arrays are missing (pack with a buffer first)");
+  return SPEC_OK;
+}
+
+// Workspace of the attention call: RoPE table, then rotated K.
+struct AttnWork {
+  size_t off_tab, off_k, total;
+};
+
+AttnWork attn_work(const spec_tree_layout &L, int hkv, int D, spec_dtype dt) {
+  AttnWork w{};
+  const size_t n_pos = (size_t)L.max_pos + 1;
+  w.off_tab = 0;
+  w.off_k = align_up(n_pos * (D / 2) * sizeof(float2), 256);
+  const size_t esz = dt == SPEC_BF16 ? 2 : 4;
+  w.total = align_up(w.off_k + (size_t)L.n_rows * hkv * D * esz, 256);
+  return w;
+}
+
+}  // namespace
+
+size_t e2etv_work_bytes(int64_t R) { return 4 * align_up((size_t)R * sizeof(float), 256); }
+
+E2etvWork e2etv_carve(void *d_work, int64_t R) {
+  char *p = static_cast<char *>(d_work);
+  const size_t step = align_up((size_t)R * sizeof(float), 256);
+  E2etvWork w;
+  w.lse_q2 = reinterpret_cast<float *>(p);
+  w.lse_p2 = reinterpret_cast<float *>(p + step);
+  w.S = reinterpret_cast<float *>(p + 2 * step);
+  w.coef = reinterpret_cast<float *>(p + 3 * step);
+  return w;
+}
+
+}  // namespace spec
+
+using namespace spec;
+
+extern "C" const char *spec_status_string(spec_status s) {
+  switch (s) {
+    case SPEC_OK: return "SPEC_OK";
+    case SPEC_ERR_INVALID_ARG: return "SPEC_ERR_INVALID_ARG";
+    case SPEC_ERR_UNSUPPORTED: return "SPEC_ERR_UNSUPPORTED";
+    case SPEC_ERR_WORKSPACE: return "SPEC_ERR_WORKSPACE";
+    case SPEC_ERR_HIP: return "SPEC_ERR_HIP";
+  }
+  return "SPEC_ERR_UNKNOWN";
+}
+
+extern "C" const char *spec_last_error(void) { return g_last_error; }
+
+extern "C" int32_t spec_abi_version(void) { return SPEC_TREE_ABI_VERSION; }
+
+extern "C" spec_status spec_tree_attn_fwd(const spec_tree_layout *layout, int32_t hq, int32_t hkv,
+                                          int32_t D, spec_dtype dtype, const void *d_q,
+                                          const void *d_k, const void *d_v, float rope_base,
+                                          float softmax_scale, void *d_out, void *d_readout,
+                                          void *d_work, size_t *work_bytes, spec_stream stream) {
+  clear_error();
+  if (!work_bytes) return fail(SPEC_ERR_INVALID_ARG, "work_bytes must be non-NULL");
+  spec_status st = check_layout(layout, d_work != nullptr);
+  if (st != SPEC_OK) return st;
+  if (hq < 1 || hkv < 1 || hq % hkv != 0)
+    return fail(SPEC_ERR_INVALID_ARG, "need Hq >= 1, Hkv >= 1 and Hq %% Hkv == 0 (got %d, %d)", hq, hkv);
+  if (D != 32 && D != 64 && D != 128)
+    return fail(SPEC_ERR_UNSUPPORTED, "head_dim %d not in {32, 64, 128}", D);
+  if (dtype != SPEC_BF16 && dtype != SPEC_F32)
+    return fail(SPEC_ERR_UNSUPPORTED, "dtype %d not supported", (int)dtype);
+  if (dtype == SPEC_BF16 && hq / hkv > 64)
+    return fail(SPEC_ERR_UNSUPPORTED, "GQA group %d larger than 64", hq / hkv);
+  if (!(rope_base > 0.f) || !std::isfinite(rope_base))
+    return fail(SPEC_ERR_INVALID_ARG, "rope_base must be a positive finite number");
+  if ((int64_t)layout->n_rows * hq * D > (int64_t)INT32_MAX * 8)
+    return fail(SPEC_ERR_UNSUPPORTED, "tensor too large");
+  const AttnWork w = attn_work(*layout, hkv, D, dtype);
+  if (!d_work) {
+    *work_bytes = w.total;
+    return SPEC_OK;
+  }
+  if (*work_bytes < w.total) {
+    size_t have = *work_bytes;
+    *work_bytes = w.total;
+    return fail(SPEC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", have, w.total);
+  }
+  if (!d_q || !d_k || !d_v || !d_out)
+    return fail(SPEC_ERR_INVALID_ARG, "d_q, d_k, d_v and d_out must be non-NULL");
+  if (!aligned16(d_q) || !aligned16(d_k) || !aligned16(d_v) || !aligned16(d_out) ||
+      !aligned16(d_work) || (d_readout && !aligned16(d_readout)))
+    return fail(SPEC_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)D);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *wb = static_cast<char *>(d_work);
+  float2 *tab = reinterpret_cast<float2 *>(wb + w.off_tab);
+  void *kws = wb + w.off_k;
+  SPEC_HIP_TRY(launch_rope_table(tab, layout->max_pos + 1, D / 2, (double)rope_base, s));
+  SPEC_HIP_TRY(launch_rope_k(d_k, kws, tab, layout->row_pos, layout->n_rows, hkv, D, dtype, s));
+  SPEC_HIP_TRY(launch_tree_attn(*layout, hq, hkv, D, dtype, d_q, kws, d_v, tab, scale, d_out, s));
+  if (d_readout && layout->n_steps > 0) {
+    const int64_t row_bytes = (int64_t)hq * D * (dtype == SPEC_BF16 ? 2 : 4);
+    SPEC_HIP_TRY(launch_readout(layout->step_pred_row, layout->n_steps, row_bytes, d_out,
+                                d_readout, s));
+  }
+  return SPEC_OK;
+}
+
+extern "C" spec_status spec_e2etv_fwd_bwd(const spec_tree_layout *layout, int64_t vocab,
+                                          spec_dtype dtype, const void *d_draft,
+                                          const void *d_teacher, float inv_norm, float *d_alpha,
+                                          float *d_loss, float *d_grad, void *d_work,
+                                          size_t *work_bytes, spec_stream stream) {
+  clear_error();
+  if (!work_bytes) return fail(SPEC_ERR_INVALID_ARG, "work_bytes must be non-NULL");
+  if (!layout) return fail(SPEC_ERR_INVALID_ARG, "layout must be non-NULL");
+  if (layout->n_steps < 1 || layout->n_branches < 1)
+    return fail(SPEC_ERR_INVALID_ARG, "the layout has no supervised steps");
+  if (d_work && !layout->step_off)
+    return fail(SPEC_ERR_INVALID_ARG, "layout device arrays are missing (pack with a buffer first)");
+  if (vocab < 1 || vocab > (int64_t)INT32_MAX)
+    return fail(SPEC_ERR_INVALID_ARG, "vocab %lld out of range", (long long)vocab);
+  if (dtype != SPEC_BF16 && dtype != SPEC_F32)
+    return fail(SPEC_ERR_UNSUPPORTED, "logit dtype %d not supported", (int)dtype);
+  if (!std::isfinite(inv_norm)) return fail(SPEC_ERR_INVALID_ARG, "inv_norm must be finite");
+  const size_t need = e2etv_work_bytes(layout->n_steps);
+  if (!d_work) {
+    *work_bytes = need;
+    return SPEC_OK;
+  }
+  if (*work_bytes < need) {
+    size_t have = *work_bytes;
+    *work_bytes = need;
+    return fail(SPEC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", have, need);
+  }
+  if (!d_draft || !d_teacher || !d_alpha || !d_loss)
+    return fail(SPEC_ERR_INVALID_ARG, "d_draft, d_teacher, d_alpha and d_loss must be non-NULL");
+  if (!aligned16(d_draft) || !aligned16(d_teacher) || !aligned16(d_work) ||
+      (d_grad && !aligned16(d_grad)))
+    return fail(SPEC_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  const float w = inv_norm > 0.f ? inv_norm : (float)(1.0 / (double)layout->n_steps);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SPEC_HIP_TRY(launch_e2etv(*layout, vocab, dtype, d_draft, d_teacher, w, d_alpha, d_loss, d_grad,
+                            e2etv_carve(d_work, layout->n_steps), s));
+  return SPEC_OK;
+}

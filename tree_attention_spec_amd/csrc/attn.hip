@@ -1,0 +1,369 @@
+// Tree-masked GQA attention over a packed proposal tree, plus readout.
+//
+// [SpecOPD paper page, Figure 3]: packed queries share the trunk K/V and every
+// row attends to itself and its ancestors only.
+// [SpecOPD notes page, "Equations"]: a branch row sees the reference prefix
+// through its anchor and its own branch predecessors; the anchor row predicts
+// y_{b,1} and the row of y_{b,i-1} predicts y_{b,i} (never the sample's own row).
+//
+// bf16 path (CDNA4 MFMA). A workgroup owns one query block of <= 32 packed rows
+// (an AttnItem) for one KV head g and NW of the query heads that share it; wave
+// w handles query head h = g*G + w for the 32 rows, so the K/V tiles staged in
+// LDS serve NW heads. The key loop runs over the block's trunk range, then its
+// branch range, in tiles of 64 keys:
+//   S^T[key][query] = K Q^T     v_mfma_f32_32x32x16_bf16, 2 output tiles x D/16 steps
+//   online softmax  per query column, in-lane over 32 keys + one cross-half max
+//   O^T[d][query]  += V^T P^T   D/32 output tiles x 4 steps
+// Keys on the rows, queries on the columns keeps each query's scores, max and
+// sum inside one lane (plus its partner lane l^32), and lets the probabilities
+// feed the second MFMA straight from registers: the V^T tile in LDS stores its
+// 16-key groups as key quads [0, 2, 1, 3] so that a lane's 8 B-operand slots
+// line up with the keys its accumulator holds. Tiles that every query of the
+// block sees in full skip the mask; the rest compare the key against the
+// query's two visible intervals. Rows of Q are rotated in registers on load.
+//
+// fp32 path: one wavefront per (row, head) walks the visible keys in order with
+// an exact float32 online softmax (no MFMA); it serves float32 inputs.
+#include "common.h"
+
+namespace spec {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int KT = 64;  // keys per tile
+
+template <int D>
+struct AttnSmem {
+  __bf16 k[KT][D + 8];   // K tile, row-major, padded against bank conflicts
+  __bf16 vt[D][KT + 8];  // V tile transposed, key quads permuted
+};
+
+// Stage keys [k0, min(k0 + KT, ke)) of KV head g; keys past ke are zero.
+template <int D, int NT>
+__device__ inline void stage_tile(AttnSmem<D> &sm, const __bf16 *__restrict__ kws,
+                                  const __bf16 *__restrict__ v, int g, int hkv, int64_t n_rows,
+                                  int k0, int ke, int tid) {
+  constexpr int CH = D / 8;  // 16-byte chunks per row
+  for (int c = tid; c < KT * CH; c += NT) {
+    const int r = c / CH, col = c % CH;
+    const int key = k0 + r;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (key < ke) val = *reinterpret_cast<const uint4 *>(kws + ((int64_t)g * n_rows + key) * D + col * 8);
+    *reinterpret_cast<uint4 *>(&sm.k[r][col * 8]) = val;
+  }
+  for (int c = tid; c < 16 * CH; c += NT) {
+    const int kq = c % 16, col = c / 16;
+    uint32_t w[4][4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int key = k0 + 4 * kq + e;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (key < ke) val = *reinterpret_cast<const uint4 *>(v + ((int64_t)key * hkv + g) * D + col * 8);
+      w[e][0] = val.x;
+      w[e][1] = val.y;
+      w[e][2] = val.z;
+      w[e][3] = val.w;
+    }
+    // quad kq of its 16-key group goes to slot {0, 8, 4, 12}[kq % 4]
+    const int pos = 16 * (kq >> 2) + ((kq & 1) << 3) + ((kq & 2) << 1);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {  // dims 2x (low halves) and 2x+1 (high halves)
+      uint2 lo, hi;
+      lo.x = (w[0][x] & 0xffffu) | (w[1][x] << 16);
+      lo.y = (w[2][x] & 0xffffu) | (w[3][x] << 16);
+      hi.x = (w[0][x] >> 16) | (w[1][x] & 0xffff0000u);
+      hi.y = (w[2][x] >> 16) | (w[3][x] & 0xffff0000u);
+      *reinterpret_cast<uint2 *>(&sm.vt[col * 8 + 2 * x][pos]) = lo;
+      *reinterpret_cast<uint2 *>(&sm.vt[col * 8 + 2 * x + 1][pos]) = hi;
+    }
+  }
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(
+    const AttnItem *__restrict__ items, int hkv, int group, int hsub,
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ kws, const __bf16 *__restrict__ v,
+    __bf16 *__restrict__ out, const float2 *__restrict__ tab, const int32_t *__restrict__ row_pos,
+    const int32_t *__restrict__ row_trunk_hi, const int32_t *__restrict__ row_branch_lo,
+    int64_t n_rows, int hq, float sl2) {
+  constexpr int NT = NW * 64;
+  constexpr int KS = D / 16;  // contraction steps of Q K^T
+  constexpr int DT = D / 32;  // output tiles of P V
+  __shared__ AttnSmem<D> sm;
+
+  // block -> (item, kv head, head slice). Consecutive blocks cycle over KV heads,
+  // so with the round-robin dispatch over XCDs each XCD keeps to few heads.
+  const int bid = blockIdx.x;
+  const int g = bid % hkv;
+  const int rest = bid / hkv;
+  const int hs = rest % hsub;
+  const AttnItem it = items[rest / hsub];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int n = lane & 31, half = lane >> 5;
+  const int hl = hs * NW + w;
+  const bool active = hl < group;  // wave-uniform
+  const int h = g * group + (active ? hl : 0);
+  const int qrow = min(it.q0 + n, it.q1 - 1);  // padding columns repeat the last row
+
+  // Q for this lane's query column, rotated: k-step s holds dims 16s + 8*half + [0, 8)
+  bf16x8 qf[KS];
+  {
+    const __bf16 *qp = q + ((int64_t)qrow * hq + h) * D;
+    const float2 *tp = tab + (int64_t)row_pos[qrow] * (D / 2);
+#pragma unroll
+    for (int s = 0; s < KS / 2; ++s) {
+      const int d0 = 16 * s + 8 * half;  // first half; partner dims are d0 + D/2
+      const bf16x8 x1 = *reinterpret_cast<const bf16x8 *>(qp + d0);
+      const bf16x8 x2 = *reinterpret_cast<const bf16x8 *>(qp + d0 + D / 2);
+      bf16x8 y1, y2;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float2 cs = tp[d0 + j];
+        const float a = (float)x1[j], b = (float)x2[j];
+        y1[j] = (__bf16)(a * cs.x - b * cs.y);
+        y2[j] = (__bf16)(b * cs.x + a * cs.y);
+      }
+      qf[s] = y1;
+      qf[s + KS / 2] = y2;
+    }
+  }
+  // this query's visible keys: [tree start, thi] U [blo, qrow]
+  const int thi = row_trunk_hi[qrow];
+  const int blo = row_branch_lo[qrow];
+  const int bhi = qrow;
+
+  f32x16 o[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  for (int phase = 0; phase < 2; ++phase) {
+    const int kb = phase == 0 ? it.tk0 : it.bk0;
+    const int ke = phase == 0 ? it.tk1 : it.bk1;
+    for (int k0 = kb; k0 < ke; k0 += KT) {
+      stage_tile<D, NT>(sm, kws, v, g, hkv, n_rows, k0, ke, tid);
+      __syncthreads();
+      if (active) {
+        f32x16 s0, s1;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s0[i] = s1[i] = 0.f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(&sm.k[n][16 * s + 8 * half]);
+          const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(&sm.k[32 + n][16 * s + 8 * half]);
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], s1, 0, 0, 0);
+        }
+        // accumulator i of tile t holds key k0 + 32t + 8(i/4) + 4*half + i%4
+        const bool need_mask = phase == 1 || (k0 + KT > it.tfull);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float x0 = s0[i] * sl2, x1 = s1[i] * sl2;
+          if (need_mask) {
+            const int key0 = k0 + 8 * (i >> 2) + 4 * half + (i & 3);
+            const int key1 = key0 + 32;
+            const bool v0 = phase == 0 ? key0 <= thi : (key0 >= blo && key0 <= bhi);
+            const bool v1 = phase == 0 ? key1 <= thi : (key1 >= blo && key1 <= bhi);
+            x0 = v0 ? x0 : -INFINITY;
+            x1 = v1 ? x1 : -INFINITY;
+          }
+          s0[i] = x0;
+          s1[i] = x1;
+          mx = fmaxf(mx, fmaxf(x0, x1));
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m, mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float corr = __builtin_amdgcn_exp2f(m - m_use);
+        float ls = 0.f;
+        bf16x8 pf[4];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p0 = __builtin_amdgcn_exp2f(s0[i] - m_use);
+          const float p1 = __builtin_amdgcn_exp2f(s1[i] - m_use);
+          ls += p0 + p1;
+          pf[i >> 3][i & 7] = (__bf16)p0;
+          pf[2 + (i >> 3)][i & 7] = (__bf16)p1;
+        }
+        l = l * corr + ls;
+        m = m_new;
+        if (__any(corr != 1.f)) {
+#pragma unroll
+          for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[t][i] *= corr;
+        }
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&sm.vt[32 * t + n][16 * kk + 8 * half]);
+            o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], o[t], 0, 0, 0);
+          }
+      }
+      __syncthreads();
+    }
+  }
+
+  const float lt = l + __shfl_xor(l, 32);
+  const float inv = 1.f / lt;
+  if (active && it.q0 + n < it.q1) {
+    __bf16 *op = out + ((int64_t)(it.q0 + n) * hq + h) * D;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        // accumulator 4*i4 + e holds dim 32t + 8*i4 + 4*half + e
+        __bf16 r4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r4[e] = (__bf16)(o[t][4 * i4 + e] * inv);
+        uint2 pk;
+        __builtin_memcpy(&pk, r4, 8);
+        *reinterpret_cast<uint2 *>(op + 32 * t + 8 * i4 + 4 * half) = pk;
+      }
+  }
+}
+
+// Exact float32 path: one wavefront per (row, head); lane holds dims lane and lane + 64.
+template <int D>
+__global__ __launch_bounds__(64) void tree_attn_f32_kernel(
+    const float *__restrict__ q, const float *__restrict__ kws, const float *__restrict__ v,
+    float *__restrict__ out, const float2 *__restrict__ tab, const int32_t *__restrict__ tree_off,
+    const int32_t *__restrict__ row_tree, const int32_t *__restrict__ row_pos,
+    const int32_t *__restrict__ row_trunk_hi, const int32_t *__restrict__ row_branch_lo,
+    int64_t n_rows, int hq, int hkv, float scale) {
+  constexpr int H = D / 2;
+  constexpr int PER = D > 64 ? 2 : 1;
+  const int r = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int g = h / (hq / hkv);
+  const float *qp = q + ((int64_t)r * hq + h) * D;
+  const float2 *tp = tab + (int64_t)row_pos[r] * H;
+  float qr[PER], o[PER];
+  bool on[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int d = lane + 64 * e;
+    on[e] = d < D;
+    qr[e] = 0.f;
+    o[e] = 0.f;
+    if (on[e]) {
+      const int j = d < H ? d : d - H;
+      const float2 cs = tp[j];
+      const float x1 = qp[j], x2 = qp[j + H];
+      qr[e] = d < H ? x1 * cs.x - x2 * cs.y : x2 * cs.x + x1 * cs.y;
+    }
+  }
+  float m = -INFINITY, l = 0.f;
+  const int lo = tree_off[row_tree[r]], thi = row_trunk_hi[r], blo = row_branch_lo[r];
+  for (int phase = 0; phase < 2; ++phase) {
+    const int c0 = phase == 0 ? lo : blo;
+    const int c1 = phase == 0 ? thi : r;
+    for (int c = c0; c <= c1; ++c) {
+      const float *kp = kws + ((int64_t)g * n_rows + c) * D;
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e)
+        if (on[e]) part += qr[e] * kp[lane + 64 * e];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+      const float s = part * scale;
+      const float m_new = fmaxf(m, s);
+      const float corr = expf(m - m_new);
+      const float p = expf(s - m_new);
+      l = l * corr + p;
+      const float *vp = v + ((int64_t)c * hkv + g) * D;
+#pragma unroll
+      for (int e = 0; e < PER; ++e)
+        if (on[e]) o[e] = o[e] * corr + p * vp[lane + 64 * e];
+      m = m_new;
+    }
+  }
+  float *op = out + ((int64_t)r * hq + h) * D;
+#pragma unroll
+  for (int e = 0; e < PER; ++e)
+    if (on[e]) op[lane + 64 * e] = o[e] / l;
+}
+
+namespace {
+
+template <int D, int NW>
+hipError_t launch_bf16(const spec_tree_layout &L, int hq, int hkv, const void *q, const void *kws,
+                       const void *v, const float2 *tab, float scale, void *out, hipStream_t s) {
+  const int group = hq / hkv;
+  const int hsub = (group + NW - 1) / NW;
+  const int64_t nblk = (int64_t)L.n_attn_items * hkv * hsub;
+  if (nblk == 0) return hipSuccess;
+  if (nblk > INT32_MAX) return hipErrorInvalidValue;
+  const float sl2 = scale * 1.4426950408889634f;  // scores in log2 units
+  hipLaunchKernelGGL((tree_attn_bf16_kernel<D, NW>), dim3((unsigned)nblk), dim3(NW * 64), 0, s,
+                     reinterpret_cast<const AttnItem *>(L.attn_items), hkv, group, hsub,
+                     static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(kws),
+                     static_cast<const __bf16 *>(v), static_cast<__bf16 *>(out), tab, L.row_pos,
+                     L.row_trunk_hi, L.row_branch_lo, L.n_rows, hq, sl2);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bf16_d(const spec_tree_layout &L, int hq, int hkv, const void *q, const void *kws,
+                         const void *v, const float2 *tab, float scale, void *out, hipStream_t s) {
+  const int group = hq / hkv;
+  if (group >= 8) return launch_bf16<D, 8>(L, hq, hkv, q, kws, v, tab, scale, out, s);
+  if (group >= 3) return launch_bf16<D, 4>(L, hq, hkv, q, kws, v, tab, scale, out, s);
+  if (group == 2) return launch_bf16<D, 2>(L, hq, hkv, q, kws, v, tab, scale, out, s);
+  return launch_bf16<D, 1>(L, hq, hkv, q, kws, v, tab, scale, out, s);
+}
+
+template <int D>
+hipError_t launch_f32(const spec_tree_layout &L, int hq, int hkv, const void *q, const void *kws,
+                      const void *v, const float2 *tab, float scale, void *out, hipStream_t s) {
+  hipLaunchKernelGGL(tree_attn_f32_kernel<D>, dim3((unsigned)L.n_rows, hq), dim3(64), 0, s,
+                     static_cast<const float *>(q), static_cast<const float *>(kws),
+                     static_cast<const float *>(v), static_cast<float *>(out), tab, L.tree_off,
+                     L.row_tree, L.row_pos, L.row_trunk_hi, L.row_branch_lo, L.n_rows, hq, hkv,
+                     scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_tree_attn(const spec_tree_layout &L, int32_t hq, int32_t hkv, int32_t D,
+                            spec_dtype dtype, const void *q, const void *kws, const void *v,
+                            const float2 *tab, float scale, void *out, hipStream_t s) {
+  if (dtype == SPEC_BF16) {
+    switch (D) {
+      case 32: return launch_bf16_d<32>(L, hq, hkv, q, kws, v, tab, scale, out, s);
+      case 64: return launch_bf16_d<64>(L, hq, hkv, q, kws, v, tab, scale, out, s);
+      case 128: return launch_bf16_d<128>(L, hq, hkv, q, kws, v, tab, scale, out, s);
+    }
+  } else {
+    switch (D) {
+      case 32: return launch_f32<32>(L, hq, hkv, q, kws, v, tab, scale, out, s);
+      case 64: return launch_f32<64>(L, hq, hkv, q, kws, v, tab, scale, out, s);
+      case 128: return launch_f32<128>(L, hq, hkv, q, kws, v, tab, scale, out, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+// readout[s] = out[pred_row[s]]: one block per step row, 16-byte moves.
+__global__ void readout_kernel(const int32_t *__restrict__ pred_row, int64_t row_u4,
+                               const uint4 *__restrict__ out, uint4 *__restrict__ readout) {
+  const int64_t s = blockIdx.x;
+  const uint4 *src = out + (int64_t)pred_row[s] * row_u4;
+  uint4 *dst = readout + s * row_u4;
+  for (int64_t i = threadIdx.x; i < row_u4; i += blockDim.x) dst[i] = src[i];
+}
+
+hipError_t launch_readout(const int32_t *pred_row, int64_t n_steps, int64_t row_bytes,
+                          const void *out, void *readout, hipStream_t s) {
+  hipLaunchKernelGGL(readout_kernel, dim3((unsigned)n_steps), dim3(256), 0, s, pred_row,
+                     row_bytes / 16, static_cast<const uint4 *>(out), static_cast<uint4 *>(readout));
+  return hipGetLastError();
+}
+
+}  // namespace spec

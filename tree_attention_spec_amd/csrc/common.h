@@ -1,0 +1,67 @@
+// Internal helpers shared by the translation units of libspec_tree.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "spec_tree.h"
+
+namespace spec {
+
+// ---------------------------------------------------------------- error reporting
+// Record a message for spec_last_error() on the calling thread and return `s`.
+spec_status fail(spec_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+spec_status hip_fail(hipError_t e, const char *what);
+
+#define SPEC_HIP_TRY(expr)                                  \
+  do {                                                      \
+    hipError_t e_ = (expr);                                 \
+    if (e_ != hipSuccess) return ::spec::hip_fail(e_, #expr); \
+  } while (0)
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---------------------------------------------------------------- attention schedule
+// One query block of the tree-attention kernel. Query rows [q0, q1) (packed,
+// at most kAttnBlockRows) attend to trunk keys [tk0, tk1) and branch keys
+// [bk0, bk1). Every query of the block sees every trunk key below `tfull`,
+// so tiles that end at or below it need no mask.
+struct AttnItem {
+  int32_t q0, q1, tk0, tk1, tfull, bk0, bk1, cost;
+};
+static_assert(sizeof(AttnItem) == 32, "AttnItem is 8 int32");
+constexpr int kAttnBlockRows = 32;
+constexpr int kAttnItemInts = 8;
+
+// ---------------------------------------------------------------- launchers (per TU)
+hipError_t launch_pack_expand(const spec_tree_layout &L, const int32_t *d_tree_len, int32_t max_trunk,
+                              hipStream_t stream);
+
+hipError_t launch_rope_table(float2 *tab, int32_t n_pos, int32_t half_dim, double base,
+                             hipStream_t stream);
+hipError_t launch_rope_k(const void *k, void *kws, const float2 *tab, const int32_t *row_pos,
+                         int64_t n_rows, int32_t hkv, int32_t head_dim, spec_dtype dtype,
+                         hipStream_t stream);
+hipError_t launch_tree_attn(const spec_tree_layout &L, int32_t hq, int32_t hkv, int32_t head_dim,
+                            spec_dtype dtype, const void *q, const void *kws, const void *v,
+                            const float2 *tab, float scale, void *out, hipStream_t stream);
+hipError_t launch_readout(const int32_t *pred_row, int64_t n_steps, int64_t row_bytes,
+                          const void *out, void *readout, hipStream_t stream);
+
+struct E2etvWork {
+  float *lse_q2;   // [R] log2-domain log-sum-exp of the draft row
+  float *lse_p2;   // [R] same for the teacher
+  float *S;        // [R] sum of q over {q < p}
+  float *coef;     // [R] dL/d alpha
+};
+size_t e2etv_work_bytes(int64_t n_steps);
+E2etvWork e2etv_carve(void *d_work, int64_t n_steps);
+hipError_t launch_e2etv(const spec_tree_layout &L, int64_t vocab, spec_dtype dtype,
+                        const void *draft, const void *teacher, float inv_norm, float *alpha,
+                        float *loss, float *grad, const E2etvWork &w, hipStream_t stream);
+
+}  // namespace spec
