@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark of the branch-parallel scoring step on one MI355X.
+
+One step is the whole hot path over one packed proposal tree: pack (host plan,
+copy, expand), tree attention with RoPE and readout, then the E2E-TV forward
+and backward over the supervised rows. Inputs are seeded synthetic tensors,
+already resident in device memory when the timed region starts. The headline
+is supervised rows per second; per-kernel durations come from HIP events
+recorded by the library on the stream it launches on, inside the timed steps.
+
+    python bench.py [--steps K] [--warmup W] [--config gqa8b] [--no-cpu-baseline]
+
+Prints one JSON line. Only one GPU is supported (--gpus must be 1).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def causal_pairs(s) -> int:
+    """Visible (query, key) pairs: trunk triangles plus each branch row's prefix."""
+    import numpy as np
+    P = int(sum(int(t) * (int(t) + 1) // 2 for t in s["trunk_len"]))
+    a = s["anchors"].astype(np.int64)
+    w = s["branch_len"].astype(np.int64)
+    # sum_{i=1}^{W-1} (a + 1 + i) = (W-1)(a+1) + (W-1)W/2
+    P += int(np.sum((w - 1) * (a + 1) + (w - 1) * w // 2))
+    return P
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "tree_attention_spec_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, src_hash: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, s, q, k, v, z_rows_fn, N, R, n_attn=24, n_e2e=6):
+    """Time the oracle on a bounded random sample and scale it to the full step."""
+    import numpy as np
+    from oracle import e2etv_coef_ref, e2etv_grad_ref, e2etv_row_stats_ref, pack_ref, rope_ref, tree_attn_ref
+    from specgen import bf16_bits_to_f32
+
+    def widen(a):
+        return bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+
+    rng = np.random.default_rng(123)
+    t0 = time.perf_counter()
+    lay = pack_ref(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"])
+    t_pack = time.perf_counter() - t0
+    qd, kd, vd = widen(q), widen(k), widen(v)
+    t0 = time.perf_counter()
+    rope_ref(kd, lay["row_pos"][:, None], cfg.rope_base)
+    t_fixed = time.perf_counter() - t0
+    rows = rng.choice(N, size=min(n_attn, N), replace=False)
+    t0 = time.perf_counter()
+    tree_attn_ref(lay, qd, kd, vd, cfg.rope_base, rows=rows)
+    t_call = time.perf_counter() - t0
+    t_attn = t_fixed + (N / len(rows)) * max(t_call - t_fixed, 0.0)
+    srows = np.sort(rng.choice(R, size=min(n_e2e, R), replace=False))
+    zs, ys = z_rows_fn(srows)
+    t0 = time.perf_counter()
+    alpha, S, _, _, qq, pp = e2etv_row_stats_ref(zs.astype(np.float64), ys.astype(np.float64))
+    c = e2etv_coef_ref(alpha, [0, len(srows)])
+    e2etv_grad_ref(qq, pp, S, c)
+    t_e2e = (R / len(srows)) * (time.perf_counter() - t0)
+    total = t_pack + t_attn + t_e2e
+    return {
+        "value": R / total, "unit": "supervised rows/s", "cores": 1, "kind": "oracle",
+        "sample": "%d random packed rows of tree attention (plus the full K rotation) and %d random "
+                  "logit rows of E2E-TV stats+gradient, float64 NumPy, one thread; scaled to the "
+                  "full step (N=%d rows, R=%d steps)" % (len(rows), len(srows), N, R),
+        "seconds_full_step_estimate": total,
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="gqa8b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the branch-parallel scoring path is built and timed "
+              "on a single MI355X (multi-GPU sharding is a design note, not an implementation).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import tree_attention_spec_amd as tas
+    from specgen import CONFIGS, gen_logit_rows, gen_logits, gen_qkv, gen_structure
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("config %s: %s" % (cfg.name, cfg.description))
+    s = gen_structure(cfg)
+    layout, mem_bytes = tas.spec_tree_pack_query(s["trunk_len"], s["n_branches"], s["anchors"],
+                                                 s["branch_len"])
+    N, R = layout.n_rows, layout.n_steps
+    log("N=%d packed rows, R=%d supervised steps; generating inputs" % (N, R))
+
+    def dev_tensor(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v = gen_qkv(cfg, N)
+    qt, kt, vt = dev_tensor(q), dev_tensor(k), dev_tensor(v)
+    z, y = gen_logits(cfg, R)
+    zt, yt = dev_tensor(z), dev_tensor(y)
+    del z, y
+    V = cfg.vocab
+    esz_logit = 2 if cfg.logit_dtype == "bf16" else 4
+
+    mem = torch.empty(mem_bytes, dtype=torch.uint8, device=dev)
+    tree = tas.spec_tree_pack(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"], mem=mem)
+    out = torch.empty_like(qt)
+    ro = torch.empty((R, cfg.hq, cfg.head_dim), dtype=qt.dtype, device=dev)
+    awork = torch.empty(tas.attn_work_bytes(tree, cfg.hq, cfg.hkv, cfg.head_dim, qt.dtype),
+                        dtype=torch.uint8, device=dev)
+    alpha = torch.empty(R, dtype=torch.float32, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    grad = torch.empty((R, V), dtype=torch.float32, device=dev)
+    ework = torch.empty(tas.e2etv_work_bytes(tree, V, zt.dtype), dtype=torch.uint8, device=dev)
+
+    def step():
+        t = tas.spec_tree_pack(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"], mem=mem)
+        tas.spec_tree_attn_fwd(t, qt, kt, vt, rope_base=cfg.rope_base, out=out, readout_out=ro, work=awork)
+        tas.spec_e2etv_fwd_bwd(t, zt, yt, alpha_out=alpha, loss_out=loss, grad_out=grad, work=ework)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timers = [tas.KernelTimer(capacity=16) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        with timers[i]:
+            step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    per = {}
+    for tm in timers:
+        for name, ms in tm.durations():
+            per.setdefault(name, []).append(ms)
+    avg = {n: sum(x) / len(x) for n, x in per.items()}
+    log("per-kernel ms: " + ", ".join("%s %.4f" % kv for kv in avg.items()))
+    log("loss %.6f, ms/step %.3f" % (loss.item(), ms_per_step))
+
+    P = causal_pairs(s)
+    attn_flop = 4.0 * cfg.head_dim * cfg.hq * P
+    e2e_elems = float(R) * V
+    bf16 = cfg.qkv_dtype == "bf16"
+    t_attn = avg.get("tree_attn", float("nan"))
+    attn_tflops = attn_flop / (t_attn * 1e-3) / 1e12
+    attn_peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
+    e2e_kernels = [n for n in avg if n.startswith("e2etv")]
+    t_e2e = sum(avg[n] for n in e2e_kernels)
+    e2e_bytes = e2e_elems * (2 * esz_logit + 4)
+    e2e_gbs = e2e_bytes / (t_e2e * 1e-3) / 1e9
+    components = {
+        "tree_attn": {"bound": "mfma", "ms": t_attn, "algorithmic_flop": attn_flop,
+                      "causal_pairs": P, "achieved": attn_tflops, "peak": attn_peak,
+                      "unit": "TFLOP/s", "frac": attn_tflops / attn_peak},
+        "e2etv": {"bound": "hbm", "ms": t_e2e, "kernels": e2e_kernels, "algorithmic_bytes": e2e_bytes,
+                  "achieved": e2e_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": e2e_gbs / PEAK_HBM_GBS},
+    }
+    # dominant single kernel by time
+    dom = max((n for n in avg if n == "tree_attn" or n.startswith("e2etv")), key=lambda n: avg[n])
+    if dom == "tree_attn":
+        roof = {"kernel": dom, "bound": "mfma", "achieved": attn_tflops, "peak": attn_peak,
+                "unit": "TFLOP/s", "frac": attn_tflops / attn_peak,
+                "traffic": measured_traffic(dom, source_hash("attn.hip"))}
+    else:
+        per_elem = {"e2etv_stats": 2 * esz_logit, "e2etv_grad": 2 * esz_logit + 4}.get(dom, 2 * esz_logit + 4)
+        b = e2e_elems * per_elem
+        gbs = b / (avg[dom] * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes_per_launch": b,
+                "traffic": measured_traffic(dom, source_hash("e2etv.hip"))}
+
+    result = {
+        "metric": "supervised rows/s (tree-attn + E2E-TV fwd/bwd)",
+        "value": R / (ms_per_step * 1e-3),
+        "unit": "supervised rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic (seeded; no datasets or weights)",
+        "config": {"workload": cfg.name, "description": cfg.description, "n_rows": N,
+                   "supervised_rows": R, "vocab": V, "heads_q": cfg.hq, "heads_kv": cfg.hkv,
+                   "head_dim": cfg.head_dim, "parallelism": "single GPU"},
+        "roofline": roof,
+        "components": components,
+        "kernel_ms": avg,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(cfg, s, q, k, v, lambda rows: gen_logit_rows(cfg, R, rows), N, R)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

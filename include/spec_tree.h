@@ -224,6 +224,26 @@ spec_status spec_e2etv_fwd_bwd(const spec_tree_layout *layout, int64_t vocab,
                                float *d_loss, float *d_grad, void *d_work, size_t *work_bytes,
                                spec_stream stream);
 
+/*
+ * Measurement hook (benchmarks only; it changes no result).
+ *
+ * After spec_profile_attach(p) on a thread, every call on that thread records
+ * p->events[p->used] on the call's stream once before its first kernel (name
+ * "<call>:begin") and once after each kernel it launches (name = the kernel),
+ * incrementing p->used, until p->capacity events are used. The time between
+ * consecutive events is then one kernel's duration. Events are hipEvent_t
+ * handles created by the caller; names are static strings. Pass NULL to detach.
+ */
+#define SPEC_PROFILE_MAX 256
+typedef struct spec_profile {
+  void **events;                        /* [capacity] hipEvent_t, caller-created */
+  int32_t capacity;                     /* <= SPEC_PROFILE_MAX */
+  int32_t used;                         /* out: events recorded so far */
+  const char *names[SPEC_PROFILE_MAX];  /* out: what ended at events[i] */
+} spec_profile;
+
+void spec_profile_attach(spec_profile *p);
+
 /* Human-readable name of a status code (static string). */
 const char *spec_status_string(spec_status status);
 

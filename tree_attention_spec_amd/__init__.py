@@ -20,7 +20,7 @@ from ._lib import (LAYOUT_ARRAYS, SPEC_BF16, SPEC_F32, SPEC_MAX_BRANCH_LEN, Spec
                    spec_tree_layout)
 
 __all__ = ["spec_tree_pack", "spec_tree_pack_query", "spec_tree_attn_fwd", "spec_e2etv_fwd_bwd",
-           "PackedTree", "SpecError", "library"]
+           "PackedTree", "SpecError", "library", "KernelTimer"]
 
 _LIB = None
 
@@ -101,14 +101,19 @@ def spec_tree_pack(trunk_len, n_branches, anchors, branch_len, device=None, mem=
     lib = library()
     device = torch.device(device if device is not None else "cuda")
     T, nb, a, w = _i32(trunk_len), _i32(n_branches), _i32(anchors), _i32(branch_len)
-    _, need = spec_tree_pack_query(T, nb, a, w)
-    if mem is None or mem.numel() < need:
+    if mem is None:
+        _, need = spec_tree_pack_query(T, nb, a, w)
         mem = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
     layout = spec_tree_layout()
     nbytes = ctypes.c_size_t(mem.numel())
-    _lib.check(lib, lib.spec_tree_pack(len(T), _iptr(T), _iptr(nb), _iptr(a), _iptr(w),
-                                       ctypes.c_void_p(mem.data_ptr()), ctypes.byref(nbytes),
-                                       ctypes.byref(layout), ctypes.c_void_p(_stream(device))))
+    call = lambda m: lib.spec_tree_pack(len(T), _iptr(T), _iptr(nb), _iptr(a), _iptr(w),
+                                        ctypes.c_void_p(m.data_ptr()), ctypes.byref(nbytes),
+                                        ctypes.byref(layout), ctypes.c_void_p(_stream(device)))
+    st = call(mem)
+    if st == _lib.SPEC_ERR_WORKSPACE:          # buffer too small: nbytes now holds the need
+        mem = torch.empty(nbytes.value, dtype=torch.uint8, device=device)
+        st = call(mem)
+    _lib.check(lib, st)
     return PackedTree(layout, mem)
 
 
@@ -202,3 +207,41 @@ def spec_e2etv_fwd_bwd(tree: PackedTree, draft: torch.Tensor, teacher: torch.Ten
                                            ptr(grad_out), ptr(work), ctypes.byref(nbytes),
                                            ctypes.c_void_p(_stream(dev))))
     return alpha_out, loss_out, grad_out
+
+
+class KernelTimer:
+    """Per-kernel HIP-event timing of library calls on this thread (measurement only).
+
+    While attached, each call records an event before its first kernel and after
+    every kernel on the stream it launches on; ``durations()`` returns
+    (kernel name, milliseconds) pairs in launch order.
+    """
+
+    def __init__(self, capacity: int = _lib.SPEC_PROFILE_MAX):
+        self.capacity = min(capacity, _lib.SPEC_PROFILE_MAX)
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(self.capacity)]
+        for e in self.events:          # torch creates the HIP event on first record
+            e.record()
+        torch.cuda.synchronize()
+        self._handles = (ctypes.c_void_p * self.capacity)(*[e.cuda_event for e in self.events])
+        self.prof = _lib.spec_profile()
+        self.prof.events = ctypes.cast(self._handles, ctypes.POINTER(ctypes.c_void_p))
+        self.prof.capacity = self.capacity
+
+    def __enter__(self):
+        self.prof.used = 0
+        library().spec_profile_attach(ctypes.byref(self.prof))
+        return self
+
+    def __exit__(self, *exc):
+        library().spec_profile_attach(None)
+
+    def durations(self):
+        torch.cuda.synchronize()
+        out = []
+        for i in range(1, self.prof.used):
+            name = self.prof.names[i].decode()
+            if name.endswith(":begin"):
+                continue
+            out.append((name, self.events[i - 1].elapsed_time(self.events[i])))
+        return out

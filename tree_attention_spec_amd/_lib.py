@@ -49,6 +49,18 @@ class spec_tree_layout(ctypes.Structure):
     ]
 
 
+SPEC_PROFILE_MAX = 256
+
+
+class spec_profile(ctypes.Structure):
+    _fields_ = [
+        ("events", ctypes.POINTER(ctypes.c_void_p)),
+        ("capacity", ctypes.c_int32),
+        ("used", ctypes.c_int32),
+        ("names", ctypes.c_char_p * SPEC_PROFILE_MAX),
+    ]
+
+
 # name -> (length as a function of the layout scalars)
 LAYOUT_ARRAYS = {
     "tree_off": lambda L: L.n_trees + 1,
@@ -72,7 +84,7 @@ LAYOUT_ARRAYS = {
 }
 
 EXPORTS = ["spec_tree_pack", "spec_tree_attn_fwd", "spec_e2etv_fwd_bwd", "spec_status_string",
-           "spec_last_error", "spec_abi_version"]
+           "spec_last_error", "spec_abi_version", "spec_profile_attach"]
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -100,6 +112,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_last_error.argtypes = []
     lib.spec_abi_version.restype = c.c_int32
     lib.spec_abi_version.argtypes = []
+    lib.spec_profile_attach.restype = None
+    lib.spec_profile_attach.argtypes = [c.POINTER(spec_profile)]
     return lib
 
 

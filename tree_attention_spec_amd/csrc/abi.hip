@@ -11,6 +11,14 @@ namespace spec {
 
 namespace {
 thread_local char g_last_error[512] = {0};
+thread_local spec_profile *g_prof = nullptr;
+}  // namespace
+
+void prof_mark(hipStream_t s, const char *name) {
+  spec_profile *p = g_prof;
+  if (!p || p->used >= p->capacity || p->used >= SPEC_PROFILE_MAX) return;
+  if (hipEventRecord(static_cast<hipEvent_t>(p->events[p->used]), s) == hipSuccess)
+    p->names[p->used++] = name;
 }
 
 spec_status fail(spec_status s, const char *fmt, ...) {
@@ -88,6 +96,8 @@ extern "C" const char *spec_last_error(void) { return g_last_error; }
 
 extern "C" int32_t spec_abi_version(void) { return SPEC_TREE_ABI_VERSION; }
 
+extern "C" void spec_profile_attach(spec_profile *p) { g_prof = p; }
+
 extern "C" spec_status spec_tree_attn_fwd(const spec_tree_layout *layout, int32_t hq, int32_t hkv,
                                           int32_t D, spec_dtype dtype, const void *d_q,
                                           const void *d_k, const void *d_v, float rope_base,
@@ -129,13 +139,18 @@ extern "C" spec_status spec_tree_attn_fwd(const spec_tree_layout *layout, int32_
   char *wb = static_cast<char *>(d_work);
   float2 *tab = reinterpret_cast<float2 *>(wb + w.off_tab);
   void *kws = wb + w.off_k;
+  prof_mark(s, "attn:begin");
   SPEC_HIP_TRY(launch_rope_table(tab, layout->max_pos + 1, D / 2, (double)rope_base, s));
+  prof_mark(s, "rope_table");
   SPEC_HIP_TRY(launch_rope_k(d_k, kws, tab, layout->row_pos, layout->n_rows, hkv, D, dtype, s));
+  prof_mark(s, "rope_k");
   SPEC_HIP_TRY(launch_tree_attn(*layout, hq, hkv, D, dtype, d_q, kws, d_v, tab, scale, d_out, s));
+  prof_mark(s, "tree_attn");
   if (d_readout && layout->n_steps > 0) {
     const int64_t row_bytes = (int64_t)hq * D * (dtype == SPEC_BF16 ? 2 : 4);
     SPEC_HIP_TRY(launch_readout(layout->step_pred_row, layout->n_steps, row_bytes, d_out,
                                 d_readout, s));
+    prof_mark(s, "readout");
   }
   return SPEC_OK;
 }
@@ -174,6 +189,7 @@ extern "C" spec_status spec_e2etv_fwd_bwd(const spec_tree_layout *layout, int64_
     return fail(SPEC_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
   const float w = inv_norm > 0.f ? inv_norm : (float)(1.0 / (double)layout->n_steps);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  prof_mark(s, "e2etv:begin");
   SPEC_HIP_TRY(launch_e2etv(*layout, vocab, dtype, d_draft, d_teacher, w, d_alpha, d_loss, d_grad,
                             e2etv_carve(d_work, layout->n_steps), s));
   return SPEC_OK;

@@ -22,6 +22,9 @@ spec_status hip_fail(hipError_t e, const char *what);
     if (e_ != hipSuccess) return ::spec::hip_fail(e_, #expr); \
   } while (0)
 
+// Record a profiling event (no-op unless a spec_profile is attached on this thread).
+void prof_mark(hipStream_t s, const char *name);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -255,16 +255,20 @@ hipError_t launch_typed(const spec_tree_layout &L, int64_t V, const void *draft,
                      y, V, alpha, ws.S, ws.lse_q2, ws.lse_p2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  prof_mark(s, "e2etv_stats");
   hipLaunchKernelGGL(e2etv_scan_kernel, dim3(1), dim3(1024), 0, s, L.step_off, L.n_branches,
                      alpha, w, ws.coef, loss);
   e = hipGetLastError();
   if (e != hipSuccess || !grad) return e;
+  prof_mark(s, "e2etv_scan");
   const int64_t per_block = (int64_t)kGradThreads * 8;
   const int64_t chunks = (V + per_block - 1) / per_block;
   if (chunks * R > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL((e2etv_grad_kernel<T, VEC>), dim3((unsigned)(chunks * R)), dim3(kGradThreads),
                      0, s, z, y, V, ws.lse_q2, ws.lse_p2, ws.S, ws.coef, grad, (int32_t)chunks);
-  return hipGetLastError();
+  e = hipGetLastError();
+  prof_mark(s, "e2etv_grad");
+  return e;
 }
 
 }  // namespace

@@ -342,8 +342,11 @@ extern "C" spec_status spec_tree_pack(int32_t n_trees, const int32_t *h_trunk_le
   put(c.off_items, p.items.data(), p.items.size() * sizeof(AttnItem));
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  prof_mark(s, "pack:begin");
   SPEC_HIP_TRY(hipMemcpyAsync(d_mem, head.data(), c.head_bytes, hipMemcpyHostToDevice, s));
+  prof_mark(s, "pack_copy");
   SPEC_HIP_TRY(launch_pack_expand(L, at(c.off_tree_len), p.max_trunk, s));
+  prof_mark(s, "pack_expand");
   *mem_bytes = c.total;
   *layout = L;
   return SPEC_OK;
