@@ -45,7 +45,6 @@ extern "C" {
 
 #define SPEC_TREE_ABI_VERSION 1
 #define SPEC_MAX_BRANCH_LEN 64 /* largest supported branch width W_b */
-#define SPEC_ROW_GROUP 16      /* supervised steps per E2E-TV row group */
 
 typedef enum spec_status {
   SPEC_OK = 0,
@@ -89,7 +88,7 @@ typedef struct spec_tree_layout {
   int64_t n_rows;          /* N */
   int64_t n_steps;         /* R */
   int32_t n_attn_items;    /* query blocks in attn_items */
-  int32_t n_row_groups;    /* E2E-TV row groups in row_group_off */
+  int32_t reserved0;
 
   /* per tree */
   int32_t *tree_off;        /* [n_trees+1] first packed row of each tree; last = N */
@@ -114,10 +113,6 @@ typedef struct spec_tree_layout {
   int32_t *step_sample_row; /* packed row of the sample y_{b,i}; -1 for the terminal sample */
   /* library-internal attention schedule [n_attn_items * 8] */
   int32_t *attn_items;
-  /* [n_row_groups+1] step offsets of E2E-TV row groups: runs of whole
-   * consecutive branches with at most SPEC_ROW_GROUP steps (a longer branch
-   * is a group of its own) */
-  int32_t *row_group_off;
 } spec_tree_layout;
 
 /*

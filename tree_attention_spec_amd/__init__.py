@@ -16,8 +16,8 @@ import numpy as np
 import torch  # loads the HIP runtime the library binds to; keep before the library
 
 from . import _lib
-from ._lib import (LAYOUT_ARRAYS, SPEC_BF16, SPEC_F32, SPEC_MAX_BRANCH_LEN, SPEC_ROW_GROUP,  # noqa: F401
-                   SpecError, spec_tree_layout)
+from ._lib import (LAYOUT_ARRAYS, SPEC_BF16, SPEC_F32, SPEC_MAX_BRANCH_LEN, SpecError,  # noqa: F401
+                   spec_tree_layout)
 
 __all__ = ["spec_tree_pack", "spec_tree_pack_query", "spec_tree_attn_fwd", "spec_e2etv_fwd_bwd",
            "PackedTree", "SpecError", "library", "KernelTimer"]

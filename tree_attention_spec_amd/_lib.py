@@ -14,7 +14,6 @@ LIB_PATH = os.path.join(PKG, "libspec_tree.so")
 SPEC_OK, SPEC_ERR_INVALID_ARG, SPEC_ERR_UNSUPPORTED, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP = range(5)
 SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_MAX_BRANCH_LEN = 64
-SPEC_ROW_GROUP = 16
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 
@@ -28,7 +27,7 @@ class spec_tree_layout(ctypes.Structure):
         ("n_rows", ctypes.c_int64),
         ("n_steps", ctypes.c_int64),
         ("n_attn_items", ctypes.c_int32),
-        ("n_row_groups", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
         ("tree_off", _i32p),
         ("row_tree", _i32p),
         ("row_branch", _i32p),
@@ -47,7 +46,6 @@ class spec_tree_layout(ctypes.Structure):
         ("step_pred_row", _i32p),
         ("step_sample_row", _i32p),
         ("attn_items", _i32p),
-        ("row_group_off", _i32p),
     ]
 
 
@@ -83,7 +81,6 @@ LAYOUT_ARRAYS = {
     "step_pred_row": lambda L: L.n_steps,
     "step_sample_row": lambda L: L.n_steps,
     "attn_items": lambda L: L.n_attn_items * 8,
-    "row_group_off": lambda L: L.n_row_groups + 1,
 }
 
 EXPORTS = ["spec_tree_pack", "spec_tree_attn_fwd", "spec_e2etv_fwd_bwd", "spec_status_string",

@@ -64,48 +64,16 @@ AttnWork attn_work(const spec_tree_layout &L, int hkv, int D, spec_dtype dt) {
 
 }  // namespace
 
-namespace {
-// fused-path scratch bounds (independent of the device so size queries need no HIP call)
-constexpr size_t kFusedMaxGrid = 2048, kFusedMaxTeams = 512, kFusedRows = SPEC_ROW_GROUP;
+size_t e2etv_work_bytes(int64_t R) { return 4 * align_up((size_t)R * sizeof(float), 256); }
 
-struct E2etvCarve {
-  size_t step, bar, status, lse, as, bsum, total;
-};
-
-E2etvCarve e2etv_layout(int64_t R, int64_t B) {
-  E2etvCarve c{};
-  c.step = align_up((size_t)R * sizeof(float), 256);
-  size_t o = 4 * c.step;
-  c.bar = o;
-  o = align_up(o + kFusedMaxTeams * 32 * sizeof(unsigned), 256);
-  c.status = o;
-  o = align_up(o + sizeof(unsigned), 256);
-  c.lse = o;
-  o = align_up(o + 2 * kFusedRows * kFusedMaxGrid * sizeof(float4), 256);
-  c.as = o;
-  o = align_up(o + 2 * kFusedRows * kFusedMaxGrid * sizeof(float2), 256);
-  c.bsum = o;
-  o = align_up(o + (size_t)(B > 0 ? B : 1) * sizeof(double), 256);
-  c.total = o;
-  return c;
-}
-}  // namespace
-
-size_t e2etv_work_bytes(int64_t R, int64_t B) { return e2etv_layout(R, B).total; }
-
-E2etvWork e2etv_carve(void *d_work, int64_t R, int64_t B) {
+E2etvWork e2etv_carve(void *d_work, int64_t R) {
   char *p = static_cast<char *>(d_work);
-  const E2etvCarve c = e2etv_layout(R, B);
+  const size_t step = align_up((size_t)R * sizeof(float), 256);
   E2etvWork w;
   w.lse_q2 = reinterpret_cast<float *>(p);
-  w.lse_p2 = reinterpret_cast<float *>(p + c.step);
-  w.S = reinterpret_cast<float *>(p + 2 * c.step);
-  w.coef = reinterpret_cast<float *>(p + 3 * c.step);
-  w.bar = reinterpret_cast<unsigned *>(p + c.bar);
-  w.status = reinterpret_cast<unsigned *>(p + c.status);
-  w.lse_part = reinterpret_cast<float4 *>(p + c.lse);
-  w.as_part = reinterpret_cast<float2 *>(p + c.as);
-  w.branch_sum = reinterpret_cast<double *>(p + c.bsum);
+  w.lse_p2 = reinterpret_cast<float *>(p + step);
+  w.S = reinterpret_cast<float *>(p + 2 * step);
+  w.coef = reinterpret_cast<float *>(p + 3 * step);
   return w;
 }
 
@@ -204,7 +172,7 @@ extern "C" spec_status spec_e2etv_fwd_bwd(const spec_tree_layout *layout, int64_
   if (dtype != SPEC_BF16 && dtype != SPEC_F32)
     return fail(SPEC_ERR_UNSUPPORTED, "logit dtype %d not supported", (int)dtype);
   if (!std::isfinite(inv_norm)) return fail(SPEC_ERR_INVALID_ARG, "inv_norm must be finite");
-  const size_t need = e2etv_work_bytes(layout->n_steps, layout->n_branches);
+  const size_t need = e2etv_work_bytes(layout->n_steps);
   if (!d_work) {
     *work_bytes = need;
     return SPEC_OK;
@@ -223,6 +191,6 @@ extern "C" spec_status spec_e2etv_fwd_bwd(const spec_tree_layout *layout, int64_
   hipStream_t s = static_cast<hipStream_t>(stream);
   prof_mark(s, "e2etv:begin");
   SPEC_HIP_TRY(launch_e2etv(*layout, vocab, dtype, d_draft, d_teacher, w, d_alpha, d_loss, d_grad,
-                            e2etv_carve(d_work, layout->n_steps, layout->n_branches), s));
+                            e2etv_carve(d_work, layout->n_steps), s));
   return SPEC_OK;
 }

@@ -60,15 +60,9 @@ struct E2etvWork {
   float *lse_p2;   // [R] same for the teacher
   float *S;        // [R] sum of q over {q < p}
   float *coef;     // [R] dL/d alpha
-  // fused single-read path
-  unsigned *bar;         // team barrier counters
-  unsigned *status;      // nonzero after a barrier timeout
-  float4 *lse_part;      // per-member log-sum-exp partials
-  float2 *as_part;       // per-member (alpha, S) partials
-  double *branch_sum;    // [B] sum_j prod_{i<=j} alpha_{b,i}
 };
-size_t e2etv_work_bytes(int64_t n_steps, int64_t n_branches);
-E2etvWork e2etv_carve(void *d_work, int64_t n_steps, int64_t n_branches);
+size_t e2etv_work_bytes(int64_t n_steps);
+E2etvWork e2etv_carve(void *d_work, int64_t n_steps);
 hipError_t launch_e2etv(const spec_tree_layout &L, int64_t vocab, spec_dtype dtype,
                         const void *draft, const void *teacher, float inv_norm, float *alpha,
                         float *loss, float *grad, const E2etvWork &w, hipStream_t stream);

@@ -109,24 +109,7 @@ struct Plan {
   std::vector<int32_t> tree_off, tree_len, branch_tree, branch_anchor, branch_len, branch_off,
       step_off, branch_order;
   std::vector<AttnItem> items;
-  std::vector<int32_t> row_group_off;
 };
-
-// E2E-TV row groups: whole consecutive branches (caller order) with at most
-// SPEC_ROW_GROUP steps; a longer branch forms a group of its own.
-void plan_row_groups(Plan &p) {
-  p.row_group_off.assign(1, 0);
-  int32_t rows = 0;
-  for (int32_t b = 0; b < p.B; ++b) {
-    const int32_t w = p.branch_len[b];
-    if (rows > 0 && rows + w > SPEC_ROW_GROUP) {
-      p.row_group_off.push_back(p.step_off[b]);
-      rows = 0;
-    }
-    rows += w;
-  }
-  if (rows > 0) p.row_group_off.push_back(p.step_off[p.B]);
-}
 
 // Query blocks for the attention kernel, longest first. Trunk blocks take 32
 // consecutive trunk rows; branch blocks take 32 consecutive branch rows of a
@@ -252,7 +235,6 @@ spec_status make_plan(int32_t n_trees, const int32_t *h_trunk_len, const int32_t
   p.step_off[0] = 0;
   for (int64_t i = 0; i < B; ++i) p.step_off[i + 1] = p.step_off[i] + h_branch_len[i];
   plan_attention(p);
-  plan_row_groups(p);
   return SPEC_OK;
 }
 
@@ -260,7 +242,7 @@ spec_status make_plan(int32_t n_trees, const int32_t *h_trunk_len, const int32_t
 // is written by the expand kernels.
 struct Carve {
   size_t off_tree_off, off_tree_len, off_branch_tree, off_branch_anchor, off_branch_len,
-      off_branch_off, off_step_off, off_branch_order, off_items, off_groups, head_bytes;
+      off_branch_off, off_step_off, off_branch_order, off_items, head_bytes;
   size_t off_rows[7];
   size_t off_steps[3];
   size_t total;
@@ -283,7 +265,6 @@ Carve carve(const Plan &p) {
   c.off_step_off = take(p.B + 1);
   c.off_branch_order = take(p.B);
   c.off_items = take(p.items.size() * kAttnItemInts);
-  c.off_groups = take(p.row_group_off.size());
   c.head_bytes = o;
   for (auto &r : c.off_rows) r = take(p.N);
   for (auto &s : c.off_steps) s = take(p.R);
@@ -317,7 +298,6 @@ extern "C" spec_status spec_tree_pack(int32_t n_trees, const int32_t *h_trunk_le
   L.n_rows = p.N;
   L.n_steps = p.R;
   L.n_attn_items = (int32_t)p.items.size();
-  L.n_row_groups = (int32_t)p.row_group_off.size() - 1;
   if (!d_mem) {  // size query: scalars only, no HIP call
     *mem_bytes = c.total;
     *layout = L;
@@ -340,7 +320,6 @@ extern "C" spec_status spec_tree_pack(int32_t n_trees, const int32_t *h_trunk_le
   L.step_off = at(c.off_step_off);
   L.branch_order = at(c.off_branch_order);
   L.attn_items = at(c.off_items);
-  L.row_group_off = at(c.off_groups);
   int32_t **rows[7] = {&L.row_tree, &L.row_branch, &L.row_anchor, &L.row_pos,
                        &L.row_depth, &L.row_trunk_hi, &L.row_branch_lo};
   for (int i = 0; i < 7; ++i) *rows[i] = at(c.off_rows[i]);
@@ -361,7 +340,6 @@ extern "C" spec_status spec_tree_pack(int32_t n_trees, const int32_t *h_trunk_le
   put(c.off_step_off, p.step_off.data(), p.step_off.size() * 4);
   put(c.off_branch_order, p.branch_order.data(), p.branch_order.size() * 4);
   put(c.off_items, p.items.data(), p.items.size() * sizeof(AttnItem));
-  put(c.off_groups, p.row_group_off.data(), p.row_group_off.size() * 4);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   prof_mark(s, "pack:begin");
