@@ -39,49 +39,86 @@ struct AttnSmem {
   __bf16 vt[D][KT + 8];  // V tile transposed, key quads permuted
 };
 
-// Stage keys [k0, min(k0 + KT, ke)) of KV head g; keys past ke are zero.
+// Global -> register -> LDS staging of one 64-key tile of KV head g: the loads
+// of the next tile are issued before the current tile is computed (registers
+// hold them), and the LDS tiles are double-buffered, so one barrier per tile
+// suffices. Keys past `ke` read as zero.
 template <int D, int NT>
-__device__ inline void stage_tile(AttnSmem<D> &sm, const __bf16 *__restrict__ kws,
-                                  const __bf16 *__restrict__ v, int g, int hkv, int64_t n_rows,
-                                  int k0, int ke, int tid) {
-  constexpr int CH = D / 8;  // 16-byte chunks per row
-  for (int c = tid; c < KT * CH; c += NT) {
-    const int r = c / CH, col = c % CH;
-    const int key = k0 + r;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (key < ke) val = *reinterpret_cast<const uint4 *>(kws + ((int64_t)g * n_rows + key) * D + col * 8);
-    *reinterpret_cast<uint4 *>(&sm.k[r][col * 8]) = val;
-  }
-  for (int c = tid; c < 16 * CH; c += NT) {
-    const int kq = c % 16, col = c / 16;
-    uint32_t w[4][4];
+struct TileRegs {
+  static constexpr int CH = D / 8;                       // 16-byte chunks per row
+  static constexpr int KPT = (KT * CH + NT - 1) / NT;    // K chunks per thread
+  static constexpr int VPT = (16 * CH + NT - 1) / NT;    // V (key quad, chunk) tasks per thread
+  uint4 k[KPT];
+  uint4 v[VPT][4];
+
+  __device__ inline void load(const __bf16 *__restrict__ kws, const __bf16 *__restrict__ vv, int g,
+                              int hkv, int64_t n_rows, int k0, int ke, int tid) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = k0 + 4 * kq + e;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (key < ke) val = *reinterpret_cast<const uint4 *>(v + ((int64_t)key * hkv + g) * D + col * 8);
-      w[e][0] = val.x;
-      w[e][1] = val.y;
-      w[e][2] = val.z;
-      w[e][3] = val.w;
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + i * NT;
+      const int r = c / CH, col = c % CH;
+      const int key = k0 + r;
+      k[i] = make_uint4(0, 0, 0, 0);
+      if (c < KT * CH && key < ke)
+        k[i] = *reinterpret_cast<const uint4 *>(kws + ((int64_t)g * n_rows + key) * D + col * 8);
     }
-    // quad kq of its 16-key group goes to slot {0, 8, 4, 12}[kq % 4]
-    const int pos = 16 * (kq >> 2) + ((kq & 1) << 3) + ((kq & 2) << 1);
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {  // dims 2x (low halves) and 2x+1 (high halves)
-      uint2 lo, hi;
-      lo.x = (w[0][x] & 0xffffu) | (w[1][x] << 16);
-      lo.y = (w[2][x] & 0xffffu) | (w[3][x] << 16);
-      hi.x = (w[0][x] >> 16) | (w[1][x] & 0xffff0000u);
-      hi.y = (w[2][x] >> 16) | (w[3][x] & 0xffff0000u);
-      *reinterpret_cast<uint2 *>(&sm.vt[col * 8 + 2 * x][pos]) = lo;
-      *reinterpret_cast<uint2 *>(&sm.vt[col * 8 + 2 * x + 1][pos]) = hi;
+    for (int i = 0; i < VPT; ++i) {
+      const int c = tid + i * NT;
+      const int kq = c % 16, col = c / 16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = k0 + 4 * kq + e;
+        v[i][e] = make_uint4(0, 0, 0, 0);
+        if (c < 16 * CH && key < ke)
+          v[i][e] = *reinterpret_cast<const uint4 *>(vv + ((int64_t)key * hkv + g) * D + col * 8);
+      }
     }
   }
+
+  __device__ inline void store(AttnSmem<D> &sm, int tid) const {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + i * NT;
+      if (c < KT * CH) *reinterpret_cast<uint4 *>(&sm.k[c / CH][(c % CH) * 8]) = k[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = tid + i * NT;
+      if (c >= 16 * CH) continue;
+      const int kq = c % 16, col = c / 16;
+      // quad kq of its 16-key group goes to slot {0, 8, 4, 12}[kq % 4]
+      const int pos = 16 * (kq >> 2) + ((kq & 1) << 3) + ((kq & 2) << 1);
+      const uint32_t w[4][4] = {{v[i][0].x, v[i][0].y, v[i][0].z, v[i][0].w},
+                                {v[i][1].x, v[i][1].y, v[i][1].z, v[i][1].w},
+                                {v[i][2].x, v[i][2].y, v[i][2].z, v[i][2].w},
+                                {v[i][3].x, v[i][3].y, v[i][3].z, v[i][3].w}};
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {  // dims 2x (low halves) and 2x+1 (high halves)
+        uint2 lo, hi;
+        lo.x = (w[0][x] & 0xffffu) | (w[1][x] << 16);
+        lo.y = (w[2][x] & 0xffffu) | (w[3][x] << 16);
+        hi.x = (w[0][x] >> 16) | (w[1][x] & 0xffff0000u);
+        hi.y = (w[2][x] >> 16) | (w[3][x] & 0xffff0000u);
+        *reinterpret_cast<uint2 *>(&sm.vt[col * 8 + 2 * x][pos]) = lo;
+        *reinterpret_cast<uint2 *>(&sm.vt[col * 8 + 2 * x + 1][pos]) = hi;
+      }
+    }
+  }
+};
+
+// max / sum over the lane pair (l, l ^ 32), identical in both lanes
+__device__ inline float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void tree_attn_bf16_kernel(
     const AttnItem *__restrict__ items, int hkv, int group, int hsub,
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ kws, const __bf16 *__restrict__ v,
     __bf16 *__restrict__ out, const float2 *__restrict__ tab, const int32_t *__restrict__ row_pos,
@@ -90,7 +127,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(
   constexpr int NT = NW * 64;
   constexpr int KS = D / 16;  // contraction steps of Q K^T
   constexpr int DT = D / 32;  // output tiles of P V
-  __shared__ AttnSmem<D> sm;
+  __shared__ AttnSmem<D> sm[2];
 
   // block -> (item, kv head, head slice). Consecutive blocks cycle over KV heads,
   // so with the round-robin dispatch over XCDs each XCD keeps to few heads.
@@ -107,7 +144,17 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(
   const int h = g * group + (active ? hl : 0);
   const int qrow = min(it.q0 + n, it.q1 - 1);  // padding columns repeat the last row
 
-  // Q for this lane's query column, rotated: k-step s holds dims 16s + 8*half + [0, 8)
+  // tiles: trunk keys [tk0, tk1) then branch keys [bk0, bk1), 64 keys each
+  const int n_trunk = (it.tk1 - it.tk0 + KT - 1) / KT;
+  const int n_tiles = n_trunk + (it.bk1 - it.bk0 + KT - 1) / KT;
+  auto tile_k0 = [&](int t) { return t < n_trunk ? it.tk0 + KT * t : it.bk0 + KT * (t - n_trunk); };
+  auto tile_ke = [&](int t) { return t < n_trunk ? it.tk1 : it.bk1; };
+
+  TileRegs<D, NT> regs;
+  if (n_tiles > 0) regs.load(kws, v, g, hkv, n_rows, tile_k0(0), tile_ke(0), tid);
+
+  // Q for this lane's query column, rotated and pre-scaled by scale*log2(e):
+  // k-step s holds dims 16s + 8*half + [0, 8)
   bf16x8 qf[KS];
   {
     const __bf16 *qp = q + ((int64_t)qrow * hq + h) * D;
@@ -122,8 +169,8 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(
       for (int j = 0; j < 8; ++j) {
         const float2 cs = tp[d0 + j];
         const float a = (float)x1[j], b = (float)x2[j];
-        y1[j] = (__bf16)(a * cs.x - b * cs.y);
-        y2[j] = (__bf16)(b * cs.x + a * cs.y);
+        y1[j] = (__bf16)((a * cs.x - b * cs.y) * sl2);
+        y2[j] = (__bf16)((b * cs.x + a * cs.y) * sl2);
       }
       qf[s] = y1;
       qf[s + KS / 2] = y2;
@@ -141,77 +188,73 @@ __global__ __launch_bounds__(NW * 64) void tree_attn_bf16_kernel(
     for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  for (int phase = 0; phase < 2; ++phase) {
-    const int kb = phase == 0 ? it.tk0 : it.bk0;
-    const int ke = phase == 0 ? it.tk1 : it.bk1;
-    for (int k0 = kb; k0 < ke; k0 += KT) {
-      stage_tile<D, NT>(sm, kws, v, g, hkv, n_rows, k0, ke, tid);
-      __syncthreads();
-      if (active) {
-        f32x16 s0, s1;
+  for (int t = 0; t < n_tiles; ++t) {
+    AttnSmem<D> &cur = sm[t & 1];
+    const int k0 = tile_k0(t);
+    const bool branch = t >= n_trunk;
+    regs.store(cur, tid);
+    __syncthreads();
+    if (t + 1 < n_tiles) regs.load(kws, v, g, hkv, n_rows, tile_k0(t + 1), tile_ke(t + 1), tid);
+    if (active) {
+      f32x16 s0, s1;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s0[i] = s1[i] = 0.f;
+      for (int i = 0; i < 16; ++i) s0[i] = s1[i] = 0.f;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(&sm.k[n][16 * s + 8 * half]);
-          const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(&sm.k[32 + n][16 * s + 8 * half]);
-          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], s0, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], s1, 0, 0, 0);
-        }
-        // accumulator i of tile t holds key k0 + 32t + 8(i/4) + 4*half + i%4
-        const bool need_mask = phase == 1 || (k0 + KT > it.tfull);
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x0 = s0[i] * sl2, x1 = s1[i] * sl2;
-          if (need_mask) {
-            const int key0 = k0 + 8 * (i >> 2) + 4 * half + (i & 3);
-            const int key1 = key0 + 32;
-            const bool v0 = phase == 0 ? key0 <= thi : (key0 >= blo && key0 <= bhi);
-            const bool v1 = phase == 0 ? key1 <= thi : (key1 >= blo && key1 <= bhi);
-            x0 = v0 ? x0 : -INFINITY;
-            x1 = v1 ? x1 : -INFINITY;
-          }
-          s0[i] = x0;
-          s1[i] = x1;
-          mx = fmaxf(mx, fmaxf(x0, x1));
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float corr = __builtin_amdgcn_exp2f(m - m_use);
-        float ls = 0.f;
-        bf16x8 pf[4];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p0 = __builtin_amdgcn_exp2f(s0[i] - m_use);
-          const float p1 = __builtin_amdgcn_exp2f(s1[i] - m_use);
-          ls += p0 + p1;
-          pf[i >> 3][i & 7] = (__bf16)p0;
-          pf[2 + (i >> 3)][i & 7] = (__bf16)p1;
-        }
-        l = l * corr + ls;
-        m = m_new;
-        if (__any(corr != 1.f)) {
-#pragma unroll
-          for (int t = 0; t < DT; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[t][i] *= corr;
-        }
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&sm.vt[32 * t + n][16 * kk + 8 * half]);
-            o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], o[t], 0, 0, 0);
-          }
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(&cur.k[n][16 * s + 8 * half]);
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(&cur.k[32 + n][16 * s + 8 * half]);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], s1, 0, 0, 0);
       }
-      __syncthreads();
+      // accumulator i of tile t holds key k0 + 32t + 8(i/4) + 4*half + i%4
+      const bool need_mask = branch || (k0 + KT > it.tfull);
+      if (need_mask) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key0 = k0 + 8 * (i >> 2) + 4 * half + (i & 3);
+          const int key1 = key0 + 32;
+          const bool v0 = branch ? (key0 >= blo && key0 <= bhi) : key0 <= thi;
+          const bool v1 = branch ? (key1 >= blo && key1 <= bhi) : key1 <= thi;
+          s0[i] = v0 ? s0[i] : -INFINITY;
+          s1[i] = v1 ? s1[i] : -INFINITY;
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+      mx = pair_max(mx);
+      const float m_new = fmaxf(m, mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float corr = __builtin_amdgcn_exp2f(m - m_use);
+      float ls = 0.f;
+      bf16x8 pf[4];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(s0[i] - m_use);
+        const float p1 = __builtin_amdgcn_exp2f(s1[i] - m_use);
+        ls += p0 + p1;
+        pf[i >> 3][i & 7] = (__bf16)p0;
+        pf[2 + (i >> 3)][i & 7] = (__bf16)p1;
+      }
+      l = l * corr + ls;
+      m = m_new;
+      if (__any(corr != 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[dt][i] *= corr;
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&cur.vt[32 * dt + n][16 * kk + 8 * half]);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], o[dt], 0, 0, 0);
+        }
     }
   }
 
-  const float lt = l + __shfl_xor(l, 32);
-  const float inv = 1.f / lt;
+  const float inv = 1.f / pair_sum(l);
   if (active && it.q0 + n < it.q1) {
     __bf16 *op = out + ((int64_t)(it.q0 + n) * hq + h) * D;
 #pragma unroll
