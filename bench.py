@@ -66,6 +66,23 @@ def measured_traffic(kernel: str, src_hash: str):
     return rec.get("bytes_per_launch")
 
 
+def summarize_pmc(paths):
+    """Per-kernel mean of every counter in rocprofv3 --pmc databases (no GPU needed)."""
+    import collections
+    import sqlite3
+    out = {}
+    for path in paths:
+        cur = sqlite3.connect(path).cursor()
+        rows = cur.execute("select k.name, p.counter_name, p.counter_value from pmc_events p "
+                           "join kernels k on p.dispatch_id = k.dispatch_id").fetchall()
+        agg = collections.defaultdict(list)
+        for name, counter, value in rows:
+            agg[(name, counter)].append(value)
+        for (name, counter), vals in sorted(agg.items()):
+            out.setdefault(name, {})[counter] = {"dispatches": len(vals), "mean": sum(vals) / len(vals)}
+    return out
+
+
 def cpu_baseline(cfg, s, q, k, v, z_rows_fn, N, R, n_attn=24, n_e2e=6):
     """Time the oracle on a bounded random sample and scale it to the full step."""
     import numpy as np
@@ -115,7 +132,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM counters) and exit")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DB",
+                    help="print per-kernel counter means from rocprofv3 --pmc databases and exit")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        print(json.dumps(summarize_pmc(args.summarize_pmc), indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the branch-parallel scoring path is built and timed "
               "on a single MI355X (multi-GPU sharding is a design note, not an implementation).",
