@@ -1,0 +1,153 @@
+"""CPU tier for the C ABI: the library loads, exports what the header declares,
+and its size queries and argument checks work without touching a GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import pack_ref
+from specgen import CONFIGS, gen_structure
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_tree.h")
+LIB = os.path.join(ROOT, "tree_attention_spec_amd", "libspec_tree.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB),
+                                reason="libspec_tree.so not built (run __graft_entry__.build())")
+
+
+@pytest.fixture(scope="module")
+def tas():
+    import tree_attention_spec_amd
+    return tree_attention_spec_amd
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(tas):
+    names = declared_functions()
+    assert set(names) >= {"spec_tree_pack", "spec_tree_attn_fwd", "spec_e2etv_fwd_bwd"}
+    lib = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+    from tree_attention_spec_amd import _lib
+    assert set(_lib.EXPORTS) == set(names)
+
+
+def test_abi_version_and_status_strings(tas):
+    lib = tas.library()
+    ver = int(re.search(r"#define SPEC_TREE_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert lib.spec_abi_version() == ver
+    names = [lib.spec_status_string(i).decode() for i in range(5)]
+    assert names == ["SPEC_OK", "SPEC_ERR_INVALID_ARG", "SPEC_ERR_UNSUPPORTED", "SPEC_ERR_WORKSPACE",
+                     "SPEC_ERR_HIP"]
+
+
+def test_layout_struct_matches_header(tas):
+    """The ctypes mirror lists the header's fields in order."""
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct spec_tree_layout {"):text.index("} spec_tree_layout;")]
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"\b(?:int32_t|int64_t)\s*\*?\s*([a-z_0-9, *]+);", body)
+    names = []
+    for group in fields:
+        names += [f.strip(" *") for f in group.split(",")]
+    from tree_attention_spec_amd import _lib
+    assert [f[0] for f in _lib.spec_tree_layout._fields_] == names
+
+
+@pytest.mark.parametrize("name", ["tiny", "gqa8b", "batched", "stress"])
+def test_pack_size_query_matches_oracle(tas, name):
+    s = gen_structure(CONFIGS[name])
+    layout, nbytes = tas.spec_tree_pack_query(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"])
+    ref = pack_ref(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"])
+    assert (layout.n_rows, layout.n_steps) == (ref["n_rows"], ref["n_steps"])
+    assert (layout.max_branch_len, layout.max_pos) == (ref["max_branch_len"], ref["max_pos"])
+    assert layout.n_trees == len(s["trunk_len"]) and layout.n_branches == len(s["anchors"])
+    assert layout.n_attn_items >= (ref["n_rows"] + 31) // 32
+    assert nbytes >= 4 * (7 * ref["n_rows"] + 3 * ref["n_steps"])
+
+
+@pytest.mark.parametrize("bad", [
+    dict(trunk_len=[5], n_branches=[1], anchors=[5], branch_len=[2]),
+    dict(trunk_len=[5], n_branches=[1], anchors=[-1], branch_len=[2]),
+    dict(trunk_len=[5], n_branches=[1], anchors=[1], branch_len=[0]),
+    dict(trunk_len=[5], n_branches=[1], anchors=[1], branch_len=[65]),
+    dict(trunk_len=[0], n_branches=[0], anchors=[], branch_len=[]),
+    dict(trunk_len=[5], n_branches=[-1], anchors=[], branch_len=[]),
+])
+def test_pack_rejects_bad_input(tas, bad):
+    with pytest.raises(tas.SpecError) as e:
+        tas.spec_tree_pack_query(**bad)
+    assert e.value.status == 1
+    assert tas.library().spec_last_error().decode()
+
+
+def test_pack_rejects_null_and_small_buffer(tas):
+    lib = tas.library()
+    from tree_attention_spec_amd import _lib
+    T = np.array([10], np.int32)
+    nb = np.array([1], np.int32)
+    a = np.array([3], np.int32)
+    w = np.array([4], np.int32)
+    P = lambda x: x.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    layout = _lib.spec_tree_layout()
+    size = ctypes.c_size_t(0)
+    # NULL anchors with branches
+    assert lib.spec_tree_pack(1, P(T), P(nb), None, P(w), None, ctypes.byref(size),
+                              ctypes.byref(layout), None) == 1
+    # NULL layout
+    assert lib.spec_tree_pack(1, P(T), P(nb), P(a), P(w), None, ctypes.byref(size), None, None) == 1
+    # a buffer that is too small is refused before any device work
+    assert lib.spec_tree_pack(1, P(T), P(nb), P(a), P(w), None, ctypes.byref(size),
+                              ctypes.byref(layout), None) == 0
+    need = size.value
+    small = ctypes.c_size_t(need - 4)
+    assert lib.spec_tree_pack(1, P(T), P(nb), P(a), P(w), ctypes.c_void_p(0x1000), ctypes.byref(small),
+                              ctypes.byref(layout), None) == 3
+    assert small.value == need
+
+
+def _query_layout(tas):
+    s = gen_structure(CONFIGS["gqa8b"])
+    layout, _ = tas.spec_tree_pack_query(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"])
+    return layout
+
+
+def test_attention_size_query_and_checks(tas):
+    lib = tas.library()
+    L = _query_layout(tas)
+    size = ctypes.c_size_t(0)
+    call = lambda hq, hkv, D, dt, base: lib.spec_tree_attn_fwd(
+        ctypes.byref(L), hq, hkv, D, dt, None, None, None, base, 0.0, None, None, None,
+        ctypes.byref(size), None)
+    assert call(32, 8, 128, 1, 10000.0) == 0
+    # table [max_pos+1][D/2] float2 plus rotated K [Hkv][N][D] bf16
+    assert size.value >= (L.max_pos + 1) * 64 * 8 + L.n_rows * 8 * 128 * 2
+    assert call(32, 7, 128, 1, 10000.0) == 1      # Hq % Hkv != 0
+    assert call(32, 8, 96, 1, 10000.0) == 2       # unsupported head_dim
+    assert call(32, 8, 128, 5, 10000.0) == 2      # unsupported dtype
+    assert call(32, 8, 128, 1, -1.0) == 1         # bad RoPE base
+    assert call(32, 8, 128, 0, 10000.0) == 0      # float32 path
+
+
+def test_e2etv_size_query_and_checks(tas):
+    lib = tas.library()
+    L = _query_layout(tas)
+    size = ctypes.c_size_t(0)
+    call = lambda V, dt, w: lib.spec_e2etv_fwd_bwd(ctypes.byref(L), V, dt, None, None, w, None, None,
+                                                   None, None, ctypes.byref(size), None)
+    assert call(151936, 1, 0.0) == 0 and size.value >= 4 * 4 * L.n_steps
+    assert call(0, 1, 0.0) == 1                   # empty vocabulary
+    assert call(151936, 3, 0.0) == 2              # unsupported dtype
+    assert call(151936, 1, float("nan")) == 1     # non-finite normaliser
+    # device pointers are required once a workspace is given (no HIP call is reached)
+    big = ctypes.c_size_t(1 << 30)
+    assert lib.spec_e2etv_fwd_bwd(ctypes.byref(L), 151936, 1, None, None, 0.0, None, None, None,
+                                  ctypes.c_void_p(0x1000), ctypes.byref(big), None) == 1
