@@ -43,6 +43,15 @@ struct AttnSmem {
 // of the next tile are issued before the current tile is computed (registers
 // hold them), and the LDS tiles are double-buffered, so one barrier per tile
 // suffices. Keys past `ke` read as zero.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ inline uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <int D, int NT>
 struct TileRegs {
   static constexpr int CH = D / 8;                       // 16-byte chunks per row
@@ -51,16 +60,20 @@ struct TileRegs {
   uint4 k[KPT];
   uint4 v[VPT][4];
 
+  // Buffer loads whose descriptor ends at key `ke`: keys past it read as zero
+  // without any per-load condition.
   __device__ inline void load(const __bf16 *__restrict__ kws, const __bf16 *__restrict__ vv, int g,
                               int hkv, int64_t n_rows, int k0, int ke, int tid) {
+    const __amdgpu_buffer_rsrc_t rk =
+        make_rsrc(kws + (int64_t)g * n_rows * D, (uint32_t)ke * D * 2);
+    const uint32_t vrow = (uint32_t)hkv * D * 2;  // bytes between consecutive keys of V
+    const __amdgpu_buffer_rsrc_t rv =
+        make_rsrc(vv + (int64_t)g * D, ke > 0 ? (uint32_t)(ke - 1) * vrow + D * 2 : 0u);
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c = tid + i * NT;
-      const int r = c / CH, col = c % CH;
-      const int key = k0 + r;
-      k[i] = make_uint4(0, 0, 0, 0);
-      if (c < KT * CH && key < ke)
-        k[i] = *reinterpret_cast<const uint4 *>(kws + ((int64_t)g * n_rows + key) * D + col * 8);
+      const uint32_t off = ((uint32_t)(k0 + c / CH) * D + (c % CH) * 8) * 2;
+      k[i] = (KPT * NT == KT * CH || c < KT * CH) ? load16(rk, off) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -68,10 +81,8 @@ struct TileRegs {
       const int kq = c % 16, col = c / 16;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int key = k0 + 4 * kq + e;
-        v[i][e] = make_uint4(0, 0, 0, 0);
-        if (c < 16 * CH && key < ke)
-          v[i][e] = *reinterpret_cast<const uint4 *>(vv + ((int64_t)key * hkv + g) * D + col * 8);
+        const uint32_t off = (uint32_t)(k0 + 4 * kq + e) * vrow + col * 16;
+        v[i][e] = (VPT * NT == 16 * CH || c < 16 * CH) ? load16(rv, off) : make_uint4(0, 0, 0, 0);
       }
     }
   }
@@ -206,17 +217,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], s1, 0, 0, 0);
       }
-      // accumulator i of tile t holds key k0 + 32t + 8(i/4) + 4*half + i%4
+      // accumulator i of tile t holds key k0 + 32t + 8(i/4) + 4*half + i%4; a lane sees the
+      // keys [vlo, vhi] of this range (its trunk prefix, or its own branch run)
       const bool need_mask = branch || (k0 + KT > it.tfull);
       if (need_mask) {
+        const int vlo = branch ? blo : it.tk0, vhi = branch ? bhi : thi;
+        const uint32_t span = (uint32_t)(vhi - vlo);
+        const int base = k0 + 4 * half - vlo;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key0 = k0 + 8 * (i >> 2) + 4 * half + (i & 3);
-          const int key1 = key0 + 32;
-          const bool v0 = branch ? (key0 >= blo && key0 <= bhi) : key0 <= thi;
-          const bool v1 = branch ? (key1 >= blo && key1 <= bhi) : key1 <= thi;
-          s0[i] = v0 ? s0[i] : -INFINITY;
-          s1[i] = v1 ? s1[i] : -INFINITY;
+          const int o0 = base + 8 * (i >> 2) + (i & 3);
+          s0[i] = (uint32_t)o0 <= span ? s0[i] : -INFINITY;
+          s1[i] = (uint32_t)(o0 + 32) <= span ? s1[i] : -INFINITY;
         }
       }
       float mx = -INFINITY;
