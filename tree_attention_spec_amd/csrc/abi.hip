@@ -64,9 +64,14 @@ AttnWork attn_work(const spec_tree_layout &L, int hkv, int D, spec_dtype dt) {
 
 }  // namespace
 
-size_t e2etv_work_bytes(int64_t R) { return 4 * align_up((size_t)R * sizeof(float), 256); }
+// Workspace of E2E-TV: four float arrays [R], then the indicator bitmask [R][bits_row].
+static size_t e2etv_bits_row(int64_t V) { return align_up((size_t)(V + 7) / 8, 16); }
 
-E2etvWork e2etv_carve(void *d_work, int64_t R) {
+size_t e2etv_work_bytes(int64_t R, int64_t V) {
+  return 4 * align_up((size_t)R * sizeof(float), 256) + align_up((size_t)R * e2etv_bits_row(V), 256);
+}
+
+E2etvWork e2etv_carve(void *d_work, int64_t R, int64_t V) {
   char *p = static_cast<char *>(d_work);
   const size_t step = align_up((size_t)R * sizeof(float), 256);
   E2etvWork w;
@@ -74,6 +79,8 @@ E2etvWork e2etv_carve(void *d_work, int64_t R) {
   w.lse_p2 = reinterpret_cast<float *>(p + step);
   w.S = reinterpret_cast<float *>(p + 2 * step);
   w.coef = reinterpret_cast<float *>(p + 3 * step);
+  w.bits = reinterpret_cast<uint8_t *>(p + 4 * step);
+  w.bits_row = (int64_t)e2etv_bits_row(V);
   return w;
 }
 
@@ -172,7 +179,7 @@ extern "C" spec_status spec_e2etv_fwd_bwd(const spec_tree_layout *layout, int64_
   if (dtype != SPEC_BF16 && dtype != SPEC_F32)
     return fail(SPEC_ERR_UNSUPPORTED, "logit dtype %d not supported", (int)dtype);
   if (!std::isfinite(inv_norm)) return fail(SPEC_ERR_INVALID_ARG, "inv_norm must be finite");
-  const size_t need = e2etv_work_bytes(layout->n_steps);
+  const size_t need = e2etv_work_bytes(layout->n_steps, vocab);
   if (!d_work) {
     *work_bytes = need;
     return SPEC_OK;
@@ -191,6 +198,6 @@ extern "C" spec_status spec_e2etv_fwd_bwd(const spec_tree_layout *layout, int64_
   hipStream_t s = static_cast<hipStream_t>(stream);
   prof_mark(s, "e2etv:begin");
   SPEC_HIP_TRY(launch_e2etv(*layout, vocab, dtype, d_draft, d_teacher, w, d_alpha, d_loss, d_grad,
-                            e2etv_carve(d_work, layout->n_steps), s));
+                            e2etv_carve(d_work, layout->n_steps, vocab), s));
   return SPEC_OK;
 }

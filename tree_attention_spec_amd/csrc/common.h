@@ -60,9 +60,11 @@ struct E2etvWork {
   float *lse_p2;   // [R] same for the teacher
   float *S;        // [R] sum of q over {q < p}
   float *coef;     // [R] dL/d alpha
+  uint8_t *bits;   // [R][bits_row] bit u of a row: 1 iff q_u < p_u (the set S is summed over)
+  int64_t bits_row;
 };
-size_t e2etv_work_bytes(int64_t n_steps);
-E2etvWork e2etv_carve(void *d_work, int64_t n_steps);
+size_t e2etv_work_bytes(int64_t n_steps, int64_t vocab);
+E2etvWork e2etv_carve(void *d_work, int64_t n_steps, int64_t vocab);
 hipError_t launch_e2etv(const spec_tree_layout &L, int64_t vocab, spec_dtype dtype,
                         const void *draft, const void *teacher, float inv_norm, float *alpha,
                         float *loss, float *grad, const E2etvWork &w, hipStream_t stream);
