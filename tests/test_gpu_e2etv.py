@@ -97,6 +97,40 @@ def test_e2etv_bf16_rows(vocab):
     _full_compare(case, z, y, inv_norm=0.01)
 
 
+def test_e2etv_bf16_nan_draft():
+    """bf16 rows with NaN draft entries (scattered and whole blocks, quiet, signalling
+    and negative NaN patterns) give the results of -inf entries."""
+    import torch
+    say("e2etv parity: bf16 NaN draft entries, vocab 151936")
+    case = Case(small_config("gqa8b", trunk=300, branches=3, width=5, vocab=151936))
+    z, y = case.logits()
+    assert z.dtype == np.uint16
+    rng = np.random.default_rng(5)
+    zn = z.copy()
+    pats = np.array([0x7FC0, 0x7F81, 0xFFC0, 0xFFFF], np.uint16)
+    idx = rng.choice(zn.shape[1], 1000, replace=False)
+    zn[0, idx] = pats[np.arange(idx.size) % 4]   # scattered
+    zn[1, 100000:] = 0x7FC0                     # a tail block (whole slices)
+    zn[2, :60000] = 0xFFC0                      # a head block
+    isnan = (zn & 0x7FFF) > 0x7F80
+    zi = np.where(isnan, np.uint16(0xFF80), zn).astype(np.uint16)
+    tree = _pack(case.s)
+    a1, l1, g1 = _run(tree, to_device(zn), to_device(y))
+    a2, l2, g2 = _run(tree, to_device(zi), to_device(y))
+    assert torch.equal(a1, a2) and torch.equal(l1, l2) and torch.equal(g1, g2)
+    assert torch.count_nonzero(g1[1, 100000:]).item() == 0
+    _full_compare(case, zi, y)
+
+
+@pytest.mark.parametrize("width", [1, 2, 4])
+def test_e2etv_bf16_few_rows(width):
+    """A handful of rows: teams with one or two rows (pipeline prologue and tail)."""
+    say("e2etv parity: bf16 vocab 151936, %d rows" % width)
+    case = Case(small_config("gqa8b", trunk=64, branches=1, width=width, vocab=151936))
+    z, y = case.logits()
+    _full_compare(case, z, y)
+
+
 def test_e2etv_forward_only_and_determinism():
     import torch
     case = Case(small_config("gqa8b", trunk=300, branches=5, width=16, vocab=151936))

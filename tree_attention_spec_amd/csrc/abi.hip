@@ -64,22 +64,41 @@ AttnWork attn_work(const spec_tree_layout &L, int hkv, int D, spec_dtype dt) {
 
 }  // namespace
 
-// Workspace of E2E-TV: four float arrays [R], then the indicator bitmask [R][bits_row].
+// Workspace of E2E-TV: four float arrays [R], the team partials [R][kTeamMax],
+// the team exchange slots [R][kTeamMax], a status word, then the indicator
+// bitmask [R][bits_row].
 static size_t e2etv_bits_row(int64_t V) { return align_up((size_t)(V + 7) / 8, 16); }
 
-size_t e2etv_work_bytes(int64_t R, int64_t V) {
-  return 4 * align_up((size_t)R * sizeof(float), 256) + align_up((size_t)R * e2etv_bits_row(V), 256);
+namespace {
+struct E2etvOffsets {
+  size_t step, part, xchg, status, bits, total;
+};
+E2etvOffsets e2etv_offsets(int64_t R, int64_t V) {
+  E2etvOffsets o;
+  o.step = align_up((size_t)R * sizeof(float), 256);
+  o.part = 4 * o.step;
+  o.xchg = o.part + align_up((size_t)R * kTeamMax * sizeof(float2), 256);
+  o.status = o.xchg + align_up((size_t)R * kTeamMax * sizeof(unsigned long long), 256);
+  o.bits = o.status + 256;
+  o.total = o.bits + align_up((size_t)R * e2etv_bits_row(V), 256);
+  return o;
 }
+}  // namespace
+
+size_t e2etv_work_bytes(int64_t R, int64_t V) { return e2etv_offsets(R, V).total; }
 
 E2etvWork e2etv_carve(void *d_work, int64_t R, int64_t V) {
   char *p = static_cast<char *>(d_work);
-  const size_t step = align_up((size_t)R * sizeof(float), 256);
+  const E2etvOffsets o = e2etv_offsets(R, V);
   E2etvWork w;
   w.lse_q2 = reinterpret_cast<float *>(p);
-  w.lse_p2 = reinterpret_cast<float *>(p + step);
-  w.S = reinterpret_cast<float *>(p + 2 * step);
-  w.coef = reinterpret_cast<float *>(p + 3 * step);
-  w.bits = reinterpret_cast<uint8_t *>(p + 4 * step);
+  w.lse_p2 = reinterpret_cast<float *>(p + o.step);
+  w.S = reinterpret_cast<float *>(p + 2 * o.step);
+  w.coef = reinterpret_cast<float *>(p + 3 * o.step);
+  w.part = reinterpret_cast<float2 *>(p + o.part);
+  w.xchg = reinterpret_cast<unsigned long long *>(p + o.xchg);
+  w.status = reinterpret_cast<unsigned *>(p + o.status);
+  w.bits = reinterpret_cast<uint8_t *>(p + o.bits);
   w.bits_row = (int64_t)e2etv_bits_row(V);
   return w;
 }

@@ -55,11 +55,17 @@ hipError_t launch_tree_attn(const spec_tree_layout &L, int32_t hq, int32_t hkv, 
 hipError_t launch_readout(const int32_t *pred_row, int64_t n_steps, int64_t row_bytes,
                           const void *out, void *readout, hipStream_t stream);
 
+// Statistics teams: at most kTeamMax members per row.
+constexpr int kTeamMax = 16;
+
 struct E2etvWork {
   float *lse_q2;   // [R] log2-domain log-sum-exp of the draft row
   float *lse_p2;   // [R] same for the teacher
   float *S;        // [R] sum of q over {q < p}
   float *coef;     // [R] dL/d alpha
+  float2 *part;    // [R][team] (alpha, S) partials of the members of a statistics team
+  unsigned long long *xchg;  // [R][team] log-sum-exp slots the members of a team exchange
+  unsigned *status;          // raised if a team exchange timed out
   uint8_t *bits;   // [R][bits_row] bit u of a row: 1 iff q_u < p_u (the set S is summed over)
   int64_t bits_row;
 };

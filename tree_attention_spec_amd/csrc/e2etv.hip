@@ -24,6 +24,8 @@
 // strict test z' < y' is the same expression in all three places, so the set
 // {q < p} used for S and for the gradient is the same set.
 #include <algorithm>
+#include <mutex>
+#include <type_traits>
 
 #include "common.h"
 
@@ -111,7 +113,7 @@ __device__ inline float block_sum(float x, float *red) {
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kStatThreads) void e2etv_stats_kernel(
     const T *__restrict__ draft, const T *__restrict__ teacher, int64_t n_rows, int64_t V,
-    float *__restrict__ alpha, float *__restrict__ S_out, float *__restrict__ lse_q2,
+    float2 *__restrict__ part, float *__restrict__ lse_q2,
     float *__restrict__ lse_p2, uint8_t *__restrict__ bits, int64_t bits_row) {
   __shared__ float red[2 * kStatThreads / 64];
   const int tid = threadIdx.x;
@@ -174,24 +176,431 @@ __global__ __launch_bounds__(kStatThreads) void e2etv_stats_kernel(
   al = block_sum<kStatThreads>(al, red);
   ss = block_sum<kStatThreads>(ss, red);
   if (tid == 0) {
-    alpha[row] = al;
-    S_out[row] = ss;
+    part[row] = make_float2(al, ss);
     lse_q2[row] = lz2;
     lse_p2[row] = ly2;
   }
   }
 }
 
-// One workgroup. c_s for every step; L in float64 with a fixed reduction order.
-__global__ __launch_bounds__(1024) void e2etv_scan_kernel(const int32_t *__restrict__ step_off,
-                                                         int32_t n_branches,
-                                                         const float *__restrict__ alpha,
-                                                         float w, float *__restrict__ coef,
-                                                         float *__restrict__ loss) {
+// ---------------------------------------------------------------------------
+// Single-read statistics for bf16 rows whose length is a multiple of 8.
+//
+// A cooperative grid is cut into teams of T workgroups (one per CU); team t
+// takes rows t, t + n_teams, ... and member j owns vector slice j of every
+// row, so every logit is read from HBM once. Each row goes through
+//   pass 1   (data waves) log2-sum-exp2 of z log2(e) and of y log2(e) per wave;
+//   exchange (sync wave) the wave values merge into the member's, which goes into
+//            the row's slot for this member; the other members' slots of the row
+//            are polled and merged in member order: lse2(z), lse2(y);
+//   pass 2   (data waves) alpha and S over the slice, and the indicator bits;
+// and the member's alpha and S go to part[row][j], which the scan kernel adds up
+// in member order. The work is a three-stage pipeline over three register
+// buffers: in step i the data waves run pass 1 of row i, then pass 2 of row
+// i - 1, then issue the loads of row i + 2 into the buffer row i - 1 has freed,
+// while the sync wave runs the exchange of row i. One workgroup barrier per
+// step separates them, so the exchange is hidden behind a pass of compute.
+//
+// The exchange runs in a wave of its own so that its loads never queue behind
+// the data waves' loads (a wave's loads complete in issue order). Slots are
+// 64-bit words, (lse2 z, lse2 y), written once per row by one atomic store and
+// cleared to all-ones before the launch; the all-ones pattern is no value a
+// member writes (NaNs are stored canonical). Agent-scope atomic loads and stores
+// reach the coherence point, so they are seen across XCDs, whose L2s are not
+// coherent with each other, without an L2 writeback or invalidate. The poll is
+// bounded: on a timeout the status word is raised, every member leaves, and the
+// scan kernel turns alpha and the loss into NaN.
+//
+// Every merge (lanes within a wave, waves within a member, members within a row)
+// is a fixed reduction tree, so results are bitwise reproducible.
+
+constexpr int kTeamThreads = 1024;
+constexpr int kTeamData = kTeamThreads - 64;  // 15 data waves; the last wave runs the exchange
+constexpr int kTeamDataWaves = kTeamData / 64;
+constexpr unsigned kTeamSpinLimit = 1u << 20;
+constexpr uint32_t kNegInf2 = 0xff80ff80u;    // two bf16 -inf
+constexpr unsigned long long kSlotEmpty = ~0ull;
+
+struct TeamArgs {
+  const __bf16 *z, *y;
+  int64_t R, V8;                // rows, 8-element vectors per row
+  int32_t T, n_teams;
+  float *lse_q2, *lse_p2;
+  float2 *part;                 // [R][T] (alpha, S) member partials
+  uint8_t *bits;
+  int64_t bits_row;
+  unsigned long long *xchg;     // [R][T] member (lse2 z, lse2 y) slots, all-ones until written
+  unsigned *status;
+};
+
+__device__ inline float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// Two more spellings of the bf16 -> f32 unpack, so that the compiler cannot keep
+// one pass's unpacked values alive for a later one (that would double the
+// registers a slice needs). v_perm_b32 picks bytes of {src0, src1}: 0-3 from
+// src1, 4-7 from src0, 0x0c gives a zero byte.
+__device__ inline float lo_p(uint32_t w) { return __uint_as_float(__builtin_amdgcn_perm(0u, w, 0x01000c0cu)); }
+__device__ inline float hi_p(uint32_t w) { return __uint_as_float(__builtin_amdgcn_perm(0u, w, 0x03020c0cu)); }
+__device__ inline float lo_q(uint32_t w) { return __uint_as_float(__builtin_amdgcn_perm(w, 0u, 0x05040c0cu)); }
+__device__ inline float hi_q(uint32_t w) { return __uint_as_float(__builtin_amdgcn_perm(w, 0u, 0x07060c0cu)); }
+__device__ inline uint32_t word(const uint4 &v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// Wave reductions in registers: DPP within rows of 16 lanes (xor 1, xor 2, then
+// the half-row and row mirrors), then the lane swaps across rows (l ^ 16, l ^ 32).
+// Every step combines a lane with its partner by a commutative operation, so
+// every lane ends with the same bits.
+template <int CTRL>
+__device__ inline float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ inline float dpp_sum(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  x += dpp<0x140>(x);  // row_mirror
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float dpp_max(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  x = fmaxf(x, dpp<0x140>(x));
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// log2 sum_lanes 2^l over a wave (l = -inf: no contribution).
+__device__ inline float wave_lse2(float l) {
+  const float M = dpp_max(l);
+  if (M == -INFINITY) return -INFINITY;
+  return M + log2f(dpp_sum(__builtin_amdgcn_exp2f(l - M)));
+}
+// Two bf16 in one word with NaN halves replaced by -inf (inactive draft support).
+__device__ inline uint32_t nan_to_neginf2(uint32_t w) {
+  if ((w & 0x7fffu) > 0x7f80u) w = (w & 0xffff0000u) | 0xff80u;
+  if (((w >> 16) & 0x7fffu) > 0x7f80u) w = (w & 0x0000ffffu) | 0xff800000u;
+  return w;
+}
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ inline __amdgpu_buffer_rsrc_t row_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// A row slice of one thread: VPL vectors of the draft and of the teacher.
+template <int VPL>
+struct Slice {
+  uint4 z[VPL], y[VPL];
+};
+
+// Issue the loads of this thread's vectors of row r (vector k at slice offset
+// tid + kTeamData k); nothing waits for the data here. Reads past the row end
+// return zero and are masked before use. With `valid` false the range is empty:
+// the loads are issued (so every path issues the same memory operations, which
+// keeps the compiler's wait counts exact) but read nothing.
+template <int VPL>
+__device__ inline void team_load(Slice<VPL> &b, const TeamArgs &a, int64_t r, uint32_t voff, bool valid) {
+  const uint32_t bytes = valid ? (uint32_t)(a.V8 * 16) : 0u;
+  r = valid ? r : 0;
+  const __amdgpu_buffer_rsrc_t rz = row_rsrc(a.z + r * a.V8 * 8, bytes);
+  const __amdgpu_buffer_rsrc_t ry = row_rsrc(a.y + r * a.V8 * 8, bytes);
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(rz, voff, k * kTeamData * 16, 0);
+    b.z[k] = make_uint4(u.x, u.y, u.z, u.w);
+  }
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(ry, voff, k * kTeamData * 16, 0);
+    b.y[k] = make_uint4(u.x, u.y, u.z, u.w);
+  }
+}
+
+// sum 2^(x log2 e + nm) over this thread's vectors.
+template <int VPL>
+__device__ inline float sum_shifted(const uint4 (&v)[VPL], float nm) {
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < VPL; ++k)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = word(v[k], i);
+      s += __builtin_amdgcn_exp2f(fmaf(lo_p(w), kLog2e, nm));
+      s += __builtin_amdgcn_exp2f(fmaf(hi_p(w), kLog2e, nm));
+    }
+  return s;
+}
+
+// Wave log2 sum 2^(x log2 e) of one array. The shift is the wave max of a
+// sample (every lane's first vector), which is at most the true max; if the
+// sum then overflows, or is NaN (a NaN draft entry), or the sample was empty,
+// the exact max is taken instead, after NaN draft entries become -inf in the
+// words themselves (pass 2 then sees them as -inf too).
+template <int VPL>
+__device__ inline float wave_lse2_of(uint4 (&v)[VPL], bool draft) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = word(v[0], i);
+    m = __builtin_fmaxf(__builtin_fmaxf(m, lo_f(w)), hi_f(w));
+  }
+  m = dpp_max(m);
+  float s = INFINITY;
+  if (m != -INFINITY) s = dpp_sum(sum_shifted<VPL>(v, -m * kLog2e));
+  if (!(s < INFINITY)) {  // wave-uniform
+    if (draft) {
+#pragma unroll
+      for (int k = 0; k < VPL; ++k)
+        v[k] = make_uint4(nan_to_neginf2(v[k].x), nan_to_neginf2(v[k].y), nan_to_neginf2(v[k].z),
+                          nan_to_neginf2(v[k].w));
+    }
+    m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = word(v[k], i);
+        m = __builtin_fmaxf(__builtin_fmaxf(m, lo_f(w)), hi_f(w));
+      }
+    m = dpp_max(m);
+    if (m == -INFINITY) return -INFINITY;
+    s = dpp_sum(sum_shifted<VPL>(v, -m * kLog2e));
+  }
+  return m * kLog2e + log2f(s);
+}
+
+// alpha and S sums of this thread's vectors, and their indicator bytes. The
+// bytes go through a buffer resource whose range is this member's slice of the
+// bitmask row, so stores of lanes past the slice are dropped by the hardware.
+template <int VPL>
+__device__ inline float2 team_alpha(const Slice<VPL> &b, float lz2, float ly2,
+                                    __amdgpu_buffer_rsrc_t brow, uint32_t tl) {
+  float al = 0.f, ss = 0.f, nz = -lz2, ny = -ly2;
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 7; j >= 0; --j) {  // element j ends up in bit j
+      const uint32_t wz = word(b.z[k], j >> 1), wy = word(b.y[k], j >> 1);
+      const float za = fmaf((j & 1) ? hi_q(wz) : lo_q(wz), kLog2e, nz);
+      const float yb = fmaf((j & 1) ? hi_q(wy) : lo_q(wy), kLog2e, ny);
+      const float e = __builtin_amdgcn_exp2f(fminf(za, yb));
+      const bool in = za < yb;
+      al += e;
+      ss += in ? e : 0.f;
+      m = m + m + (uint32_t)in;
+    }
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)m, brow, tl, k * kTeamData, 0);
+    // one vector at a time: the next vector's work depends on this vector's sums,
+    // so the scheduler cannot hoist every compare ahead of the exponentials
+    asm volatile("" : "+v"(al), "+v"(ss), "+v"(nz), "+v"(ny));
+  }
+  return make_float2(al, ss);
+}
+
+__device__ inline unsigned long long pack_slot(float lz, float ly) {
+  if (lz != lz) lz = __uint_as_float(0x7fc00000u);  // canonical NaN, never the empty pattern
+  if (ly != ly) ly = __uint_as_float(0x7fc00000u);
+  return ((unsigned long long)__float_as_uint(ly) << 32) | __float_as_uint(lz);
+}
+
+struct TeamCtx {
+  int64_t vb;          // first vector of this member's slice
+  uint32_t n;          // vectors in the slice
+  uint32_t voff;       // byte offset of this thread's first vector in a row
+  int64_t r0, nr;      // first row of the team, rows of the team (stride n_teams)
+  int mem, team;
+};
+
+struct TeamShared {
+  float2 w[2][kTeamDataWaves];   // wave (lse2 z, lse2 y) of a row, by row parity
+  float2 as[2][kTeamDataWaves];  // wave (alpha, S) of a row, by row parity
+  float2 l[2];                   // row (lse2 z, lse2 y), by row parity
+};
+
+// Exchange of row r (sync wave): merge the wave values, publish, poll, merge.
+__device__ inline bool team_exchange(const TeamArgs &a, const TeamCtx &c, int64_t r, int par,
+                                     TeamShared &sh) {
+  const int lane = threadIdx.x & 63, T = a.T;
+  float2 p = make_float2(-INFINITY, -INFINITY);
+  if (lane < kTeamDataWaves) p = sh.w[par][lane];
+  const float mz = wave_lse2(p.x), my = wave_lse2(p.y);
+  unsigned long long *slots = a.xchg + r * T;
+  if (lane == 0)
+    __hip_atomic_store(slots + c.mem, pack_slot(mz, my), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  unsigned long long v = kSlotEmpty;
+  unsigned spins = 0;
+  for (;;) {
+    if (lane < T && v == kSlotEmpty)
+      v = __hip_atomic_load(slots + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!__any(lane < T && v == kSlotEmpty)) break;
+    unsigned bad = 0;
+    if (lane == 63) bad = __hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__shfl(bad, 63) != 0u || ++spins > kTeamSpinLimit) {
+      if (lane == 0) __hip_atomic_store(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  const float gz = lane < T ? __uint_as_float((uint32_t)v) : -INFINITY;
+  const float gy = lane < T ? __uint_as_float((uint32_t)(v >> 32)) : -INFINITY;
+  const float lz2 = wave_lse2(gz), ly2 = wave_lse2(gy);
+  if (lane == 0) {
+    sh.l[par] = make_float2(lz2, ly2);
+    if (c.mem == 0) {
+      a.lse_q2[r] = lz2;
+      a.lse_p2[r] = ly2;
+    }
+  }
+  return true;
+}
+
+// The member's (alpha, S) of a row from the wave values (sync wave).
+__device__ inline void team_flush(const TeamArgs &a, const TeamCtx &c, int64_t r, int par,
+                                  const TeamShared &sh) {
+  const int lane = threadIdx.x & 63;
+  float2 q = make_float2(0.f, 0.f);
+  if (lane < kTeamDataWaves) q = sh.as[par][lane];
+  q.x = dpp_sum(q.x);
+  q.y = dpp_sum(q.y);
+  if (lane == 0) a.part[r * a.T + c.mem] = q;
+}
+
+// Pass 1 of row i in `cur` (if the team has a row i) and the step's workgroup
+// barrier, in a data wave.
+template <int VPL>
+__device__ inline void data_pass1(Slice<VPL> &cur, const TeamCtx &c, int64_t i, TeamShared &sh,
+                                  int wv, uint32_t tl) {
+  if (i < c.nr) {
+#pragma unroll
+    for (int k = 0; k < VPL; ++k)
+      if ((uint32_t)((k + 1) * kTeamData) > c.n && tl + (uint32_t)(k * kTeamData) >= c.n) {
+        cur.z[k] = make_uint4(kNegInf2, kNegInf2, kNegInf2, kNegInf2);
+        cur.y[k] = cur.z[k];
+      }
+    const float lz = wave_lse2_of<VPL>(cur.z, true);
+    const float ly = wave_lse2_of<VPL>(cur.y, false);
+    if ((threadIdx.x & 63) == 0) sh.w[i & 1][wv] = make_float2(lz, ly);
+  }
+  __syncthreads();
+}
+
+// Step i >= 1 of the pipeline in a data wave: pass 1 of row i in `cur`, the
+// barrier, pass 2 of row i - 1 in `old`, then the loads of row i + 2 into `old`.
+// Steps past the team's rows still issue the same memory operations, through
+// empty buffer ranges that read and write nothing, so the loop has no branch
+// around a memory operation and no early exit: the compiler's wait counts then
+// see the true age of each buffer's loads (the next buffer's loads stay in
+// flight while a row is worked on).
+template <int VPL>
+__device__ inline void data_step(Slice<VPL> &cur, Slice<VPL> &old, const TeamArgs &a,
+                                 const TeamCtx &c, int64_t i, TeamShared &sh, int wv) {
+  // Slice-local vector index of this thread; laundered so that the per-vector
+  // slice tests are made here rather than kept in scalar registers across steps.
+  uint32_t tl = threadIdx.x;
+  asm volatile("" : "+v"(tl));
+  data_pass1<VPL>(cur, c, i, sh, wv, tl);
+  const int64_t r = c.r0 + i * a.n_teams;
+  const bool has2 = i <= c.nr;  // row i - 1 is one of the team's
+  const float2 l = sh.l[(i - 1) & 1];
+  const __amdgpu_buffer_rsrc_t brow =
+      row_rsrc(has2 ? a.bits + (r - a.n_teams) * a.bits_row + c.vb : a.bits, has2 ? c.n : 0u);
+  float2 as = team_alpha<VPL>(old, l.x, l.y, brow, tl);
+  as.x = dpp_sum(as.x);
+  as.y = dpp_sum(as.y);
+  if ((threadIdx.x & 63) == 0) sh.as[(i - 1) & 1][wv] = as;
+  team_load<VPL>(old, a, r + 2 * a.n_teams, c.voff, i + 2 < c.nr);
+}
+
+// The data waves and the sync wave run separate loops (the branch is uniform
+// per wave) that meet at the same workgroup barriers, one per step; keeping the
+// two codes apart also keeps the compiler from waiting on the data waves'
+// in-flight loads where the paths would otherwise merge. The steps after the
+// first run in groups of three (one per buffer rotation), the last group padded
+// with steps that have no row. A failed exchange only raises the status word
+// (the results are then NaN); every wave still runs all steps, so the barriers
+// always pair up.
+template <int VPL>
+__global__ __launch_bounds__(kTeamThreads) void e2etv_stats_team_kernel(TeamArgs a) {
+  __shared__ TeamShared sh;
+  TeamCtx c;
+  c.team = blockIdx.x / a.T;
+  c.mem = blockIdx.x % a.T;
+  if (c.team >= a.n_teams) return;
+  c.vb = a.V8 * c.mem / a.T;
+  c.n = (uint32_t)(a.V8 * (c.mem + 1) / a.T - c.vb);
+  c.voff = (uint32_t)((c.vb + threadIdx.x) * 16);
+  c.r0 = c.team;
+  c.nr = (a.R - c.team + a.n_teams - 1) / a.n_teams;
+  if (c.nr <= 0) return;
+  const int64_t last = 3 * ((c.nr + 2) / 3);  // final step: steps 1..last fill whole groups
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wv < kTeamDataWaves) {
+    Slice<VPL> A, B, C;
+    team_load<VPL>(A, a, c.r0, c.voff, true);
+    team_load<VPL>(B, a, c.r0 + a.n_teams, c.voff, c.nr > 1);
+    // step 0: pass 1 of the first row only
+    uint32_t tl = threadIdx.x;
+    asm volatile("" : "+v"(tl));
+    data_pass1<VPL>(A, c, 0, sh, wv, tl);
+    team_load<VPL>(C, a, c.r0 + 2 * a.n_teams, c.voff, c.nr > 2);
+    // rows rotate through A, B, C: step i runs pass 1 in buffer i % 3 and pass 2
+    // (then the next loads) in buffer (i + 2) % 3
+    for (int64_t i = 1; i <= last; i += 3) {
+      data_step<VPL>(B, A, a, c, i, sh, wv);
+      data_step<VPL>(C, B, a, c, i + 1, sh, wv);
+      data_step<VPL>(A, C, a, c, i + 2, sh, wv);
+    }
+    __syncthreads();
+  } else {
+    bool ok = true;
+    for (int64_t i = 0; i <= last; ++i) {
+      const int64_t r = c.r0 + i * a.n_teams;
+      __syncthreads();
+      if (i >= 2 && i - 2 < c.nr) team_flush(a, c, r - 2 * a.n_teams, i & 1, sh);
+      if (ok && i < c.nr) ok = team_exchange(a, c, r, i & 1, sh);
+    }
+    __syncthreads();
+    if (c.nr + 1 > last)  // row nr - 1 had no step i = nr + 1 to flush it
+      team_flush(a, c, c.r0 + (c.nr - 1) * a.n_teams, (int)((c.nr - 1) & 1), sh);
+  }
+}
+
+// Slots to the empty pattern and the status word to zero, before a team launch.
+__global__ void e2etv_team_clear(unsigned long long *xchg, int64_t n, unsigned *status) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    xchg[i] = kSlotEmpty;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0u;
+}
+
+// One workgroup. alpha_s and S_s from the member partials (member order), c_s
+// for every step, and L in float64 with a fixed reduction order. A raised
+// status word (a statistics team barrier that timed out) makes alpha and L NaN.
+__global__ __launch_bounds__(1024) void e2etv_scan_kernel(
+    const int32_t *__restrict__ step_off, int32_t n_branches, const float2 *__restrict__ part,
+    int32_t team, const unsigned *__restrict__ status, float w, float *__restrict__ alpha,
+    float *__restrict__ S, float *__restrict__ coef, float *__restrict__ loss) {
   __shared__ double red[1024 / 64];
-  double part = 0.0;
+  const bool failed = status != nullptr && *status != 0u;
+  double part_sum = 0.0;
   for (int b = threadIdx.x; b < n_branches; b += blockDim.x) {
     const int s0 = step_off[b], s1 = step_off[b + 1];
+    for (int s = s0; s < s1; ++s) {
+      float al = 0.f, ss = 0.f;
+      for (int j = 0; j < team; ++j) {
+        const float2 p = part[(int64_t)s * team + j];
+        al += p.x;
+        ss += p.y;
+      }
+      alpha[s] = failed ? NAN : al;
+      S[s] = ss;
+    }
     // G_{W} = 1, G_i = 1 + alpha_{i+1} G_{i+1}; park G_i in coef
     double G = 1.0;
     for (int s = s1 - 1; s >= s0; --s) {
@@ -206,16 +615,16 @@ __global__ __launch_bounds__(1024) void e2etv_scan_kernel(const int32_t *__restr
       A *= (double)alpha[s];
       sumA += A;
     }
-    part += sumA;
+    part_sum += sumA;
   }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part;
+  for (int off = 32; off >= 1; off >>= 1) part_sum += __shfl_xor(part_sum, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part_sum;
   __syncthreads();
   if (threadIdx.x == 0) {
     double t = 0.0;
     for (int k = 0; k < (int)(blockDim.x >> 6); ++k) t += red[k];
-    loss[0] = (float)(1.0 - (double)w * t);
+    loss[0] = failed ? NAN : (float)(1.0 - (double)w * t);
   }
 }
 
@@ -272,6 +681,87 @@ __global__ __launch_bounds__(kGradThreads) void e2etv_grad_kernel(
 
 namespace {
 
+constexpr int kTeamMaxVpl = 3;  // vectors per lane and array; three row buffers live per lane
+
+struct TeamDevice {
+  bool init = false;
+  int cus = 0, coop = 0;
+  int occ[kTeamMaxVpl + 1] = {};
+};
+
+template <int VPL>
+int team_occupancy() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void *)e2etv_stats_team_kernel<VPL>,
+                                                   kTeamThreads, 0) != hipSuccess)
+    n = 0;
+  return n;
+}
+
+// Device properties and team-kernel occupancy, looked up once per device.
+TeamDevice team_device(int dev) {
+  static std::mutex mu;
+  static TeamDevice cache[64];
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev < 0 || dev >= 64) return TeamDevice{};
+  TeamDevice &d = cache[dev];
+  if (!d.init) {
+    hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    hipDeviceGetAttribute(&d.coop, hipDeviceAttributeCooperativeLaunch, dev);
+    d.occ[1] = team_occupancy<1>();
+    d.occ[2] = team_occupancy<2>();
+    d.occ[3] = team_occupancy<3>();
+    d.init = true;
+  }
+  return d;
+}
+
+// Single-read statistics if the rows fit a team; *team = 0 if they do not.
+hipError_t launch_team_stats(int64_t R, int64_t V, const void *draft, const void *teacher,
+                             const E2etvWork &ws, hipStream_t s, int *team) {
+  *team = 0;
+  const int64_t V8 = V / 8;
+  const int64_t per_member = (int64_t)kTeamData * kTeamMaxVpl;
+  const int64_t T = (V8 + per_member - 1) / per_member;
+  if (T < 1 || T > kTeamMax || V8 * 16 > INT32_MAX) return hipSuccess;
+  const int vpl = (int)(((V8 + T - 1) / T + kTeamData - 1) / kTeamData);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const TeamDevice d = team_device(dev);
+  if (!d.coop || d.cus < 1 || d.occ[vpl] < 1) return hipSuccess;
+  const int64_t n_teams = std::min<int64_t>((int64_t)d.occ[vpl] * d.cus / T, R);
+  if (n_teams < 1) return hipSuccess;
+  const int64_t n_slots = R * T;
+  hipLaunchKernelGGL(e2etv_team_clear, dim3((unsigned)std::min<int64_t>(256, (n_slots + 255) / 256)), dim3(256),
+                     0, s, ws.xchg, n_slots, ws.status);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  TeamArgs a;
+  a.z = static_cast<const __bf16 *>(draft);
+  a.y = static_cast<const __bf16 *>(teacher);
+  a.R = R;
+  a.V8 = V8;
+  a.T = (int32_t)T;
+  a.n_teams = (int32_t)n_teams;
+  a.lse_q2 = ws.lse_q2;
+  a.lse_p2 = ws.lse_p2;
+  a.part = ws.part;
+  a.bits = ws.bits;
+  a.bits_row = ws.bits_row;
+  a.xchg = ws.xchg;
+  a.status = ws.status;
+  void *args[] = {&a};
+  static_assert(kTeamMaxVpl == 3, "one instantiation per vectors-per-lane count");
+  const void *fn = vpl == 1   ? (const void *)e2etv_stats_team_kernel<1>
+                   : vpl == 2 ? (const void *)e2etv_stats_team_kernel<2>
+                              : (const void *)e2etv_stats_team_kernel<3>;
+  e = hipLaunchCooperativeKernel(fn, dim3((unsigned)(n_teams * T)), dim3(kTeamThreads), args, 0, s);
+  if (e != hipSuccess) return e;
+  *team = (int)T;
+  return hipSuccess;
+}
+
 template <typename T, bool VEC>
 hipError_t launch_typed(const spec_tree_layout &L, int64_t V, const void *draft,
                         const void *teacher, float w, float *alpha, float *loss, float *grad,
@@ -279,19 +769,30 @@ hipError_t launch_typed(const spec_tree_layout &L, int64_t V, const void *draft,
   const T *z = static_cast<const T *>(draft);
   const T *y = static_cast<const T *>(teacher);
   const int64_t R = L.n_steps;
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(R, cus));
-  hipLaunchKernelGGL((e2etv_stats_kernel<T, VEC>), dim3((unsigned)grid), dim3(kStatThreads), 0, s, z,
-                     y, R, V, alpha, ws.S, ws.lse_q2, ws.lse_p2, ws.bits, ws.bits_row);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  int team = 0;
+  hipError_t e = hipSuccess;
+  const unsigned *status = nullptr;
+  if (std::is_same<T, __bf16>::value && VEC) {
+    e = launch_team_stats(R, V, draft, teacher, ws, s, &team);
+    if (e != hipSuccess) return e;
+    if (team) status = ws.status;
+  }
+  if (!team) {
+    int dev = 0, cus = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(R, cus));
+    hipLaunchKernelGGL((e2etv_stats_kernel<T, VEC>), dim3((unsigned)grid), dim3(kStatThreads), 0, s,
+                       z, y, R, V, ws.part, ws.lse_q2, ws.lse_p2, ws.bits, ws.bits_row);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    team = 1;
+  }
   prof_mark(s, "e2etv_stats");
   hipLaunchKernelGGL(e2etv_scan_kernel, dim3(1), dim3(1024), 0, s, L.step_off, L.n_branches,
-                     alpha, w, ws.coef, loss);
+                     ws.part, team, status, w, alpha, ws.S, ws.coef, loss);
   e = hipGetLastError();
   if (e != hipSuccess || !grad) return e;
   prof_mark(s, "e2etv_scan");
