@@ -275,6 +275,17 @@ __device__ inline float dpp_max(float x) {
   r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// Sum over each row of 16 lanes (the first four steps of dpp_sum); every lane
+// of a row ends with the same bits.
+__device__ inline float row16_sum(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
+  return x;
+}
+constexpr int kTeamRows = kTeamDataWaves * 4;  // 16-lane rows of the data waves
+
 // log2 sum_lanes 2^l over a wave (l = -inf: no contribution).
 __device__ inline float wave_lse2(float l) {
   const float M = dpp_max(l);
@@ -337,30 +348,35 @@ __device__ inline float sum_shifted(const uint4 (&v)[VPL], float nm) {
   return s;
 }
 
-// Wave log2 sum 2^(x log2 e) of one array. The shift is the wave max of a
-// sample (every lane's first vector), which is at most the true max; if the
-// sum then overflows, or is NaN (a NaN draft entry), or the sample was empty,
-// the exact max is taken instead, after NaN draft entries become -inf in the
-// words themselves (pass 2 then sees them as -inf too).
+// log2 sum 2^(x log2 e) of one array over each 16-lane row of the wave, each
+// element taken as 2^(x log2 e - c) with a wave-uniform shift c (log2 units).
+// c comes from the caller (an earlier row's log-sum-exp) or, if it is -inf,
+// from the wave max of a sample (every lane's first vector). If any row's sum
+// then leaves [2^-60, 2^64) - too far from the row's own scale for full
+// precision, an overflow, or a NaN (a NaN draft entry) - the wave takes the
+// exact wave max as the shift instead, after NaN draft entries become -inf in
+// the words themselves (pass 2 then sees them as -inf too).
 template <int VPL>
-__device__ inline float wave_lse2_of(uint4 (&v)[VPL], bool draft) {
-  float m = -INFINITY;
+__device__ inline float rows_lse2_of(uint4 (&v)[VPL], bool draft, float c) {
+  if (c == -INFINITY) {  // wave-uniform
+    float m = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w = word(v[0], i);
-    m = __builtin_fmaxf(__builtin_fmaxf(m, lo_f(w)), hi_f(w));
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = word(v[0], i);
+      m = __builtin_fmaxf(__builtin_fmaxf(m, lo_f(w)), hi_f(w));
+    }
+    c = dpp_max(m) * kLog2e;
   }
-  m = dpp_max(m);
-  float s = INFINITY;
-  if (m != -INFINITY) s = dpp_sum(sum_shifted<VPL>(v, -m * kLog2e));
-  if (!(s < INFINITY)) {  // wave-uniform
+  float s = 0.f;
+  if (c > -INFINITY && c < INFINITY) s = row16_sum(sum_shifted<VPL>(v, -c));
+  if (__any(!(s >= 0x1p-60f && s < 0x1p64f))) {  // wave-uniform
     if (draft) {
 #pragma unroll
       for (int k = 0; k < VPL; ++k)
         v[k] = make_uint4(nan_to_neginf2(v[k].x), nan_to_neginf2(v[k].y), nan_to_neginf2(v[k].z),
                           nan_to_neginf2(v[k].w));
     }
-    m = -INFINITY;
+    float m = -INFINITY;
 #pragma unroll
     for (int k = 0; k < VPL; ++k)
 #pragma unroll
@@ -370,9 +386,10 @@ __device__ inline float wave_lse2_of(uint4 (&v)[VPL], bool draft) {
       }
     m = dpp_max(m);
     if (m == -INFINITY) return -INFINITY;
-    s = dpp_sum(sum_shifted<VPL>(v, -m * kLog2e));
+    c = m * kLog2e;
+    s = row16_sum(sum_shifted<VPL>(v, -c));
   }
-  return m * kLog2e + log2f(s);
+  return c + log2f(s);  // -inf for a row with no active element
 }
 
 // alpha and S sums of this thread's vectors, and their indicator bytes. The
@@ -391,10 +408,16 @@ __device__ inline float2 team_alpha(const Slice<VPL> &b, float lz2, float ly2,
       const float za = fmaf((j & 1) ? hi_q(wz) : lo_q(wz), kLog2e, nz);
       const float yb = fmaf((j & 1) ? hi_q(wy) : lo_q(wy), kLog2e, ny);
       const float e = __builtin_amdgcn_exp2f(fminf(za, yb));
-      const bool in = za < yb;
+      // in = za < yb; t = in ? e : 0; m = 2 m + in (the carry-in is the compare)
+      float t;
+      asm("v_cmp_lt_f32 vcc, %2, %3\n\t"
+          "v_cndmask_b32 %1, 0, %4, vcc\n\t"
+          "v_addc_co_u32 %0, vcc, %0, %0, vcc"
+          : "+v"(m), "=&v"(t)
+          : "v"(za), "v"(yb), "v"(e)
+          : "vcc");
       al += e;
-      ss += in ? e : 0.f;
-      m = m + m + (uint32_t)in;
+      ss += t;
     }
     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)m, brow, tl, k * kTeamData, 0);
     // one vector at a time: the next vector's work depends on this vector's sums,
@@ -419,21 +442,31 @@ struct TeamCtx {
 };
 
 struct TeamShared {
-  float2 w[2][kTeamDataWaves];   // wave (lse2 z, lse2 y) of a row, by row parity
-  float2 as[2][kTeamDataWaves];  // wave (alpha, S) of a row, by row parity
-  float2 l[2];                   // row (lse2 z, lse2 y), by row parity
+  float2 w[2][kTeamRows];        // 16-lane row (lse2 z, lse2 y) of a logit row, by row parity
+  float2 as[2][kTeamRows];       // 16-lane row (alpha, S) of a logit row, by row parity
+  float2 l[4];                   // logit row (lse2 z, lse2 y), by row mod 4
 };
 
-// Exchange of row r (sync wave): merge the wave values, publish, poll, merge.
-__device__ inline bool team_exchange(const TeamArgs &a, const TeamCtx &c, int64_t r, int par,
-                                     TeamShared &sh) {
-  const int lane = threadIdx.x & 63, T = a.T;
+// Exchange of a row (sync wave), in two halves a step apart. publish: merge
+// the wave values into the member's and store it into the row's slot.
+__device__ inline void team_publish(const TeamArgs &a, const TeamCtx &c, int64_t r, int par,
+                                    const TeamShared &sh) {
+  const int lane = threadIdx.x & 63;
   float2 p = make_float2(-INFINITY, -INFINITY);
-  if (lane < kTeamDataWaves) p = sh.w[par][lane];
+  if (lane < kTeamRows) p = sh.w[par][lane];
   const float mz = wave_lse2(p.x), my = wave_lse2(p.y);
-  unsigned long long *slots = a.xchg + r * T;
   if (lane == 0)
-    __hip_atomic_store(slots + c.mem, pack_slot(mz, my), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.xchg + r * a.T + c.mem, pack_slot(mz, my), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// collect: poll the row's slots until every member's is written, merge them in
+// member order into sh.l[slot]; member 0 also stores the row's values. False
+// if the poll timed out (or another team's did).
+__device__ inline bool team_collect(const TeamArgs &a, const TeamCtx &c, int64_t r, int slot,
+                                    TeamShared &sh) {
+  const int lane = threadIdx.x & 63, T = a.T;
+  const unsigned long long *slots = a.xchg + r * T;
   unsigned long long v = kSlotEmpty;
   unsigned spins = 0;
   for (;;) {
@@ -452,7 +485,7 @@ __device__ inline bool team_exchange(const TeamArgs &a, const TeamCtx &c, int64_
   const float gy = lane < T ? __uint_as_float((uint32_t)(v >> 32)) : -INFINITY;
   const float lz2 = wave_lse2(gz), ly2 = wave_lse2(gy);
   if (lane == 0) {
-    sh.l[par] = make_float2(lz2, ly2);
+    sh.l[slot] = make_float2(lz2, ly2);
     if (c.mem == 0) {
       a.lse_q2[r] = lz2;
       a.lse_p2[r] = ly2;
@@ -466,7 +499,7 @@ __device__ inline void team_flush(const TeamArgs &a, const TeamCtx &c, int64_t r
                                   const TeamShared &sh) {
   const int lane = threadIdx.x & 63;
   float2 q = make_float2(0.f, 0.f);
-  if (lane < kTeamDataWaves) q = sh.as[par][lane];
+  if (lane < kTeamRows) q = sh.as[par][lane];
   q.x = dpp_sum(q.x);
   q.y = dpp_sum(q.y);
   if (lane == 0) a.part[r * a.T + c.mem] = q;
@@ -476,7 +509,7 @@ __device__ inline void team_flush(const TeamArgs &a, const TeamCtx &c, int64_t r
 // barrier, in a data wave.
 template <int VPL>
 __device__ inline void data_pass1(Slice<VPL> &cur, const TeamCtx &c, int64_t i, TeamShared &sh,
-                                  int wv, uint32_t tl) {
+                                  int wv, uint32_t tl, float2 shift) {
   if (i < c.nr) {
 #pragma unroll
     for (int k = 0; k < VPL; ++k)
@@ -484,20 +517,20 @@ __device__ inline void data_pass1(Slice<VPL> &cur, const TeamCtx &c, int64_t i, 
         cur.z[k] = make_uint4(kNegInf2, kNegInf2, kNegInf2, kNegInf2);
         cur.y[k] = cur.z[k];
       }
-    const float lz = wave_lse2_of<VPL>(cur.z, true);
-    const float ly = wave_lse2_of<VPL>(cur.y, false);
-    if ((threadIdx.x & 63) == 0) sh.w[i & 1][wv] = make_float2(lz, ly);
+    const float lz = rows_lse2_of<VPL>(cur.z, true, shift.x);
+    const float ly = rows_lse2_of<VPL>(cur.y, false, shift.y);
+    if ((threadIdx.x & 15) == 0) sh.w[i & 1][wv * 4 + ((threadIdx.x & 63) >> 4)] = make_float2(lz, ly);
   }
   __syncthreads();
 }
 
-// Step i >= 1 of the pipeline in a data wave: pass 1 of row i in `cur`, the
-// barrier, pass 2 of row i - 1 in `old`, then the loads of row i + 2 into `old`.
+// Step i >= 2 of the pipeline in a data wave: pass 1 of row i in `cur`, the
+// barrier, pass 2 of row i - 2 in `old`, then the loads of row i + 2 into `old`.
 // Steps past the team's rows still issue the same memory operations, through
 // empty buffer ranges that read and write nothing, so the loop has no branch
 // around a memory operation and no early exit: the compiler's wait counts then
-// see the true age of each buffer's loads (the next buffer's loads stay in
-// flight while a row is worked on).
+// see the true age of each buffer's loads (later buffers' loads stay in flight
+// while a row is worked on).
 template <int VPL>
 __device__ inline void data_step(Slice<VPL> &cur, Slice<VPL> &old, const TeamArgs &a,
                                  const TeamCtx &c, int64_t i, TeamShared &sh, int wv) {
@@ -505,27 +538,36 @@ __device__ inline void data_step(Slice<VPL> &cur, Slice<VPL> &old, const TeamArg
   // slice tests are made here rather than kept in scalar registers across steps.
   uint32_t tl = threadIdx.x;
   asm volatile("" : "+v"(tl));
-  data_pass1<VPL>(cur, c, i, sh, wv, tl);
+  // the shift of pass 1: the log-sum-exps of row i - 3, the latest this step can see
+  data_pass1<VPL>(cur, c, i, sh, wv, tl, i >= 3 ? sh.l[(i - 3) & 3] : make_float2(-INFINITY, -INFINITY));
   const int64_t r = c.r0 + i * a.n_teams;
-  const bool has2 = i <= c.nr;  // row i - 1 is one of the team's
-  const float2 l = sh.l[(i - 1) & 1];
+  const bool has2 = i - 2 < c.nr;  // row i - 2 is one of the team's
+  const float2 l = sh.l[(i - 2) & 3];
   const __amdgpu_buffer_rsrc_t brow =
-      row_rsrc(has2 ? a.bits + (r - a.n_teams) * a.bits_row + c.vb : a.bits, has2 ? c.n : 0u);
+      row_rsrc(has2 ? a.bits + (r - 2 * a.n_teams) * a.bits_row + c.vb : a.bits, has2 ? c.n : 0u);
   float2 as = team_alpha<VPL>(old, l.x, l.y, brow, tl);
-  as.x = dpp_sum(as.x);
-  as.y = dpp_sum(as.y);
-  if ((threadIdx.x & 63) == 0) sh.as[(i - 1) & 1][wv] = as;
+  as.x = row16_sum(as.x);
+  as.y = row16_sum(as.y);
+  if ((threadIdx.x & 15) == 0) sh.as[i & 1][wv * 4 + ((threadIdx.x & 63) >> 4)] = as;
   team_load<VPL>(old, a, r + 2 * a.n_teams, c.voff, i + 2 < c.nr);
 }
 
 // The data waves and the sync wave run separate loops (the branch is uniform
 // per wave) that meet at the same workgroup barriers, one per step; keeping the
 // two codes apart also keeps the compiler from waiting on the data waves'
-// in-flight loads where the paths would otherwise merge. The steps after the
-// first run in groups of three (one per buffer rotation), the last group padded
-// with steps that have no row. A failed exchange only raises the status word
-// (the results are then NaN); every wave still runs all steps, so the barriers
-// always pair up.
+// in-flight loads where the paths would otherwise merge.
+//
+// Pipeline, four row buffers A, B, C, D (row i in buffer i % 4):
+//   data step i:  pass 1 of row i | barrier | pass 2 of row i - 2, then the
+//                 loads of row i + 2 into the buffer row i - 2 has freed;
+//   sync step i:  barrier | (alpha, S) of row i - 3 to part | publish row i |
+//                 collect row i - 1 (whose slots the other members wrote in
+//                 their step i - 1, so the poll rarely waits).
+// A row's log-sum-exps are ready one step before its pass 2 needs them. The
+// steps from 2 on run in groups of four (one per buffer rotation), the last
+// group padded with steps that have no row. A failed exchange only raises the
+// status word (the results are then NaN); every wave still runs all steps, so
+// the barriers always pair up.
 template <int VPL>
 __global__ __launch_bounds__(kTeamThreads) void e2etv_stats_team_kernel(TeamArgs a) {
   __shared__ TeamShared sh;
@@ -539,35 +581,41 @@ __global__ __launch_bounds__(kTeamThreads) void e2etv_stats_team_kernel(TeamArgs
   c.r0 = c.team;
   c.nr = (a.R - c.team + a.n_teams - 1) / a.n_teams;
   if (c.nr <= 0) return;
-  const int64_t last = 3 * ((c.nr + 2) / 3);  // final step: steps 1..last fill whole groups
+  const int64_t last = 4 * ((c.nr + 3) / 4) + 1;  // final step: steps 2..last fill whole groups
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wv < kTeamDataWaves) {
-    Slice<VPL> A, B, C;
+    Slice<VPL> A, B, C, D;
     team_load<VPL>(A, a, c.r0, c.voff, true);
     team_load<VPL>(B, a, c.r0 + a.n_teams, c.voff, c.nr > 1);
-    // step 0: pass 1 of the first row only
     uint32_t tl = threadIdx.x;
     asm volatile("" : "+v"(tl));
-    data_pass1<VPL>(A, c, 0, sh, wv, tl);
+    // steps 0 and 1: pass 1 only, and the loads of rows 2 and 3
+    const float2 none = make_float2(-INFINITY, -INFINITY);
+    data_pass1<VPL>(A, c, 0, sh, wv, tl, none);
     team_load<VPL>(C, a, c.r0 + 2 * a.n_teams, c.voff, c.nr > 2);
-    // rows rotate through A, B, C: step i runs pass 1 in buffer i % 3 and pass 2
-    // (then the next loads) in buffer (i + 2) % 3
-    for (int64_t i = 1; i <= last; i += 3) {
-      data_step<VPL>(B, A, a, c, i, sh, wv);
-      data_step<VPL>(C, B, a, c, i + 1, sh, wv);
+    data_pass1<VPL>(B, c, 1, sh, wv, tl, none);
+    team_load<VPL>(D, a, c.r0 + 3 * a.n_teams, c.voff, c.nr > 3);
+    for (int64_t i = 2; i <= last; i += 4) {
+      data_step<VPL>(C, A, a, c, i, sh, wv);
+      data_step<VPL>(D, B, a, c, i + 1, sh, wv);
       data_step<VPL>(A, C, a, c, i + 2, sh, wv);
+      data_step<VPL>(B, D, a, c, i + 3, sh, wv);
     }
     __syncthreads();
   } else {
+    // The sync wave's work is a short dependent chain that the data waves'
+    // steady compute would otherwise crowd out on its SIMD; it issues first.
+    __builtin_amdgcn_s_setprio(3);
     bool ok = true;
     for (int64_t i = 0; i <= last; ++i) {
       const int64_t r = c.r0 + i * a.n_teams;
       __syncthreads();
-      if (i >= 2 && i - 2 < c.nr) team_flush(a, c, r - 2 * a.n_teams, i & 1, sh);
-      if (ok && i < c.nr) ok = team_exchange(a, c, r, i & 1, sh);
+      if (i >= 3 && i - 3 < c.nr) team_flush(a, c, r - 3 * a.n_teams, (int)((i - 3) & 1), sh);
+      if (i < c.nr) team_publish(a, c, r, (int)(i & 1), sh);
+      if (ok && i >= 1 && i - 1 < c.nr) ok = team_collect(a, c, r - a.n_teams, (int)((i - 1) & 3), sh);
     }
     __syncthreads();
-    if (c.nr + 1 > last)  // row nr - 1 had no step i = nr + 1 to flush it
+    if (c.nr + 2 > last)  // row nr - 1 had no step i = nr + 2 to flush it
       team_flush(a, c, c.r0 + (c.nr - 1) * a.n_teams, (int)((c.nr - 1) & 1), sh);
   }
 }
