@@ -65,13 +65,14 @@ AttnWork attn_work(const spec_tree_layout &L, int hkv, int D, spec_dtype dt) {
 }  // namespace
 
 // Workspace of E2E-TV: four float arrays [R], the team partials [R][kTeamMax],
-// the team exchange slots [R][kTeamMax], a status word, then the indicator
-// bitmask [R][bits_row].
+// the team exchange slots [R][kTeamMax], the status and ticket words, the
+// per-branch sums [R] (float64; a branch has at least one step), then the
+// indicator bitmask [R][bits_row].
 static size_t e2etv_bits_row(int64_t V) { return align_up((size_t)(V + 7) / 8, 16); }
 
 namespace {
 struct E2etvOffsets {
-  size_t step, part, xchg, status, bits, total;
+  size_t step, part, xchg, status, bsum, bits, total;
 };
 E2etvOffsets e2etv_offsets(int64_t R, int64_t V) {
   E2etvOffsets o;
@@ -79,7 +80,8 @@ E2etvOffsets e2etv_offsets(int64_t R, int64_t V) {
   o.part = 4 * o.step;
   o.xchg = o.part + align_up((size_t)R * kTeamMax * sizeof(float2), 256);
   o.status = o.xchg + align_up((size_t)R * kTeamMax * sizeof(unsigned long long), 256);
-  o.bits = o.status + 256;
+  o.bsum = o.status + 256;
+  o.bits = o.bsum + align_up((size_t)R * sizeof(double), 256);
   o.total = o.bits + align_up((size_t)R * e2etv_bits_row(V), 256);
   return o;
 }
@@ -98,6 +100,7 @@ E2etvWork e2etv_carve(void *d_work, int64_t R, int64_t V) {
   w.part = reinterpret_cast<float2 *>(p + o.part);
   w.xchg = reinterpret_cast<unsigned long long *>(p + o.xchg);
   w.status = reinterpret_cast<unsigned *>(p + o.status);
+  w.branch_sum = reinterpret_cast<double *>(p + o.bsum);
   w.bits = reinterpret_cast<uint8_t *>(p + o.bits);
   w.bits_row = (int64_t)e2etv_bits_row(V);
   return w;

@@ -65,7 +65,8 @@ struct E2etvWork {
   float *coef;     // [R] dL/d alpha
   float2 *part;    // [R][team] (alpha, S) partials of the members of a statistics team
   unsigned long long *xchg;  // [R][team] log-sum-exp slots the members of a team exchange
-  unsigned *status;          // raised if a team exchange timed out
+  unsigned *status;          // [0] raised if a team exchange timed out; [1] the scan kernel's ticket
+  double *branch_sum;        // [R] per-branch sum of prefix products (at most R branches)
   uint8_t *bits;   // [R][bits_row] bit u of a row: 1 iff q_u < p_u (the set S is summed over)
   int64_t bits_row;
 };

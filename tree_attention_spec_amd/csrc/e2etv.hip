@@ -114,9 +114,11 @@ template <typename T, bool VEC>
 __global__ __launch_bounds__(kStatThreads) void e2etv_stats_kernel(
     const T *__restrict__ draft, const T *__restrict__ teacher, int64_t n_rows, int64_t V,
     float2 *__restrict__ part, float *__restrict__ lse_q2,
-    float *__restrict__ lse_p2, uint8_t *__restrict__ bits, int64_t bits_row) {
+    float *__restrict__ lse_p2, uint8_t *__restrict__ bits, int64_t bits_row,
+    unsigned *__restrict__ ticket) {
   __shared__ float red[2 * kStatThreads / 64];
   const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && tid == 0) *ticket = 0u;  // the scan kernel's ticket
   for (int64_t row = blockIdx.x; row < n_rows; row += gridDim.x) {
   const T *z = draft + row * V;
   const T *y = teacher + row * V;
@@ -620,59 +622,85 @@ __global__ __launch_bounds__(kTeamThreads) void e2etv_stats_team_kernel(TeamArgs
   }
 }
 
-// Slots to the empty pattern and the status word to zero, before a team launch.
+// Slots to the empty pattern, the status word and the scan ticket to zero,
+// before a team launch.
 __global__ void e2etv_team_clear(unsigned long long *xchg, int64_t n, unsigned *status) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     xchg[i] = kSlotEmpty;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0u;
+  if (blockIdx.x == 0 && threadIdx.x < 2) status[threadIdx.x] = 0u;
 }
 
-// One workgroup. alpha_s and S_s from the member partials (member order), c_s
-// for every step, and L in float64 with a fixed reduction order. A raised
-// status word (a statistics team barrier that timed out) makes alpha and L NaN.
-__global__ __launch_bounds__(1024) void e2etv_scan_kernel(
+// One wave per branch and one lane per step (a branch has at most 64 steps).
+// Each lane adds its row's member partials in member order into alpha_s and
+// S_s; the branch's alphas are then broadcast lane by lane in float64 so that
+// lane i forms A_{i-1} = prod_{j<i} alpha_j (ascending order) and
+// G_i = 1 + alpha_{i+1} G_{i+1} with G_W = 1, hence c_i = -w A_{i-1} G_i with
+// no division. The branch's sum of A_j is a fixed butterfly over the lanes.
+// The last workgroup to take a ticket (cleared by the statistics kernels) adds
+// the branch sums in branch order and writes L = 1 - w * sum. A raised status
+// word (a statistics team exchange that timed out) makes alpha and L NaN.
+constexpr int kScanWaves = 16;
+__global__ __launch_bounds__(kScanWaves * 64) void e2etv_scan_kernel(
     const int32_t *__restrict__ step_off, int32_t n_branches, const float2 *__restrict__ part,
     int32_t team, const unsigned *__restrict__ status, float w, float *__restrict__ alpha,
-    float *__restrict__ S, float *__restrict__ coef, float *__restrict__ loss) {
-  __shared__ double red[1024 / 64];
+    float *__restrict__ S, float *__restrict__ coef, double *__restrict__ branch_sum,
+    unsigned *__restrict__ ticket, float *__restrict__ loss) {
+  __shared__ double red[kScanWaves];
+  __shared__ bool is_last;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int b = blockIdx.x * kScanWaves + wv;
   const bool failed = status != nullptr && *status != 0u;
-  double part_sum = 0.0;
-  for (int b = threadIdx.x; b < n_branches; b += blockDim.x) {
-    const int s0 = step_off[b], s1 = step_off[b + 1];
-    for (int s = s0; s < s1; ++s) {
-      float al = 0.f, ss = 0.f;
+  if (b < n_branches) {
+    const int s0 = step_off[b], n = step_off[b + 1] - s0;
+    float al = 0.f, ss = 0.f;
+    if (lane < n) {
+      const float2 *pp = part + (int64_t)(s0 + lane) * team;
       for (int j = 0; j < team; ++j) {
-        const float2 p = part[(int64_t)s * team + j];
+        const float2 p = pp[j];
         al += p.x;
         ss += p.y;
       }
-      alpha[s] = failed ? NAN : al;
-      S[s] = ss;
+      alpha[s0 + lane] = failed ? NAN : al;
+      S[s0 + lane] = ss;
     }
-    // G_{W} = 1, G_i = 1 + alpha_{i+1} G_{i+1}; park G_i in coef
-    double G = 1.0;
-    for (int s = s1 - 1; s >= s0; --s) {
-      coef[s] = (float)G;
-      G = 1.0 + (double)alpha[s] * G;
+    const double ad = al;
+    double A = 1.0, G = 1.0;
+    for (int j = 0; j < n; ++j) {
+      const double aj = __shfl(ad, j);
+      if (j < lane) A *= aj;
     }
-    // A_0 = 1, A_i = A_{i-1} alpha_i; c_i = -w A_{i-1} G_i; branch sum of A_j
-    double A = 1.0, sumA = 0.0;
-    for (int s = s0; s < s1; ++s) {
-      const double Gi = coef[s];
-      coef[s] = (float)(-(double)w * A * Gi);
-      A *= (double)alpha[s];
-      sumA += A;
+    for (int j = n - 1; j > 0; --j) {
+      const double aj = __shfl(ad, j);
+      if (j > lane) G = 1.0 + aj * G;
     }
-    part_sum += sumA;
-  }
+    double sumA = 0.0;
+    if (lane < n) {
+      coef[s0 + lane] = (float)(-(double)w * A * G);
+      sumA = A * ad;
+    }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) part_sum += __shfl_xor(part_sum, off);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part_sum;
+    for (int off = 1; off < 64; off <<= 1) sumA += __shfl_xor(sumA, off);
+    if (lane == 0) {
+      branch_sum[b] = sumA;
+      __threadfence();  // the branch sum is visible to whichever workgroup finishes last
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) is_last = atomicAdd(ticket, 1u) == gridDim.x - 1;
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+  double t = 0.0;
+  for (int k = threadIdx.x; k < n_branches; k += blockDim.x) t += branch_sum[k];
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) t += __shfl_xor(t, off);
+  if (lane == 0) red[wv] = t;
   __syncthreads();
   if (threadIdx.x == 0) {
-    double t = 0.0;
-    for (int k = 0; k < (int)(blockDim.x >> 6); ++k) t += red[k];
-    loss[0] = failed ? NAN : (float)(1.0 - (double)w * t);
+    double tot = 0.0;
+    for (int k = 0; k < kScanWaves; ++k) tot += red[k];
+    loss[0] = failed ? NAN : (float)(1.0 - (double)w * tot);
+    *ticket = 0u;
   }
 }
 
@@ -833,14 +861,15 @@ hipError_t launch_typed(const spec_tree_layout &L, int64_t V, const void *draft,
     if (e != hipSuccess) return e;
     const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(R, cus));
     hipLaunchKernelGGL((e2etv_stats_kernel<T, VEC>), dim3((unsigned)grid), dim3(kStatThreads), 0, s,
-                       z, y, R, V, ws.part, ws.lse_q2, ws.lse_p2, ws.bits, ws.bits_row);
+                       z, y, R, V, ws.part, ws.lse_q2, ws.lse_p2, ws.bits, ws.bits_row, ws.status + 1);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     team = 1;
   }
   prof_mark(s, "e2etv_stats");
-  hipLaunchKernelGGL(e2etv_scan_kernel, dim3(1), dim3(1024), 0, s, L.step_off, L.n_branches,
-                     ws.part, team, status, w, alpha, ws.S, ws.coef, loss);
+  hipLaunchKernelGGL(e2etv_scan_kernel, dim3((unsigned)((L.n_branches + kScanWaves - 1) / kScanWaves)),
+                     dim3(kScanWaves * 64), 0, s, L.step_off, L.n_branches, ws.part, team, status, w,
+                     alpha, ws.S, ws.coef, ws.branch_sum, ws.status + 1, loss);
   e = hipGetLastError();
   if (e != hipSuccess || !grad) return e;
   prof_mark(s, "e2etv_scan");
