@@ -12,7 +12,9 @@
 // LDS serve NW heads. The key loop runs over the block's trunk range, then its
 // branch range, in tiles of 64 keys:
 //   S^T[key][query] = K Q^T     v_mfma_f32_32x32x16_bf16, 2 output tiles x D/16 steps
-//   online softmax  per query column, in-lane over 32 keys + one cross-half max
+//   online softmax  per query column, in-lane over 32 keys + one cross-half max;
+//                   the reference maximum moves only when a score exceeds it by
+//                   more than 2^8, so the output is rarely rescaled
 //   O^T[d][query]  += V^T P^T   D/32 output tiles x 4 steps
 // Keys on the rows, queries on the columns keeps each query's scores, max and
 // sum inside one lane (plus its partner lane l^32), and lets the probabilities
@@ -32,6 +34,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int KT = 64;  // keys per tile
+constexpr float kLazyMax = 8.f;  // log2 headroom of the softmax reference
 
 template <int D>
 struct AttnSmem {
@@ -231,38 +234,61 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
           s1[i] = (uint32_t)(o0 + 32) <= span ? s1[i] : -INFINITY;
         }
       }
-      float mx = -INFINITY;
+      float ma = s0[0], mb = s1[0];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-      mx = pair_max(mx);
-      const float m_new = fmaxf(m, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float corr = __builtin_amdgcn_exp2f(m - m_use);
-      float ls = 0.f;
-      bf16x8 pf[4];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p0 = __builtin_amdgcn_exp2f(s0[i] - m_use);
-        const float p1 = __builtin_amdgcn_exp2f(s1[i] - m_use);
-        ls += p0 + p1;
-        pf[i >> 3][i & 7] = (__bf16)p0;
-        pf[2 + (i >> 3)][i & 7] = (__bf16)p1;
+      for (int i = 1; i < 16; ++i) {
+        ma = fmaxf(ma, s0[i]);
+        mb = fmaxf(mb, s1[i]);
       }
-      l = l * corr + ls;
-      m = m_new;
-      if (__any(corr != 1.f)) {
+      const float mx = pair_max(fmaxf(ma, mb));
+      // The reference m moves only when a score exceeds it by more than
+      // kLazyMax, so O and l are rescaled on few tiles; in between the
+      // probabilities are at most 2^kLazyMax.
+      if (__any(mx > m + kLazyMax)) {
+        const float m_new = mx > m + kLazyMax ? mx : m;
+        const float corr = m_new == m ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+        l *= corr;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
           for (int i = 0; i < 16; ++i) o[dt][i] *= corr;
+        m = m_new;
+      }
+      const float m_use = m == -INFINITY ? 0.f : m;
+      float ls0 = 0.f, ls1 = 0.f;
+      bf16x8 pf[4];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(s0[i] - m_use);
+        ls0 += p0;
+        pf[i >> 3][i & 7] = (__bf16)p0;
       }
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+      for (int i = 0; i < 16; ++i) {
+        const float p1 = __builtin_amdgcn_exp2f(s1[i] - m_use);
+        ls1 += p1;
+        pf[2 + (i >> 3)][i & 7] = (__bf16)p1;
+      }
+      l += ls0 + ls1;
+      // O^T += V^T P^T, key group by key group: the first half of the MFMAs needs
+      // only the first 32 keys' probabilities, so the exponentials of the other
+      // 32 run beside them
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
           const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&cur.vt[32 * dt + n][16 * kk + 8 * half]);
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], o[dt], 0, 0, 0);
         }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two V^T fragments
+      __builtin_amdgcn_sched_group_barrier(0x402, 56, 0);  // probabilities of keys 0..31
+#pragma unroll
+      for (int i = 0; i < 4 * DT - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA,
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next fragment,
+        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);  // keys 32..63 meanwhile
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
   }
 
