@@ -394,12 +394,10 @@ __device__ inline float rows_lse2_of(uint4 (&v)[VPL], bool draft, float c) {
   return c + log2f(s);  // -inf for a row with no active element
 }
 
-// alpha and S sums of this thread's vectors, and their indicator bytes. The
-// bytes go through a buffer resource whose range is this member's slice of the
-// bitmask row, so stores of lanes past the slice are dropped by the hardware.
+// alpha and S sums of this thread's vectors; m[k] gets the indicator byte of
+// vector k (bit j: element j has z' < y').
 template <int VPL>
-__device__ inline float2 team_alpha(const Slice<VPL> &b, float lz2, float ly2,
-                                    __amdgpu_buffer_rsrc_t brow, uint32_t tl) {
+__device__ inline float2 alpha_core(const Slice<VPL> &b, float lz2, float ly2, uint32_t (&mk)[VPL]) {
   float al = 0.f, ss = 0.f, nz = -lz2, ny = -ly2;
 #pragma unroll
   for (int k = 0; k < VPL; ++k) {
@@ -421,12 +419,25 @@ __device__ inline float2 team_alpha(const Slice<VPL> &b, float lz2, float ly2,
       al += e;
       ss += t;
     }
-    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)m, brow, tl, k * kTeamData, 0);
+    mk[k] = m;
     // one vector at a time: the next vector's work depends on this vector's sums,
     // so the scheduler cannot hoist every compare ahead of the exponentials
     asm volatile("" : "+v"(al), "+v"(ss), "+v"(nz), "+v"(ny));
   }
   return make_float2(al, ss);
+}
+
+// alpha_core, with the indicator bytes stored through a buffer resource whose
+// range is this member's slice of the bitmask row (stores of lanes past the
+// slice are dropped by the hardware).
+template <int VPL>
+__device__ inline float2 team_alpha(const Slice<VPL> &b, float lz2, float ly2,
+                                    __amdgpu_buffer_rsrc_t brow, uint32_t tl) {
+  uint32_t mk[VPL];
+  const float2 r = alpha_core<VPL>(b, lz2, ly2, mk);
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)mk[k], brow, tl, k * kTeamData, 0);
+  return r;
 }
 
 __device__ inline unsigned long long pack_slot(float lz, float ly) {
@@ -622,11 +633,323 @@ __global__ __launch_bounds__(kTeamThreads) void e2etv_stats_team_kernel(TeamArgs
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fused statistics and gradient (bf16 rows, length a multiple of 8, and every
+// branch short enough that its rows fall in two consecutive steps of the team
+// pipeline: W_b - 1 <= n_teams). Without a gradient buffer the same kernel
+// runs with its gradient stores dropped, so alpha and L do not depend on
+// whether the gradient is asked for.
+//
+// The team pipeline above, extended by a third exchange and a write stage, so
+// that every logit is read once and every gradient element written once
+// (8 bytes per element): a member keeps the draft words and the indicator bits
+// of its slice of a row after pass 2, and three steps later, once the partials
+// of every row of the row's branch are published, writes the gradient
+//   g = c_s q (1[z' < y'] - S_s) = (bit ? c_s (1 - S_s) : -c_s S_s) 2^z'
+// straight from registers. Rows are numbered r = team + i n_teams, so the rows
+// of a branch sit in one step or two adjacent ones.
+//   data step i:  pass 1 of row i | barrier | pass 2 of row i - 2 (bits and
+//                 draft words kept; the last wave through it stores the
+//                 member's (alpha, S) partial of the row into its slot) |
+//                 gradient of row i - 5 | loads of row i + 2
+//   sync step i:  barrier | publish row i | collect row i - 1 and the
+//                 coefficient of row i - 4 (one poll)
+// The coefficient of row g polls the partial slots of every row of g's
+// branch (rows of g's step and the next, flushed during data step g + 3, a
+// step before the poll), adds each row's
+// partials in member order, forms A and G in float64 as the scan kernel does
+// and leaves (lse2 z, c (1 - S), -c S) of row g in LDS for the next data step.
+// Member 0 of a row stores its alpha; member 0 of a branch's first row stores
+// the branch's sum of prefix products, which a one-workgroup kernel adds in
+// branch order after this one. Partial slots are 64-bit words written once by
+// agent-scope atomic stores and cleared to all-ones before the launch.
+
+constexpr int kFuseMaxVpl = 2;  // four row buffers and four held draft slices per lane
+
+struct FuseArgs {
+  TeamArgs t;
+  float *grad;                   // [R][V] float32, or null (no gradient)
+  float *alpha;                  // [R]
+  const int32_t *step_off;       // [B + 1]
+  const int32_t *step_branch;    // [R]
+  double *branch_sum;            // [B]
+  float w;                       // loss normaliser
+};
+
+struct FuseShared {
+  TeamShared t;
+  unsigned cnt[2];                               // data waves through pass 2, by step parity
+  float4 gc[4];                                  // row (lse2 z, c (1 - S), -c S, -), by row mod 4
+  unsigned long long pp[64 * kTeamMax];          // a branch's partial slots, row-major [W][T]
+};
+
+__device__ inline unsigned long long pack_pair(float a, float b) { return pack_slot(a, b); }
+
+// The member's (alpha, S) of a row, into the row's slot for this member.
+__device__ inline void fuse_flush(const FuseArgs &a, const TeamCtx &c, int64_t r, int par,
+                                  const FuseShared &sh) {
+  const int lane = threadIdx.x & 63;
+  float2 q = make_float2(0.f, 0.f);
+  if (lane < kTeamRows) q = sh.t.as[par][lane];
+  q.x = dpp_sum(q.x);
+  q.y = dpp_sum(q.y);
+  unsigned long long *slot = reinterpret_cast<unsigned long long *>(a.t.part) + r * a.t.T + c.mem;
+  if (lane == 0) __hip_atomic_store(slot, pack_pair(q.x, q.y), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Sync work of step i after the flush and the publish: collect row i - 1 (if
+// `col`) and the coefficient of row g = i - 4 (if `coef`). The slots of both
+// are polled together, so a step costs one round trip to the coherence point.
+// The coefficient polls the partial slots of every row of g's branch, adds
+// each row's partials in member order, forms A and G in float64 as the scan
+// kernel does and leaves (lse2 z, c (1 - S), -c S) of row g in LDS for the next
+// data step. False on a poll timeout.
+__device__ inline bool fuse_sync(const FuseArgs &a, const TeamCtx &c, int64_t i, bool col, bool coef,
+                                 FuseShared &sh) {
+  const int lane = threadIdx.x & 63, T = a.t.T;
+  const int64_t n = a.t.n_teams;
+  const int64_t rc = c.r0 + (i - 1) * n, g = c.r0 + (i - 4) * n;
+  int b = 0, s0 = 0, W = 0, WT = 0;
+  if (coef) {
+    b = a.step_branch[g];
+    s0 = a.step_off[b];
+    W = a.step_off[b + 1] - s0;
+    WT = W * T;
+  }
+  const unsigned long long *xs = a.t.xchg + rc * T;
+  const unsigned long long *ps = reinterpret_cast<const unsigned long long *>(a.t.part) + (int64_t)s0 * T;
+  constexpr int kPer = kTeamMax;  // slots per lane: W T <= 64 kTeamMax
+  unsigned long long vx = kSlotEmpty, v[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) v[k] = kSlotEmpty;
+  const bool wx = col && lane < T;
+  unsigned spins = 0;
+  for (;;) {
+    if (wx && vx == kSlotEmpty) vx = __hip_atomic_load(xs + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int e = lane + 64 * k;
+      if (64 * k < WT && e < WT && v[k] == kSlotEmpty)
+        v[k] = __hip_atomic_load(ps + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    bool missing = wx && vx == kSlotEmpty;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) missing |= (lane + 64 * k < WT) && v[k] == kSlotEmpty;
+    if (!__any(missing)) break;
+    unsigned bad = 0;
+    if (lane == 63) bad = __hip_atomic_load(a.t.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__shfl(bad, 63) != 0u || ++spins > kTeamSpinLimit) {
+      if (lane == 0) __hip_atomic_store(a.t.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (col) {  // row i - 1: merge the members' log-sum-exps in member order
+    const float gz = wx ? __uint_as_float((uint32_t)vx) : -INFINITY;
+    const float gy = wx ? __uint_as_float((uint32_t)(vx >> 32)) : -INFINITY;
+    const float lz2 = wave_lse2(gz), ly2 = wave_lse2(gy);
+    if (lane == 0) sh.t.l[(i - 1) & 3] = make_float2(lz2, ly2);
+  }
+  if (!coef) return true;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k)
+    if (lane + 64 * k < WT) sh.pp[lane + 64 * k] = v[k];
+  float al = 0.f, ss = 0.f;
+  if (lane < W) {
+    for (int j = 0; j < T; ++j) {
+      const unsigned long long x = sh.pp[lane * T + j];
+      al += __uint_as_float((uint32_t)x);
+      ss += __uint_as_float((uint32_t)(x >> 32));
+    }
+  }
+  // lane i: A_{i-1} = prod_{j<i} alpha_j (ascending), G_i = 1 + alpha_{i+1} G_{i+1};
+  // alpha_j reaches every lane through a scalar read of lane j
+  const double ad = al;
+  double A = 1.0, G = 1.0;
+  for (int j = 0; j < W; ++j) {
+    const double aj = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), j));
+    if (j < lane) A *= aj;
+  }
+  for (int j = W - 1; j > 0; --j) {
+    const double aj = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), j));
+    if (j > lane) G = 1.0 + aj * G;
+  }
+  const float cf = (float)(-(double)a.w * A * G);
+  const int gl = (int)(g - s0);
+  const float cg = __shfl(cf, gl), sg = __shfl(ss, gl);
+  if (lane == 0) {
+    const float lz2 = sh.t.l[(i - 4) & 3].x;
+    sh.gc[(i - 4) & 3] = make_float4(lz2, cg * (1.f - sg), -cg * sg, 0.f);
+  }
+  if (c.mem == 0) {
+    if (lane == gl) a.alpha[g] = al;
+    if (gl == 0) {  // the branch's first row: its sum of prefix products
+      double sumA = lane < W ? A * ad : 0.0;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) sumA += __shfl_xor(sumA, off);
+      if (lane == 0) a.branch_sum[b] = sumA;
+    }
+  }
+  return true;
+}
+
+// Gradient of one row slice from the held draft words and indicator bits.
+template <int VPL>
+__device__ inline void fuse_grad(const uint4 (&zh)[VPL], uint32_t bits, float4 gc,
+                                 __amdgpu_buffer_rsrc_t grow, uint32_t tl) {
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    float g[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t wz = word(zh[k], j >> 1);
+      const float q = __builtin_amdgcn_exp2f(fmaf((j & 1) ? hi_f(wz) : lo_f(wz), kLog2e, -gc.x));
+      g[j] = ((bits >> (8 * k + j)) & 1u ? gc.y : gc.z) * q;
+    }
+    const uint32_t off = (tl + (uint32_t)(k * kTeamData)) * 32u;
+    __builtin_amdgcn_raw_buffer_store_b128(
+        u32x4{__float_as_uint(g[0]), __float_as_uint(g[1]), __float_as_uint(g[2]), __float_as_uint(g[3])},
+        grow, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(
+        u32x4{__float_as_uint(g[4]), __float_as_uint(g[5]), __float_as_uint(g[6]), __float_as_uint(g[7])},
+        grow, off + 16u, 0, 0);
+  }
+}
+
+// Data step i >= 2 of the fused pipeline (see above). `cur` holds row i,
+// `old` row i - 2 (then the loads of row i + 2); (zw, bw) receive row i - 2's
+// draft words and bits, (zr, br) hold row i - 5's.
+template <int VPL>
+__device__ inline void fuse_step(Slice<VPL> &cur, Slice<VPL> &old, uint4 (&zw)[VPL], uint32_t &bw,
+                                 const uint4 (&zr)[VPL], uint32_t br, const FuseArgs &a,
+                                 const TeamCtx &c, int64_t i, FuseShared &sh, int wv) {
+  uint32_t tl = threadIdx.x;
+  asm volatile("" : "+v"(tl));
+  data_pass1<VPL>(cur, c, i, sh.t, wv, tl, i >= 3 ? sh.t.l[(i - 3) & 3] : make_float2(-INFINITY, -INFINITY));
+  const int64_t n = a.t.n_teams;
+  const int64_t r = c.r0 + i * n;
+  const float2 l = sh.t.l[(i - 2) & 3];
+  uint32_t mk[VPL];
+  float2 as = alpha_core<VPL>(old, l.x, l.y, mk);
+  uint32_t bits = 0;
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    bits |= mk[k] << (8 * k);
+    zw[k] = old.z[k];
+  }
+  bw = bits;
+  as.x = row16_sum(as.x);
+  as.y = row16_sum(as.y);
+  if ((threadIdx.x & 15) == 0) sh.t.as[i & 1][wv * 4 + ((threadIdx.x & 63) >> 4)] = as;
+  // the last data wave through pass 2 flushes the member's (alpha, S) of row
+  // i - 2 and rearms the counter for step i + 2
+  unsigned prev = 0;
+  if ((threadIdx.x & 63) == 0)
+    prev = __hip_atomic_fetch_add(&sh.cnt[i & 1], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if (__builtin_amdgcn_readfirstlane(prev) == (unsigned)kTeamDataWaves - 1) {
+    if (i - 2 < c.nr) fuse_flush(a, c, r - 2 * n, (int)(i & 1), sh);
+    if ((threadIdx.x & 63) == 0) sh.cnt[i & 1] = 0u;
+  }
+  const bool hasg = i >= 5 && i - 5 < c.nr && a.grad != nullptr;
+  const int64_t V = a.t.V8 * 8;
+  const __amdgpu_buffer_rsrc_t grow =
+      row_rsrc(hasg ? a.grad + (r - 5 * n) * V + c.vb * 8 : a.grad, hasg ? c.n * 32u : 0u);
+  fuse_grad<VPL>(zr, br, sh.gc[(i - 5) & 3], grow, tl);
+  team_load<VPL>(old, a.t, r + 2 * n, c.voff, i + 2 < c.nr);
+}
+
+template <int VPL>
+__global__ __launch_bounds__(kTeamThreads) void e2etv_fused_team_kernel(FuseArgs a) {
+  __shared__ FuseShared sh;
+  TeamCtx c;
+  c.team = blockIdx.x / a.t.T;
+  c.mem = blockIdx.x % a.t.T;
+  if (c.team >= a.t.n_teams) return;
+  c.vb = a.t.V8 * c.mem / a.t.T;
+  c.n = (uint32_t)(a.t.V8 * (c.mem + 1) / a.t.T - c.vb);
+  c.voff = (uint32_t)((c.vb + threadIdx.x) * 16);
+  c.r0 = c.team;
+  c.nr = (a.t.R - c.team + a.t.n_teams - 1) / a.t.n_teams;
+  if (c.nr <= 0) return;
+  const int64_t last = 4 * ((c.nr + 6) / 4) + 1;  // steps 2..last fill whole groups; last >= nr + 4
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (threadIdx.x < 2) sh.cnt[threadIdx.x] = 0u;  // first used after the barrier of step 2
+  if (wv < kTeamDataWaves) {
+    Slice<VPL> A, B, C, D;
+    uint4 Z0[VPL], Z1[VPL], Z2[VPL], Z3[VPL];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) Z0[k] = Z1[k] = Z2[k] = Z3[k] = make_uint4(0, 0, 0, 0);
+    uint32_t b0 = 0, b1 = 0, b2 = 0, b3 = 0;
+    team_load<VPL>(A, a.t, c.r0, c.voff, true);
+    team_load<VPL>(B, a.t, c.r0 + a.t.n_teams, c.voff, c.nr > 1);
+    uint32_t tl = threadIdx.x;
+    asm volatile("" : "+v"(tl));
+    const float2 none = make_float2(-INFINITY, -INFINITY);
+    data_pass1<VPL>(A, c, 0, sh.t, wv, tl, none);
+    team_load<VPL>(C, a.t, c.r0 + 2 * a.t.n_teams, c.voff, c.nr > 2);
+    data_pass1<VPL>(B, c, 1, sh.t, wv, tl, none);
+    team_load<VPL>(D, a.t, c.r0 + 3 * a.t.n_teams, c.voff, c.nr > 3);
+    // row i in buffer i % 4; row i - 2's draft slice held in Z[(i - 2) % 4]
+    for (int64_t i = 2; i <= last; i += 4) {
+      fuse_step<VPL>(C, A, Z0, b0, Z1, b1, a, c, i, sh, wv);
+      fuse_step<VPL>(D, B, Z1, b1, Z2, b2, a, c, i + 1, sh, wv);
+      fuse_step<VPL>(A, C, Z2, b2, Z3, b3, a, c, i + 2, sh, wv);
+      fuse_step<VPL>(B, D, Z3, b3, Z0, b0, a, c, i + 3, sh, wv);
+    }
+    __syncthreads();
+  } else {
+    __builtin_amdgcn_s_setprio(3);
+    bool ok = true;
+    for (int64_t i = 0; i <= last; ++i) {
+      const int64_t r = c.r0 + i * a.t.n_teams;
+      __syncthreads();
+      if (i < c.nr) team_publish(a.t, c, r, (int)(i & 1), sh.t);
+      const bool col = i >= 1 && i - 1 < c.nr, coef = i >= 4 && i - 4 < c.nr;  // wave-uniform
+      if (ok && (col || coef)) ok = fuse_sync(a, c, i, col, coef, sh);
+    }
+    __syncthreads();
+  }
+}
+
+// L = 1 - w * sum of the branch sums in branch order (one workgroup, after the
+// fused kernel); a raised status word makes L NaN.
+__global__ __launch_bounds__(1024) void e2etv_loss_kernel(const double *__restrict__ branch_sum,
+                                                          int32_t n_branches, const unsigned *__restrict__ status,
+                                                          float w, float *__restrict__ alpha, int64_t R,
+                                                          float *__restrict__ loss) {
+  __shared__ double red[16];
+  const bool failed = *status != 0u;
+  if (failed)
+    for (int64_t s = threadIdx.x; s < R; s += blockDim.x) alpha[s] = NAN;
+  double t = 0.0;
+  for (int k = threadIdx.x; k < n_branches; k += blockDim.x) t += branch_sum[k];
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) t += __shfl_xor(t, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = t;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double tot = 0.0;
+    for (int k = 0; k < (int)(blockDim.x >> 6); ++k) tot += red[k];
+    loss[0] = failed ? NAN : (float)(1.0 - (double)w * tot);
+  }
+}
+
 // Slots to the empty pattern, the status word and the scan ticket to zero,
 // before a team launch.
 __global__ void e2etv_team_clear(unsigned long long *xchg, int64_t n, unsigned *status) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     xchg[i] = kSlotEmpty;
+  if (blockIdx.x == 0 && threadIdx.x < 2) status[threadIdx.x] = 0u;
+}
+
+// Exchange slots and partial slots to the empty pattern, the status word to
+// zero, before a fused launch.
+__global__ void e2etv_fuse_clear(unsigned long long *xchg, unsigned long long *part, int64_t n,
+                                 unsigned *status) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    xchg[i] = kSlotEmpty;
+    part[i] = kSlotEmpty;
+  }
   if (blockIdx.x == 0 && threadIdx.x < 2) status[threadIdx.x] = 0u;
 }
 
@@ -763,12 +1086,22 @@ struct TeamDevice {
   bool init = false;
   int cus = 0, coop = 0;
   int occ[kTeamMaxVpl + 1] = {};
+  int fuse_occ[kFuseMaxVpl + 1] = {};
 };
 
 template <int VPL>
 int team_occupancy() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void *)e2etv_stats_team_kernel<VPL>,
+                                                   kTeamThreads, 0) != hipSuccess)
+    n = 0;
+  return n;
+}
+
+template <int VPL>
+int fuse_occupancy() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void *)e2etv_fused_team_kernel<VPL>,
                                                    kTeamThreads, 0) != hipSuccess)
     n = 0;
   return n;
@@ -787,6 +1120,8 @@ TeamDevice team_device(int dev) {
     d.occ[1] = team_occupancy<1>();
     d.occ[2] = team_occupancy<2>();
     d.occ[3] = team_occupancy<3>();
+    d.fuse_occ[1] = fuse_occupancy<1>();
+    d.fuse_occ[2] = fuse_occupancy<2>();
     d.init = true;
   }
   return d;
@@ -838,6 +1173,65 @@ hipError_t launch_team_stats(int64_t R, int64_t V, const void *draft, const void
   return hipSuccess;
 }
 
+// Fused statistics and gradient if the rows fit a team and every branch spans
+// at most two pipeline steps; *done = false (nothing launched) otherwise.
+hipError_t launch_fused(const spec_tree_layout &L, int64_t V, const void *draft, const void *teacher,
+                        float w, float *alpha, float *loss, float *grad, const E2etvWork &ws,
+                        hipStream_t s, bool *done) {
+  *done = false;
+  const int64_t R = L.n_steps;
+  const int64_t V8 = V / 8;
+  const int64_t per_member = (int64_t)kTeamData * kFuseMaxVpl;
+  const int64_t T = (V8 + per_member - 1) / per_member;
+  if (T < 1 || T > kTeamMax || V8 * 32 > INT32_MAX || L.max_branch_len > 64) return hipSuccess;
+  const int vpl = (int)(((V8 + T - 1) / T + kTeamData - 1) / kTeamData);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const TeamDevice d = team_device(dev);
+  if (!d.coop || d.cus < 1 || vpl < 1 || vpl > kFuseMaxVpl || d.fuse_occ[vpl] < 1) return hipSuccess;
+  const int64_t n_teams = std::min<int64_t>((int64_t)d.fuse_occ[vpl] * d.cus / T, R);
+  if (n_teams < 1 || (int64_t)L.max_branch_len - 1 > n_teams) return hipSuccess;
+  const int64_t n_slots = R * T;
+  hipLaunchKernelGGL(e2etv_fuse_clear, dim3((unsigned)std::min<int64_t>(1024, (n_slots + 255) / 256)), dim3(256),
+                     0, s, ws.xchg, reinterpret_cast<unsigned long long *>(ws.part), n_slots, ws.status);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  FuseArgs a;
+  a.t.z = static_cast<const __bf16 *>(draft);
+  a.t.y = static_cast<const __bf16 *>(teacher);
+  a.t.R = R;
+  a.t.V8 = V8;
+  a.t.T = (int32_t)T;
+  a.t.n_teams = (int32_t)n_teams;
+  a.t.lse_q2 = ws.lse_q2;
+  a.t.lse_p2 = ws.lse_p2;
+  a.t.part = ws.part;
+  a.t.bits = ws.bits;
+  a.t.bits_row = ws.bits_row;
+  a.t.xchg = ws.xchg;
+  a.t.status = ws.status;
+  a.grad = grad;
+  a.alpha = alpha;
+  a.step_off = L.step_off;
+  a.step_branch = L.step_branch;
+  a.branch_sum = ws.branch_sum;
+  a.w = w;
+  void *args[] = {&a};
+  static_assert(kFuseMaxVpl == 2, "one instantiation per vectors-per-lane count");
+  const void *fn = vpl == 1 ? (const void *)e2etv_fused_team_kernel<1> : (const void *)e2etv_fused_team_kernel<2>;
+  e = hipLaunchCooperativeKernel(fn, dim3((unsigned)(n_teams * T)), dim3(kTeamThreads), args, 0, s);
+  if (e != hipSuccess) return e;
+  prof_mark(s, "e2etv_fused");
+  hipLaunchKernelGGL(e2etv_loss_kernel, dim3(1), dim3(1024), 0, s, ws.branch_sum, L.n_branches, ws.status,
+                     w, alpha, R, loss);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  prof_mark(s, "e2etv_loss");
+  *done = true;
+  return hipSuccess;
+}
+
 template <typename T, bool VEC>
 hipError_t launch_typed(const spec_tree_layout &L, int64_t V, const void *draft,
                         const void *teacher, float w, float *alpha, float *loss, float *grad,
@@ -848,6 +1242,11 @@ hipError_t launch_typed(const spec_tree_layout &L, int64_t V, const void *draft,
   int team = 0;
   hipError_t e = hipSuccess;
   const unsigned *status = nullptr;
+  if (std::is_same<T, __bf16>::value && VEC) {
+    bool fused = false;
+    e = launch_fused(L, V, draft, teacher, w, alpha, loss, grad, ws, s, &fused);
+    if (e != hipSuccess || fused) return e;
+  }
   if (std::is_same<T, __bf16>::value && VEC) {
     e = launch_team_stats(R, V, draft, teacher, ws, s, &team);
     if (e != hipSuccess) return e;
