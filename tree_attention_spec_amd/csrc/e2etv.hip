@@ -665,6 +665,7 @@ __global__ __launch_bounds__(kTeamThreads) void e2etv_stats_team_kernel(TeamArgs
 // agent-scope atomic stores and cleared to all-ones before the launch.
 
 constexpr int kFuseMaxVpl = 2;  // four row buffers and four held draft slices per lane
+constexpr int kFuseRowCap = 2048;  // rows per team whose branch extents sit in LDS
 
 struct FuseArgs {
   TeamArgs t;
@@ -681,6 +682,7 @@ struct FuseShared {
   unsigned cnt[2];                               // data waves through pass 2, by step parity
   float4 gc[4];                                  // row (lse2 z, c (1 - S), -c S, -), by row mod 4
   unsigned long long pp[64 * kTeamMax];          // a branch's partial slots, row-major [W][T]
+  int4 rows[kFuseRowCap];                        // the team's k-th row: (branch, first step, width, -)
 };
 
 __device__ inline unsigned long long pack_pair(float a, float b) { return pack_slot(a, b); }
@@ -711,9 +713,10 @@ __device__ inline bool fuse_sync(const FuseArgs &a, const TeamCtx &c, int64_t i,
   const int64_t rc = c.r0 + (i - 1) * n, g = c.r0 + (i - 4) * n;
   int b = 0, s0 = 0, W = 0, WT = 0;
   if (coef) {
-    b = a.step_branch[g];
-    s0 = a.step_off[b];
-    W = a.step_off[b + 1] - s0;
+    const int4 e = sh.rows[i - 4];
+    b = e.x;
+    s0 = e.y;
+    W = e.z;
     WT = W * T;
   }
   const unsigned long long *xs = a.t.xchg + rc * T;
@@ -899,6 +902,13 @@ __global__ __launch_bounds__(kTeamThreads) void e2etv_fused_team_kernel(FuseArgs
     __syncthreads();
   } else {
     __builtin_amdgcn_s_setprio(3);
+    // the branch extent of every row of the team, once, so that no poll waits
+    // behind a dependent pair of global loads
+    for (int64_t k = threadIdx.x & 63; k < c.nr; k += 64) {
+      const int b = a.step_branch[c.r0 + k * a.t.n_teams];
+      const int s0 = a.step_off[b];
+      sh.rows[k] = make_int4(b, s0, a.step_off[b + 1] - s0, 0);
+    }
     bool ok = true;
     for (int64_t i = 0; i <= last; ++i) {
       const int64_t r = c.r0 + i * a.t.n_teams;
@@ -1191,7 +1201,8 @@ hipError_t launch_fused(const spec_tree_layout &L, int64_t V, const void *draft,
   const TeamDevice d = team_device(dev);
   if (!d.coop || d.cus < 1 || vpl < 1 || vpl > kFuseMaxVpl || d.fuse_occ[vpl] < 1) return hipSuccess;
   const int64_t n_teams = std::min<int64_t>((int64_t)d.fuse_occ[vpl] * d.cus / T, R);
-  if (n_teams < 1 || (int64_t)L.max_branch_len - 1 > n_teams) return hipSuccess;
+  if (n_teams < 1 || (int64_t)L.max_branch_len - 1 > n_teams || (R + n_teams - 1) / n_teams > kFuseRowCap)
+    return hipSuccess;
   const int64_t n_slots = R * T;
   hipLaunchKernelGGL(e2etv_fuse_clear, dim3((unsigned)std::min<int64_t>(1024, (n_slots + 255) / 256)), dim3(256),
                      0, s, ws.xchg, reinterpret_cast<unsigned long long *>(ws.part), n_slots, ws.status);
