@@ -66,6 +66,48 @@ def measured_traffic(kernel: str, src_hash: str):
     return rec.get("bytes_per_launch")
 
 
+# Library timing marks -> the kernels each covers (matched by substring of the
+# kernel name rocprofv3 records) and the source file whose hash keys its
+# measured traffic.
+MARK_KERNELS = {
+    "tree_attn": (["tree_attn_bf16_kernel", "tree_attn_f32_kernel"], "attn.hip"),
+    "rope_k": (["rope_k_kernel"], "rope.hip"),
+    "readout": (["readout_kernel"], "attn.hip"),
+    "e2etv_clear": (["e2etv_fuse_clear"], "e2etv.hip"),
+    "e2etv_fused": (["e2etv_fused_team_kernel"], "e2etv.hip"),
+    "e2etv_loss": (["e2etv_loss_kernel"], "e2etv.hip"),
+    "e2etv_stats": (["e2etv_team_clear", "e2etv_stats_team_kernel", "e2etv_stats_kernel"], "e2etv.hip"),
+    "e2etv_scan": (["e2etv_scan_kernel"], "e2etv.hip"),
+    "e2etv_grad": (["e2etv_grad_kernel"], "e2etv.hip"),
+}
+
+
+def write_traffic(fetch_db, write_db, copy_fetch_db, copy_write_db, workload):
+    """profiles/traffic.json from FETCH_SIZE / WRITE_SIZE runs, scaled by a 1 GiB copy."""
+    pm = summarize_pmc([fetch_db, write_db])
+    cp = summarize_pmc([copy_fetch_db, copy_write_db])
+    copy = next(v for k, v in cp.items() if "copyBuffer" in k)
+    n = 1 << 30
+    fs = n / (copy["FETCH_SIZE"]["mean"] * 1024.0)
+    ws = n / (copy["WRITE_SIZE"]["mean"] * 1024.0)
+    out = {"_calibration": {"copy_bytes": n, "fetch_kib": copy["FETCH_SIZE"]["mean"],
+                            "write_kib": copy["WRITE_SIZE"]["mean"], "fetch_scale": fs, "write_scale": ws,
+                            "note": "1 GiB device copy (bench.py --copy-calibration)"}}
+    for mark, (subs, src) in MARK_KERNELS.items():
+        ks = [v for k, v in pm.items() if any(sub in k for sub in subs)]
+        if not ks:
+            continue
+        fk = sum(v.get("FETCH_SIZE", {}).get("mean", 0.0) for v in ks)
+        wk = sum(v.get("WRITE_SIZE", {}).get("mean", 0.0) for v in ks)
+        out[mark] = {"source_hash": source_hash(src), "workload": workload,
+                     "fetch_bytes": fk * 1024 * fs, "write_bytes": wk * 1024 * ws,
+                     "bytes_per_launch": fk * 1024 * fs + wk * 1024 * ws,
+                     "fetch_kib_raw": fk, "write_kib_raw": wk}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
 def summarize_pmc(paths):
     """Per-kernel mean of every counter in rocprofv3 --pmc databases (no GPU needed)."""
     import collections
@@ -134,9 +176,14 @@ def main():
                     help="only run a plain 1 GiB device copy (to scale HBM counters) and exit")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DB",
                     help="print per-kernel counter means from rocprofv3 --pmc databases and exit")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB"),
+                    help="write profiles/traffic.json from four rocprofv3 --pmc databases and exit")
     args = ap.parse_args()
     if args.summarize_pmc:
         print(json.dumps(summarize_pmc(args.summarize_pmc), indent=1))
+        return
+    if args.write_traffic:
+        print(json.dumps(write_traffic(*args.write_traffic, workload=args.config), indent=1))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the branch-parallel scoring path is built and timed "

@@ -1208,6 +1208,7 @@ hipError_t launch_fused(const spec_tree_layout &L, int64_t V, const void *draft,
                      0, s, ws.xchg, reinterpret_cast<unsigned long long *>(ws.part), n_slots, ws.status);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  prof_mark(s, "e2etv_clear");
   FuseArgs a;
   a.t.z = static_cast<const __bf16 *>(draft);
   a.t.y = static_cast<const __bf16 *>(teacher);
