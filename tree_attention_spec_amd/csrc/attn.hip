@@ -200,7 +200,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   for (int t = 0; t < DT; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
+  // m: the softmax reference of this lane's query (log2 units); the score
+  // MFMAs start from -m_use, so they produce s - m_use directly
   float m = -INFINITY, l = 0.f;
+  f32x16 negm;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negm[i] = 0.f;
 
   for (int t = 0; t < n_tiles; ++t) {
     AttnSmem<D> &cur = sm[t & 1];
@@ -210,9 +215,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     __syncthreads();
     if (t + 1 < n_tiles) regs.load(kws, v, g, hkv, n_rows, tile_k0(t + 1), tile_ke(t + 1), tid);
     if (active) {
-      f32x16 s0, s1;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s0[i] = s1[i] = 0.f;
+      f32x16 s0 = negm, s1 = negm;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(&cur.k[n][16 * s + 8 * half]);
@@ -234,13 +237,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
           s1[i] = (uint32_t)(o0 + 32) <= span ? s1[i] : -INFINITY;
         }
       }
-      float ma = s0[0], mb = s1[0];
+      // three-input maxima: 16 instructions for the 32 scores of the lane
+      auto max3 = [](float x, float y, float z) { return fmaxf(fmaxf(x, y), z); };
+      float ma[5], mb[5];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) {
-        ma = fmaxf(ma, s0[i]);
-        mb = fmaxf(mb, s1[i]);
+      for (int k = 0; k < 5; ++k) {
+        ma[k] = max3(s0[3 * k], s0[3 * k + 1], s0[3 * k + 2]);
+        mb[k] = max3(s1[3 * k], s1[3 * k + 1], s1[3 * k + 2]);
       }
-      const float mx = pair_max(fmaxf(ma, mb));
+      const float mc = max3(s0[15], s1[15], ma[0]);
+      const float md = max3(ma[1], ma[2], ma[3]), me = max3(ma[4], mb[0], mb[1]), mf = max3(mb[2], mb[3], mb[4]);
+      const float m_use = m == -INFINITY ? 0.f : m;
+      const float mx = pair_max(fmaxf(max3(mc, md, me), mf)) + m_use;
       // The reference m moves only when a score exceeds it by more than
       // kLazyMax, so O and l are rescaled on few tiles; in between the
       // probabilities are at most 2^kLazyMax.
@@ -253,19 +261,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
           for (int i = 0; i < 16; ++i) o[dt][i] *= corr;
         m = m_new;
+        // re-base this tile's scores and the next tiles' starting value
+        const float m_use2 = m == -INFINITY ? 0.f : m;
+        const float d = m_use - m_use2;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          s0[i] += d;
+          s1[i] += d;
+          negm[i] = -m_use2;
+        }
       }
-      const float m_use = m == -INFINITY ? 0.f : m;
       float ls0 = 0.f, ls1 = 0.f;
       bf16x8 pf[4];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p0 = __builtin_amdgcn_exp2f(s0[i] - m_use);
+        const float p0 = __builtin_amdgcn_exp2f(s0[i]);
         ls0 += p0;
         pf[i >> 3][i & 7] = (__bf16)p0;
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p1 = __builtin_amdgcn_exp2f(s1[i] - m_use);
+        const float p1 = __builtin_amdgcn_exp2f(s1[i]);
         ls1 += p1;
         pf[2 + (i >> 3)][i & 7] = (__bf16)p1;
       }
