@@ -125,6 +125,72 @@ def summarize_pmc(paths):
     return out
 
 
+def ablation(cfg, s, tree, qt, kt, vt, out, steps, warmup):
+    """Shared-prefix scoring against uncached independent scoring, same kernel.
+
+    The independent layout packs every branch as a tree of its own: the trunk
+    through the branch's anchor, then the branch (the unpacked causal sequence of
+    the branch). Q, K and V rows are gathered from the shared layout's rows, so
+    both layouts score the same tokens at the same positions; the branch and
+    anchor rows of both must agree up to summation order.
+    """
+    import numpy as np
+    import torch
+    import tree_attention_spec_amd as tas
+    dev = qt.device
+    lay = {k_: v_.cpu().numpy() for k_, v_ in tree.arrays().items()}
+    a = s["anchors"].astype(np.int64)
+    w = s["branch_len"].astype(np.int64)
+    t_of_b = np.repeat(np.arange(len(s["trunk_len"])), s["n_branches"])
+    trunk_rows = lay["tree_off"][t_of_b].astype(np.int64)
+    idx = np.concatenate([np.concatenate([trunk_rows[b] + np.arange(a[b] + 1), lay["branch_off"][b] + np.arange(w[b] - 1)])
+                          for b in range(len(a))])
+    idx_t = torch.from_numpy(idx).to(dev)
+    qi, ki, vi = qt.index_select(0, idx_t), kt.index_select(0, idx_t), vt.index_select(0, idx_t)
+    tree_i = tas.spec_tree_pack((a + 1).astype(np.int32), np.ones(len(a), np.int32), a.astype(np.int32),
+                                w.astype(np.int32), device=dev)
+    out_i = torch.empty_like(qi)
+    work_i = torch.empty(tas.attn_work_bytes(tree_i, cfg.hq, cfg.hkv, cfg.head_dim, qi.dtype), dtype=torch.uint8,
+                         device=dev)
+
+    def timed(tr, q_, k_, v_, o_, wk):
+        for _ in range(warmup):
+            tas.spec_tree_attn_fwd(tr, q_, k_, v_, rope_base=cfg.rope_base, out=o_, work=wk)
+        per = {}
+        for _ in range(steps):
+            tm = tas.KernelTimer(capacity=16)
+            with tm:
+                tas.spec_tree_attn_fwd(tr, q_, k_, v_, rope_base=cfg.rope_base, out=o_, work=wk)
+            for name, ms in tm.durations():
+                per.setdefault(name, []).append(ms)
+        return {n_: sum(x) / len(x) for n_, x in per.items()}
+
+    work_s = torch.empty(tas.attn_work_bytes(tree, cfg.hq, cfg.hkv, cfg.head_dim, qt.dtype), dtype=torch.uint8,
+                         device=dev)
+    t_shared = timed(tree, qt, kt, vt, out, work_s)
+    t_ind = timed(tree_i, qi, ki, vi, out_i, work_i)
+    # branch rows and anchor rows of both layouts
+    toff_i = tree_i.arrays()["tree_off"].cpu().numpy().astype(np.int64)
+    rows_s, rows_i = [], []
+    for b in range(len(a)):
+        rows_s.append(np.concatenate([[trunk_rows[b] + a[b]], lay["branch_off"][b] + np.arange(w[b] - 1)]))
+        rows_i.append(toff_i[b] + a[b] + np.arange(w[b]))
+    rs = torch.from_numpy(np.concatenate(rows_s)).to(dev)
+    ri = torch.from_numpy(np.concatenate(rows_i)).to(dev)
+    diff = (out.index_select(0, rs).float() - out_i.index_select(0, ri).float()).abs().max().item()
+    p_shared = causal_pairs(s)
+    p_ind = int(np.sum((a + 1) * (a + 2) // 2 + (w - 1) * (a + 1) + (w - 1) * w // 2))
+    return {
+        "what": "tree attention (RoPE + attention kernels) on the shared-prefix packed tree vs every branch "
+                "scored as its own causal sequence (trunk through its anchor + its branch), same kernels",
+        "shared": {"rows": int(tree.n_rows), "causal_pairs": p_shared, "kernel_ms": t_shared},
+        "independent": {"rows": int(tree_i.n_rows), "causal_pairs": p_ind, "kernel_ms": t_ind},
+        "pair_ratio": p_ind / p_shared,
+        "attention_time_ratio": t_ind["tree_attn"] / t_shared["tree_attn"],
+        "max_abs_diff_branch_and_anchor_rows": diff,
+    }
+
+
 def cpu_baseline(cfg, s, q, k, v, z_rows_fn, N, R, n_attn=24, n_e2e=6):
     """Time the oracle on a bounded random sample and scale it to the full step."""
     import numpy as np
@@ -172,6 +238,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="gqa8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ablation", action="store_true",
+                    help="also time every branch scored as its own causal sequence (uncached independent "
+                         "scoring) with the same kernels, and report the ratio to the shared-prefix layout")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM counters) and exit")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DB",
@@ -321,6 +390,9 @@ def main():
         "components": components,
         "kernel_ms": avg,
     }
+    if args.ablation:
+        log("ablation: every branch as its own causal sequence")
+        result["ablation"] = ablation(cfg, s, tree, qt, kt, vt, out, steps=max(2, min(args.steps, 5)), warmup=2)
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(cfg, s, q, k, v, lambda rows: gen_logit_rows(cfg, R, rows), N, R)

@@ -143,3 +143,36 @@ def test_attn_workload_sampled(name):
     pr = torch.from_numpy(case.lay["step_pred_row"][steps].astype(np.int64)).cuda()
     assert torch.equal(ro[torch.from_numpy(steps).cuda()], out[pr])
     assert torch.isfinite(out.float()).all()
+
+
+def test_attn_independent_layout_matches_shared():
+    """Every branch packed as its own tree (trunk through its anchor, then the branch) —
+    the uncached independent scoring the paper page's Figure 13 compares against — gives
+    the shared-prefix layout's branch and anchor rows (same tokens, same positions)."""
+    import torch
+    import tree_attention_spec_amd as tas
+    say("attn: independent per-branch layout vs shared prefix")
+    case = Case(small_config("batched", n_trees=2, trunk=200, branches=9, width=8, hq=8, hkv=2,
+                             head_dim=128))
+    q, k, v = case.qkv()
+    out, _ = _run(case)
+    s, lay = case.s, case.lay
+    a = s["anchors"].astype(np.int64)
+    w = s["branch_len"].astype(np.int64)
+    t_of_b = np.repeat(np.arange(len(s["trunk_len"])), s["n_branches"])
+    trunk0 = lay["tree_off"][t_of_b].astype(np.int64)
+    idx = np.concatenate([np.concatenate([trunk0[b] + np.arange(a[b] + 1), lay["branch_off"][b] + np.arange(w[b] - 1)])
+                          for b in range(len(a))])
+    tree_i = tas.spec_tree_pack((a + 1).astype(np.int32), np.ones(len(a), np.int32), a.astype(np.int32),
+                                w.astype(np.int32))
+    assert tree_i.n_rows == len(idx)
+    out_i, _ = tas.spec_tree_attn_fwd(tree_i, to_device(q[idx]), to_device(k[idx]), to_device(v[idx]),
+                                      rope_base=case.cfg.rope_base)
+    torch.cuda.synchronize()
+    toff_i = from_device(tree_i.arrays()["tree_off"]).astype(np.int64)
+    rows_s = np.concatenate([np.concatenate([[trunk0[b] + a[b]], lay["branch_off"][b] + np.arange(w[b] - 1)])
+                             for b in range(len(a))])
+    rows_i = np.concatenate([toff_i[b] + a[b] + np.arange(w[b]) for b in range(len(a))])
+    diff = np.abs(from_device(out)[rows_s] - from_device(out_i)[rows_i]).max()
+    say("  max abs diff %.3e over %d rows" % (diff, len(rows_s)))
+    assert diff <= ATTN_ATOL
