@@ -207,13 +207,38 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
   for (int i = 0; i < 16; ++i) negm[i] = 0.f;
 
+  // O^T += V^T P^T for one tile's probabilities p and V^T tile vt
+  auto pv = [&](const AttnSmem<D> &vt, const bf16x8 (&p)[4]) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&vt.vt[32 * dt + n][16 * kk + 8 * half]);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[kk], o[dt], 0, 0, 0);
+      }
+  };
+
+  // Software pipeline: the P V product of a tile runs one tile late, beside the
+  // next tile's exponentials (the two take about the same time), so each tile is
+  //   S(t), softmax(t) with O += V(t-1) P(t-1) | barrier | stage tile t+1 | barrier.
+  // Before the first tile the "previous" probabilities are zero and the other
+  // V^T buffer is cleared, so that product adds nothing.
+  bf16x8 pp[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pp[kk][e] = (__bf16)0.f;
+  if (n_tiles > 0) regs.store(sm[0], tid);
+  for (int i = tid; i < (int)(sizeof(sm[1].vt) / 16); i += NT)
+    reinterpret_cast<uint4 *>(&sm[1].vt[0][0])[i] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+  if (n_tiles > 1) regs.load(kws, v, g, hkv, n_rows, tile_k0(1), tile_ke(1), tid);
+
   for (int t = 0; t < n_tiles; ++t) {
     AttnSmem<D> &cur = sm[t & 1];
+    AttnSmem<D> &prv = sm[(t + 1) & 1];  // tile t - 1, then the staging buffer of tile t + 1
     const int k0 = tile_k0(t);
     const bool branch = t >= n_trunk;
-    regs.store(cur, tid);
-    __syncthreads();
-    if (t + 1 < n_tiles) regs.load(kws, v, g, hkv, n_rows, tile_k0(t + 1), tile_ke(t + 1), tid);
     if (active) {
       f32x16 s0 = negm, s1 = negm;
 #pragma unroll
@@ -253,6 +278,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       // kLazyMax, so O and l are rescaled on few tiles; in between the
       // probabilities are at most 2^kLazyMax.
       if (__any(mx > m + kLazyMax)) {
+        pv(prv, pp);  // the previous tile's product, at the old reference
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pp[kk][e] = (__bf16)0.f;
         const float m_new = mx > m + kLazyMax ? mx : m;
         const float corr = m_new == m ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
         l *= corr;
@@ -286,27 +316,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         pf[2 + (i >> 3)][i & 7] = (__bf16)p1;
       }
       l += ls0 + ls1;
-      // O^T += V^T P^T, key group by key group: the first half of the MFMAs needs
-      // only the first 32 keys' probabilities, so the exponentials of the other
-      // 32 run beside them
+      pv(prv, pp);  // the previous tile's product, beside this tile's exponentials
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&cur.vt[32 * dt + n][16 * kk + 8 * half]);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], o[dt], 0, 0, 0);
-        }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two V^T fragments
-      __builtin_amdgcn_sched_group_barrier(0x402, 56, 0);  // probabilities of keys 0..31
-#pragma unroll
-      for (int i = 0; i < 4 * DT - 2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA,
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the next fragment,
-        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);  // keys 32..63 meanwhile
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      for (int kk = 0; kk < 4; ++kk) pp[kk] = pf[kk];
     }
+    __syncthreads();  // every wave is done with tile t - 1
+    if (t + 1 < n_tiles) regs.store(prv, tid);
+    __syncthreads();
+    if (t + 2 < n_tiles) regs.load(kws, v, g, hkv, n_rows, tile_k0(t + 2), tile_ke(t + 2), tid);
   }
+  if (active && n_tiles > 0) pv(sm[(n_tiles - 1) & 1], pp);
 
   const float inv = 1.f / pair_sum(l);
   if (active && it.q0 + n < it.q1) {
