@@ -203,7 +203,8 @@ spec_status spec_tree_attn_fwd(const spec_tree_layout *layout, int32_t n_heads_q
  * -inv_norm * A_{b,i-1} * G_{b,i} (prefix products A, suffix sums G).
  *
  * Arguments:
- *   layout        from spec_tree_pack (uses n_steps, n_branches, step_off).
+ *   layout        from spec_tree_pack (uses n_steps, n_branches, max_branch_len,
+ *                 step_off, step_branch).
  *   vocab         V >= 1.
  *   logit_dtype   SPEC_BF16 or SPEC_F32.
  *   d_draft       [R, V] draft logits z; NaN or -inf mean inactive support (q = 0).
@@ -216,6 +217,11 @@ spec_status spec_tree_attn_fwd(const spec_tree_layout *layout, int32_t n_heads_q
  *   d_work        workspace of *work_bytes bytes, or NULL for a size query.
  * Data preconditions (not checked; violations give NaN): teacher finite, at
  * least one active draft entry per row.
+ * For bf16 logits with V a multiple of 8 the work runs as one cooperative
+ * kernel whose workgroups wait on each other through bounded polls; if a poll
+ * ever times out (it cannot while the kernel is resident on the device as a
+ * whole) alpha and the loss come back NaN. Calls that share a workspace must
+ * not overlap in time.
  * Errors: SPEC_ERR_INVALID_ARG, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP.
  */
 spec_status spec_e2etv_fwd_bwd(const spec_tree_layout *layout, int64_t vocab,

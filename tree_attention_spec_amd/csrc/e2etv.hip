@@ -6,23 +6,29 @@
 // support is kept. [SpecOPD notes page, "Inputs and code mapping"]: low
 // precision is promoted to float32; NaN draft entries are inactive support.
 //
-// Three kernels on the caller's stream:
-//   e2etv_stats  a persistent grid, one 1024-thread workgroup per CU, walks the
-//                rows; per row, pass 1 streams it for both log-sum-exps (online
-//                max/sum per lane) and pass 2 re-streams it (partly from cache,
-//                since only one row per CU is in flight) for
-//                alpha = sum 2^min(z', y') and S = sum over {z' < y'} of 2^z', where
-//                z' = z*log2(e) - lse2(z) is log2 q (and y' likewise log2 p);
-//   e2etv_scan   one workgroup: per branch the suffix sums G and prefix products
-//                A give c_s = dL/d alpha_s = -w A_{i-1} G_i (no division), and the
-//                loss is reduced in float64 in a fixed order;
-//   e2etv_grad   grad[s,u] = c_s * q_u * (1[z'_u < y'_u] - S_s), written once. The
-//                statistics pass stores the decision z'_u < y'_u as a bitmask, so
-//                the gradient reads the draft row and 1 bit per element, not the
-//                teacher row (6.1 instead of 8 bytes per element).
+// Main path (bf16 rows whose length is a multiple of 8, every branch spanning
+// at most two steps of the team pipeline): one cooperative kernel,
+// e2etv_fused_team_kernel, reads each logit once and writes each gradient
+// element once (8 bytes per element). Teams of workgroups split every row by
+// vocabulary slices, exchange per-member log-sum-exps and (alpha, S) partials
+// through agent-scope atomics, form each row's coefficient
+// c_s = dL/d alpha_s = -w A_{i-1} G_i from its branch's alphas, and write
+// grad[s,u] = c_s q_u (1[z'_u < y'_u] - S_s) from the row slice still held in
+// registers (z' = z log2(e) - lse2(z) is log2 q, y' likewise log2 p).
+// e2etv_loss_kernel then adds the per-branch sums of prefix products in
+// branch order. Details above the kernel.
+//
+// Fallback path (float32 rows, other lengths, long branches), three kernels:
+//   statistics   e2etv_stats_team_kernel (single read of each row by a team) or
+//                e2etv_stats_kernel (one workgroup per row, two passes): the
+//                log-sum-exps, alpha = sum 2^min(z', y'), S = sum over {z' < y'}
+//                of 2^z', and the decision z' < y' as a bitmask;
+//   e2etv_scan   one wave per branch: suffix sums G and prefix products A give
+//                c_s (no division); the loss is reduced in float64 in a fixed order;
+//   e2etv_grad   grad[s,u] from the draft row and the bitmask, written once.
 // Every reduction has a fixed order, so results are bitwise reproducible. The
-// strict test z' < y' is the same expression in all three places, so the set
-// {q < p} used for S and for the gradient is the same set.
+// strict test z' < y' is the same expression wherever {q < p} is used, so the
+// set used for S and for the gradient is the same set.
 #include <algorithm>
 #include <mutex>
 #include <type_traits>
