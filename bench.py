@@ -70,8 +70,9 @@ def measured_traffic(kernel: str, src_hash: str):
 # kernel name rocprofv3 records) and the source file whose hash keys its
 # measured traffic.
 MARK_KERNELS = {
-    "tree_attn": (["tree_attn_bf16_kernel", "tree_attn_f32_kernel"], "attn.hip"),
+    "tree_attn": (["tree_attn_tiled_kernel", "tree_attn_bf16_kernel", "tree_attn_f32_kernel"], "attn.hip"),
     "rope_k": (["rope_k_kernel"], "rope.hip"),
+    "kv_tiles": (["kv_tile_kernel"], "rope.hip"),
     "readout": (["readout_kernel"], "attn.hip"),
     "e2etv_clear": (["e2etv_fuse_clear"], "e2etv.hip"),
     "e2etv_fused": (["e2etv_fused_team_kernel"], "e2etv.hip"),

@@ -47,9 +47,12 @@ spec_status check_layout(const spec_tree_layout *L, bool need_device) {
   return SPEC_OK;
 }
 
-// Workspace of the attention call: RoPE table, then rotated K.
+// Workspace of the attention call: RoPE table, then rotated K ([Hkv][N][D]), or,
+// for bf16 with head dim 128, rotated K and transposed V in 64-key tiles
+// ([Hkv][ceil(N/64)][64*128] each).
 struct AttnWork {
-  size_t off_tab, off_k, total;
+  size_t off_tab, off_k, off_v, total;
+  bool tiled;
 };
 
 AttnWork attn_work(const spec_tree_layout &L, int hkv, int D, spec_dtype dt) {
@@ -57,8 +60,17 @@ AttnWork attn_work(const spec_tree_layout &L, int hkv, int D, spec_dtype dt) {
   const size_t n_pos = (size_t)L.max_pos + 1;
   w.off_tab = 0;
   w.off_k = align_up(n_pos * (D / 2) * sizeof(float2), 256);
-  const size_t esz = dt == SPEC_BF16 ? 2 : 4;
-  w.total = align_up(w.off_k + (size_t)L.n_rows * hkv * D * esz, 256);
+  w.tiled = dt == SPEC_BF16 && D == 128;
+  if (w.tiled) {
+    const size_t tiles = ((size_t)L.n_rows + kKeyTile - 1) / kKeyTile;
+    const size_t bytes = (size_t)hkv * tiles * kKeyTile * D * 2;
+    w.off_v = w.off_k + align_up(bytes, 256);
+    w.total = w.off_v + align_up(bytes, 256);
+  } else {
+    const size_t esz = dt == SPEC_BF16 ? 2 : 4;
+    w.off_v = 0;
+    w.total = align_up(w.off_k + (size_t)L.n_rows * hkv * D * esz, 256);
+  }
   return w;
 }
 
@@ -171,9 +183,16 @@ extern "C" spec_status spec_tree_attn_fwd(const spec_tree_layout *layout, int32_
   prof_mark(s, "attn:begin");
   SPEC_HIP_TRY(launch_rope_table(tab, layout->max_pos + 1, D / 2, (double)rope_base, s));
   prof_mark(s, "rope_table");
-  SPEC_HIP_TRY(launch_rope_k(d_k, kws, tab, layout->row_pos, layout->n_rows, hkv, D, dtype, s));
-  prof_mark(s, "rope_k");
-  SPEC_HIP_TRY(launch_tree_attn(*layout, hq, hkv, D, dtype, d_q, kws, d_v, tab, scale, d_out, s));
+  if (w.tiled) {
+    void *vws = wb + w.off_v;
+    SPEC_HIP_TRY(launch_kv_tiles(d_k, d_v, kws, vws, tab, layout->row_pos, layout->n_rows, hkv, s));
+    prof_mark(s, "kv_tiles");
+    SPEC_HIP_TRY(launch_tree_attn_tiled(*layout, hq, hkv, d_q, kws, vws, tab, scale, d_out, s));
+  } else {
+    SPEC_HIP_TRY(launch_rope_k(d_k, kws, tab, layout->row_pos, layout->n_rows, hkv, D, dtype, s));
+    prof_mark(s, "rope_k");
+    SPEC_HIP_TRY(launch_tree_attn(*layout, hq, hkv, D, dtype, d_q, kws, d_v, tab, scale, d_out, s));
+  }
   prof_mark(s, "tree_attn");
   if (d_readout && layout->n_steps > 0) {
     const int64_t row_bytes = (int64_t)hq * D * (dtype == SPEC_BF16 ? 2 : 4);

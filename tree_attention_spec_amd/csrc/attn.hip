@@ -345,6 +345,219 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
+// ---------------------------------------------------------------------------
+// Head dim 128 with tiled K and V (kv_tile_kernel): the same block decomposition
+// and per-tile math as tree_attn_bf16_kernel, but a 64-key tile is copied
+// global -> LDS by direct-to-LDS loads (16 bytes per lane, laid out by the
+// pre-pass exactly as the MFMA fragments read them), so staging takes no
+// registers and no VALU work. Key tiles are aligned to multiples of 64 in the
+// packed order; keys outside a query's visible ranges are masked as before.
+// The copy of tile t+1 is issued before tile t is computed, into the other of
+// two LDS buffers; one wait and one barrier per tile.
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima), as an
+// immediate the compiler's own wait bookkeeping sees
+constexpr int kWaitVm0 = 0x0F70;
+
+struct alignas(16) TiledSmem {
+  __bf16 k[KT * 128];   // slot r*16 + (c ^ (r & 15)) holds dims 8c..8c+7 of key r
+  __bf16 vt[128 * KT];  // slot d*8 + (c ^ (d & 7)) holds positions 8c..8c+7 of dim d
+};
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void tree_attn_tiled_kernel(
+    const AttnItem *__restrict__ items, int hkv, int group, int hsub,
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ kt, const __bf16 *__restrict__ vt,
+    __bf16 *__restrict__ out, const float2 *__restrict__ tab, const int32_t *__restrict__ row_pos,
+    const int32_t *__restrict__ row_trunk_hi, const int32_t *__restrict__ row_branch_lo,
+    int32_t n_key_tiles, int hq, float sl2) {
+  constexpr int D = 128, KS = D / 16, DT = D / 32;
+  constexpr int CHUNKS = 2 * KT * D * 2 / 1024;  // 1 KB copies per tile (K and V)
+  __shared__ TiledSmem smA, smB;
+
+  const int bid = blockIdx.x;
+  const int g = bid % hkv;
+  const int rest = bid / hkv;
+  const int hs = rest % hsub;
+  const AttnItem it = items[rest / hsub];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int n = lane & 31, half = lane >> 5;
+  const int hl = hs * NW + w;
+  const bool active = hl < group;  // wave-uniform
+  const int h = g * group + (active ? hl : 0);
+  const int qrow = min(it.q0 + n, it.q1 - 1);
+
+  // 64-aligned key tiles: trunk tiles cover [tk0, tk1), then branch tiles [bk0, bk1)
+  const int tt0 = it.tk0 / KT, tt1 = it.tk1 > it.tk0 ? (it.tk1 - 1) / KT + 1 : tt0;
+  const int bt0 = it.bk0 / KT, bt1 = it.bk1 > it.bk0 ? (it.bk1 - 1) / KT + 1 : bt0;
+  const int n_trunk = tt1 - tt0;
+  const int n_tiles = n_trunk + (bt1 - bt0);
+  auto tile_index = [&](int t) { return t < n_trunk ? tt0 + t : bt0 + (t - n_trunk); };
+
+  // copy tile t into `dst`: wave w issues copies w, w + NW, ... of the tile's
+  // 1 KB pieces (K pieces first, then V^T)
+  const __bf16 *kbase = kt + (int64_t)g * n_key_tiles * KT * D;
+  const __bf16 *vbase = vt + (int64_t)g * n_key_tiles * KT * D;
+  auto copy_tile = [&](int t, TiledSmem &dst) {
+    const int64_t off = (int64_t)tile_index(t) * KT * D;
+#pragma unroll
+    for (int j = w; j < CHUNKS; j += NW) {
+      const bool isk = j < CHUNKS / 2;
+      const int jj = isk ? j : j - CHUNKS / 2;
+      const __bf16 *src = (isk ? kbase : vbase) + off + jj * 512 + lane * 8;
+      __bf16 *lds = (isk ? dst.k : dst.vt) + jj * 512;
+      __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+    }
+  };
+
+  if (n_tiles > 0) copy_tile(0, smA);
+
+  bf16x8 qf[KS];
+  {
+    const __bf16 *qp = q + ((int64_t)qrow * hq + h) * D;
+    const float2 *tp = tab + (int64_t)row_pos[qrow] * (D / 2);
+#pragma unroll
+    for (int s = 0; s < KS / 2; ++s) {
+      const int d0 = 16 * s + 8 * half;
+      const bf16x8 x1 = *reinterpret_cast<const bf16x8 *>(qp + d0);
+      const bf16x8 x2 = *reinterpret_cast<const bf16x8 *>(qp + d0 + D / 2);
+      bf16x8 y1, y2;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float2 cs = tp[d0 + j];
+        const float a = (float)x1[j], b = (float)x2[j];
+        y1[j] = (__bf16)((a * cs.x - b * cs.y) * sl2);
+        y2[j] = (__bf16)((b * cs.x + a * cs.y) * sl2);
+      }
+      qf[s] = y1;
+      qf[s + KS / 2] = y2;
+    }
+  }
+  int thi = row_trunk_hi[qrow];
+  int blo = row_branch_lo[qrow];
+  // kept in registers: a reload inside the tile loop would have to wait for
+  // the tile copies in flight
+  asm volatile("" : "+v"(thi), "+v"(blo));
+  const int bhi = qrow;
+
+  f32x16 o[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  f32x16 negm;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negm[i] = 0.f;
+
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+
+  auto body = [&](int t, const TiledSmem &cur, TiledSmem &next) {
+    if (t + 1 < n_tiles) copy_tile(t + 1, next);
+    __builtin_amdgcn_sched_barrier(0);  // the copies go out before this tile's work
+    const int k0 = tile_index(t) * KT;
+    const bool branch = t >= n_trunk;
+    if (active) {
+      f32x16 s0 = negm, s1 = negm;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int c = 2 * s + half;
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(&cur.k[(n * 16 + (c ^ (n & 15))) * 8]);
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(&cur.k[((32 + n) * 16 + (c ^ (n & 15))) * 8]);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], s1, 0, 0, 0);
+      }
+      const bool need_mask = branch || k0 < it.tk0 || (k0 + KT > it.tfull);
+      if (need_mask) {
+        const int vlo = branch ? blo : it.tk0, vhi = branch ? bhi : thi;
+        const uint32_t span = (uint32_t)(vhi - vlo);
+        const int base = k0 + 4 * half - vlo;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int o0 = base + 8 * (i >> 2) + (i & 3);
+          s0[i] = (uint32_t)o0 <= span ? s0[i] : -INFINITY;
+          s1[i] = (uint32_t)(o0 + 32) <= span ? s1[i] : -INFINITY;
+        }
+      }
+      auto max3 = [](float x, float y, float z) { return fmaxf(fmaxf(x, y), z); };
+      float ma[5], mb[5];
+#pragma unroll
+      for (int k = 0; k < 5; ++k) {
+        ma[k] = max3(s0[3 * k], s0[3 * k + 1], s0[3 * k + 2]);
+        mb[k] = max3(s1[3 * k], s1[3 * k + 1], s1[3 * k + 2]);
+      }
+      const float mc = max3(s0[15], s1[15], ma[0]);
+      const float md = max3(ma[1], ma[2], ma[3]), me = max3(ma[4], mb[0], mb[1]), mf = max3(mb[2], mb[3], mb[4]);
+      const float m_use = m == -INFINITY ? 0.f : m;
+      const float mx = pair_max(fmaxf(max3(mc, md, me), mf)) + m_use;
+      if (__any(mx > m + kLazyMax)) {
+        const float m_new = mx > m + kLazyMax ? mx : m;
+        const float corr = m_new == m ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+        l *= corr;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[dt][i] *= corr;
+        m = m_new;
+        const float m_use2 = m == -INFINITY ? 0.f : m;
+        const float d = m_use - m_use2;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          s0[i] += d;
+          s1[i] += d;
+          negm[i] = -m_use2;
+        }
+      }
+      float ls0 = 0.f, ls1 = 0.f;
+      bf16x8 pf[4];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(s0[i]);
+        ls0 += p0;
+        pf[i >> 3][i & 7] = (__bf16)p0;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p1 = __builtin_amdgcn_exp2f(s1[i]);
+        ls1 += p1;
+        pf[2 + (i >> 3)][i & 7] = (__bf16)p1;
+      }
+      l += ls0 + ls1;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int row = 32 * dt + n, c = 2 * kk + half;
+          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&cur.vt[(row * 8 + (c ^ (row & 7))) * 8]);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], o[dt], 0, 0, 0);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of tile t + 1 landed
+    __syncthreads();
+  };
+  for (int t = 0; t < n_tiles; t += 2) {
+    body(t, smA, smB);
+    if (t + 1 < n_tiles) body(t + 1, smB, smA);
+  }
+
+  const float inv = 1.f / pair_sum(l);
+  if (active && it.q0 + n < it.q1) {
+    __bf16 *op = out + ((int64_t)(it.q0 + n) * hq + h) * D;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        __bf16 r4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r4[e] = (__bf16)(o[t][4 * i4 + e] * inv);
+        uint2 pk;
+        __builtin_memcpy(&pk, r4, 8);
+        *reinterpret_cast<uint2 *>(op + 32 * t + 8 * i4 + 4 * half) = pk;
+      }
+  }
+}
+
 // Exact float32 path: one wavefront per (row, head); lane holds dims lane and lane + 64.
 template <int D>
 __global__ __launch_bounds__(64) void tree_attn_f32_kernel(
@@ -434,6 +647,24 @@ hipError_t launch_bf16_d(const spec_tree_layout &L, int hq, int hkv, const void 
   return launch_bf16<D, 1>(L, hq, hkv, q, kws, v, tab, scale, out, s);
 }
 
+template <int NW>
+hipError_t launch_tiled(const spec_tree_layout &L, int hq, int hkv, const void *q, const void *kt,
+                        const void *vt, const float2 *tab, float scale, void *out, hipStream_t s) {
+  const int group = hq / hkv;
+  const int hsub = (group + NW - 1) / NW;
+  const int64_t nblk = (int64_t)L.n_attn_items * hkv * hsub;
+  if (nblk == 0) return hipSuccess;
+  if (nblk > INT32_MAX) return hipErrorInvalidValue;
+  const int32_t n_key_tiles = (int32_t)((L.n_rows + KT - 1) / KT);
+  const float sl2 = scale * 1.4426950408889634f;
+  hipLaunchKernelGGL((tree_attn_tiled_kernel<NW>), dim3((unsigned)nblk), dim3(NW * 64), 0, s,
+                     reinterpret_cast<const AttnItem *>(L.attn_items), hkv, group, hsub,
+                     static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(kt),
+                     static_cast<const __bf16 *>(vt), static_cast<__bf16 *>(out), tab, L.row_pos,
+                     L.row_trunk_hi, L.row_branch_lo, n_key_tiles, hq, sl2);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_f32(const spec_tree_layout &L, int hq, int hkv, const void *q, const void *kws,
                       const void *v, const float2 *tab, float scale, void *out, hipStream_t s) {
@@ -446,6 +677,16 @@ hipError_t launch_f32(const spec_tree_layout &L, int hq, int hkv, const void *q,
 }
 
 }  // namespace
+
+hipError_t launch_tree_attn_tiled(const spec_tree_layout &L, int32_t hq, int32_t hkv, const void *q,
+                                  const void *kt, const void *vt, const float2 *tab, float scale,
+                                  void *out, hipStream_t s) {
+  const int group = hq / hkv;
+  if (group >= 8) return launch_tiled<8>(L, hq, hkv, q, kt, vt, tab, scale, out, s);
+  if (group >= 3) return launch_tiled<4>(L, hq, hkv, q, kt, vt, tab, scale, out, s);
+  if (group == 2) return launch_tiled<2>(L, hq, hkv, q, kt, vt, tab, scale, out, s);
+  return launch_tiled<1>(L, hq, hkv, q, kt, vt, tab, scale, out, s);
+}
 
 hipError_t launch_tree_attn(const spec_tree_layout &L, int32_t hq, int32_t hkv, int32_t D,
                             spec_dtype dtype, const void *q, const void *kws, const void *v,

@@ -52,6 +52,14 @@ hipError_t launch_rope_k(const void *k, void *kws, const float2 *tab, const int3
 hipError_t launch_tree_attn(const spec_tree_layout &L, int32_t hq, int32_t hkv, int32_t head_dim,
                             spec_dtype dtype, const void *q, const void *kws, const void *v,
                             const float2 *tab, float scale, void *out, hipStream_t stream);
+// Head dim 128, bf16: K rotated and V transposed into 64-key tiles (rope.hip),
+// read by the tiled attention kernel (attn.hip).
+constexpr int kKeyTile = 64;
+hipError_t launch_kv_tiles(const void *k, const void *v, void *kt, void *vt, const float2 *tab,
+                           const int32_t *row_pos, int64_t n_rows, int32_t hkv, hipStream_t stream);
+hipError_t launch_tree_attn_tiled(const spec_tree_layout &L, int32_t hq, int32_t hkv, const void *q,
+                                  const void *kt, const void *vt, const float2 *tab, float scale,
+                                  void *out, hipStream_t stream);
 hipError_t launch_readout(const int32_t *pred_row, int64_t n_steps, int64_t row_bytes,
                           const void *out, void *readout, hipStream_t stream);
 

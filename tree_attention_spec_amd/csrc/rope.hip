@@ -83,4 +83,89 @@ hipError_t launch_rope_k(const void *k, void *kws, const float2 *tab, const int3
   return hipGetLastError();
 }
 
+// Tiled K and V for the bf16 head-dim-128 attention kernel, which copies whole
+// 64-key tiles into LDS with direct-to-LDS loads (no registers, no shuffles on
+// the way). Per KV head g and key tile t (keys 64t .. 64t+63, zero past N):
+//   Kt[g][t]: 64 rows x 16 chunks of 8 dims, rotated like rope_k; chunk c of row r
+//             sits in slot r*16 + (c ^ (r & 15)), so the 32 rows an MFMA fragment
+//             reads fall in distinct LDS banks;
+//   Vt[g][t]: V transposed, 128 dims x 8 chunks of 8 keys; within each 16-key
+//             group the key quads are stored in the order [0, 2, 1, 3] (the order
+//             the P^T operand of the P V MFMA expects), and chunk c of dim d sits
+//             in slot d*8 + (c ^ (d & 7)).
+// One 256-thread workgroup per (tile, head); V goes through LDS for the transpose.
+constexpr int kTileKeys = kKeyTile;
+
+__global__ __launch_bounds__(256) void kv_tile_kernel(const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
+                                                      __bf16 *__restrict__ kt, __bf16 *__restrict__ vt,
+                                                      const float2 *__restrict__ tab,
+                                                      const int32_t *__restrict__ row_pos, int64_t n_rows,
+                                                      int32_t hkv, int32_t n_tiles) {
+  constexpr int D = 128, H = 64, CH = 16;
+  __shared__ __bf16 vs[kTileKeys][D + 8];
+  const int tile = blockIdx.x % n_tiles, g = blockIdx.x / n_tiles;
+  const int tid = threadIdx.x;
+  const int64_t key0 = (int64_t)tile * kTileKeys;
+  // V rows of the tile into LDS (zero past the last row)
+  for (int i = tid; i < kTileKeys * CH; i += 256) {
+    const int r = i / CH, c = i % CH;
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (key0 + r < n_rows) x = *reinterpret_cast<const uint4 *>(v + ((key0 + r) * hkv + g) * D + c * 8);
+    *reinterpret_cast<uint2 *>(&vs[r][c * 8]) = make_uint2(x.x, x.y);
+    *reinterpret_cast<uint2 *>(&vs[r][c * 8 + 4]) = make_uint2(x.z, x.w);
+  }
+  // K: rotate and store swizzled chunks
+  __bf16 *kdst = kt + ((int64_t)g * n_tiles + tile) * kTileKeys * D;
+  for (int p = tid; p < kTileKeys * CH; p += 256) {
+    const int r = p / CH, c = (p % CH) ^ (r & (CH - 1));
+    __bf16 y[8];
+    if (key0 + r < n_rows) {
+      const __bf16 *src = k + ((key0 + r) * hkv + g) * D;
+      const int j0 = (c % (CH / 2)) * 8;  // pair index of the chunk's first dim
+      const float2 *cs = tab + (int64_t)row_pos[key0 + r] * H + j0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x1 = (float)src[j0 + e], x2 = (float)src[j0 + e + H];
+        const float2 t = cs[e];
+        y[e] = c < CH / 2 ? (__bf16)(x1 * t.x - x2 * t.y) : (__bf16)(x2 * t.x + x1 * t.y);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = (__bf16)0.f;
+    }
+    uint4 pk;
+    __builtin_memcpy(&pk, y, 16);
+    *reinterpret_cast<uint4 *>(kdst + (int64_t)p * 8) = pk;
+  }
+  __syncthreads();
+  // V^T: slot p = d*8 + c' holds logical chunk c = c' ^ (d & 7): positions
+  // 8c .. 8c+7 of dim d, i.e. key quads [0, 2, 1, 3][2 (c & 1) + 0, 1] of the
+  // 16-key group c / 2
+  __bf16 *vdst = vt + ((int64_t)g * n_tiles + tile) * kTileKeys * D;
+  for (int p = tid; p < D * 8; p += 256) {
+    const int d = p / 8, c = (p % 8) ^ (d & 7);
+    const int grp = c / 2, q0 = (c & 1) ? 1 : 0;  // quads 0, 2 (c even) or 1, 3 (c odd)
+    __bf16 y[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y[e] = vs[16 * grp + 4 * q0 + e][d];
+      y[4 + e] = vs[16 * grp + 4 * (q0 + 2) + e][d];
+    }
+    uint4 pk;
+    __builtin_memcpy(&pk, y, 16);
+    *reinterpret_cast<uint4 *>(vdst + (int64_t)p * 8) = pk;
+  }
+}
+
+hipError_t launch_kv_tiles(const void *k, const void *v, void *kt, void *vt, const float2 *tab,
+                           const int32_t *row_pos, int64_t n_rows, int32_t hkv, hipStream_t stream) {
+  const int64_t n_tiles = (n_rows + kTileKeys - 1) / kTileKeys;
+  if (n_tiles * hkv > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kv_tile_kernel, dim3((unsigned)(n_tiles * hkv)), dim3(256), 0, stream,
+                     static_cast<const __bf16 *>(k), static_cast<const __bf16 *>(v),
+                     static_cast<__bf16 *>(kt), static_cast<__bf16 *>(vt), tab, row_pos, n_rows, hkv,
+                     (int32_t)n_tiles);
+  return hipGetLastError();
+}
+
 }  // namespace spec
