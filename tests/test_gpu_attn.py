@@ -49,6 +49,9 @@ SMALL = [
     dict(tag="s_2trees_g2", base="batched", n_trees=2, trunk=130, branches=11, width=8, hq=4, hkv=2,
          head_dim=128),
     dict(tag="s_d128_g8", base="stress", trunk=260, branches=30, width=16, hq=16, hkv=2, head_dim=128),
+    # head dim 128 with GQA groups 1 and 3 (one and four waves per workgroup, a partial head slice)
+    dict(tag="s_d128_g1", base="gqa8b", trunk=230, branches=12, width=9, hq=2, hkv=2, head_dim=128),
+    dict(tag="s_d128_g3", base="gqa8b", n_trees=3, trunk=90, branches=5, width=11, hq=6, hkv=2, head_dim=128),
 ]
 
 
