@@ -360,7 +360,7 @@ constexpr int kWaitVm0 = 0x0F70;
 
 struct alignas(16) TiledSmem {
   __bf16 k[KT * 128];   // slot r*16 + (c ^ (r & 15)) holds dims 8c..8c+7 of key r
-  __bf16 vt[128 * KT];  // slot d*8 + (c ^ (d & 7)) holds positions 8c..8c+7 of dim d
+  __bf16 vt[128 * KT];  // slot d*8 + (c ^ vt_swizzle(d)) holds positions 8c..8c+7 of dim d
 };
 
 template <int NW>
@@ -400,8 +400,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const __bf16 *vbase = vt + (int64_t)g * n_key_tiles * KT * D;
   auto copy_tile = [&](int t, TiledSmem &dst) {
     const int64_t off = (int64_t)tile_index(t) * KT * D;
+    static_assert(CHUNKS % NW == 0, "each wave issues the same number of copies");
 #pragma unroll
-    for (int j = w; j < CHUNKS; j += NW) {
+    for (int i = 0; i < CHUNKS / NW; ++i) {
+      const int j = w + NW * i;
       const bool isk = j < CHUNKS / 2;
       const int jj = isk ? j : j - CHUNKS / 2;
       const __bf16 *src = (isk ? kbase : vbase) + off + jj * 512 + lane * 8;
@@ -410,12 +412,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   };
 
+  // per-row inputs first: the RoPE table row depends on row_pos
+  const int pos = row_pos[qrow];
+  int thi = row_trunk_hi[qrow];
+  int blo = row_branch_lo[qrow];
   if (n_tiles > 0) copy_tile(0, smA);
 
   bf16x8 qf[KS];
   {
     const __bf16 *qp = q + ((int64_t)qrow * hq + h) * D;
-    const float2 *tp = tab + (int64_t)row_pos[qrow] * (D / 2);
+    const float2 *tp = tab + (int64_t)pos * (D / 2);
 #pragma unroll
     for (int s = 0; s < KS / 2; ++s) {
       const int d0 = 16 * s + 8 * half;
@@ -433,10 +439,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       qf[s + KS / 2] = y2;
     }
   }
-  int thi = row_trunk_hi[qrow];
-  int blo = row_branch_lo[qrow];
-  // kept in registers: a reload inside the tile loop would have to wait for
-  // the tile copies in flight
+  // kept in registers and computed here, beside the first tile copy: left to
+  // itself the compiler sinks the Q loads and rotation behind the first
+  // barrier, and a reload of thi/blo inside the tile loop would wait for the
+  // tile copies in flight
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    u32x4 r = __builtin_bit_cast(u32x4, qf[s]);
+    asm volatile("" : "+v"(r));
+    qf[s] = __builtin_bit_cast(bf16x8, r);
+  }
   asm volatile("" : "+v"(thi), "+v"(blo));
   const int bhi = qrow;
 
@@ -529,7 +541,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const int row = 32 * dt + n, c = 2 * kk + half;
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&cur.vt[(row * 8 + (c ^ (row & 7))) * 8]);
+          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&cur.vt[(row * 8 + (c ^ vt_swizzle(row))) * 8]);
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], o[dt], 0, 0, 0);
         }
     }

@@ -55,6 +55,11 @@ hipError_t launch_tree_attn(const spec_tree_layout &L, int32_t hq, int32_t hkv, 
 // Head dim 128, bf16: K rotated and V transposed into 64-key tiles (rope.hip),
 // read by the tiled attention kernel (attn.hip).
 constexpr int kKeyTile = 64;
+// Slot swizzle of the V^T key tiles: chunk c (8 keys) of dim d is stored in
+// slot d*8 + (c ^ vt_swizzle(d)). Any 16 consecutive dims reading one chunk
+// then fall in 16 distinct 16-byte bank groups of LDS, and so do any 8 (a
+// 128-bit LDS read is served 16 lanes at a time).
+__device__ __host__ inline int vt_swizzle(int d) { return (d & 7) ^ ((d >> 3) & 1); }
 hipError_t launch_kv_tiles(const void *k, const void *v, void *kt, void *vt, const float2 *tab,
                            const int32_t *row_pos, int64_t n_rows, int32_t hkv, hipStream_t stream);
 hipError_t launch_tree_attn_tiled(const spec_tree_layout &L, int32_t hq, int32_t hkv, const void *q,

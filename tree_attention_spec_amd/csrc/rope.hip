@@ -92,7 +92,7 @@ hipError_t launch_rope_k(const void *k, void *kws, const float2 *tab, const int3
 //   Vt[g][t]: V transposed, 128 dims x 8 chunks of 8 keys; within each 16-key
 //             group the key quads are stored in the order [0, 2, 1, 3] (the order
 //             the P^T operand of the P V MFMA expects), and chunk c of dim d sits
-//             in slot d*8 + (c ^ (d & 7)).
+//             in slot d*8 + (c ^ vt_swizzle(d)).
 // One 256-thread workgroup per (tile, head); V goes through LDS for the transpose.
 constexpr int kTileKeys = kKeyTile;
 
@@ -138,12 +138,12 @@ __global__ __launch_bounds__(256) void kv_tile_kernel(const __bf16 *__restrict__
     *reinterpret_cast<uint4 *>(kdst + (int64_t)p * 8) = pk;
   }
   __syncthreads();
-  // V^T: slot p = d*8 + c' holds logical chunk c = c' ^ (d & 7): positions
+  // V^T: slot p = d*8 + c' holds logical chunk c = c' ^ vt_swizzle(d): positions
   // 8c .. 8c+7 of dim d, i.e. key quads [0, 2, 1, 3][2 (c & 1) + 0, 1] of the
   // 16-key group c / 2
   __bf16 *vdst = vt + ((int64_t)g * n_tiles + tile) * kTileKeys * D;
   for (int p = tid; p < D * 8; p += 256) {
-    const int d = p / 8, c = (p % 8) ^ (d & 7);
+    const int d = p / 8, c = (p % 8) ^ vt_swizzle(d);
     const int grp = c / 2, q0 = (c & 1) ? 1 : 0;  // quads 0, 2 (c even) or 1, 3 (c odd)
     __bf16 y[8];
 #pragma unroll
