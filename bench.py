@@ -47,39 +47,42 @@ def causal_pairs(s) -> int:
 
 
 def source_hash(*names) -> str:
+    """Hash of the named library sources and the header they all share."""
     h = hashlib.sha256()
-    for n in names:
+    for n in ("common.h",) + names:
         with open(os.path.join(ROOT, "tree_attention_spec_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, src_hash: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
+def measured_traffic(kernel: str, src_hash: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on this workload and the kernel's source has not changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f).get(kernel)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_hash") != src_hash:
+    if not rec or rec.get("source_hash") != src_hash or rec.get("workload") != workload:
         return None
     return rec.get("bytes_per_launch")
 
 
 # Library timing marks -> the kernels each covers (matched by substring of the
-# kernel name rocprofv3 records) and the source file whose hash keys its
-# measured traffic.
+# kernel name rocprofv3 records) and the source files whose hash keys its
+# measured traffic (the attention kernel reads tiles laid out by rope.hip).
 MARK_KERNELS = {
-    "tree_attn": (["tree_attn_tiled_kernel", "tree_attn_bf16_kernel", "tree_attn_f32_kernel"], "attn.hip"),
-    "rope_k": (["rope_k_kernel"], "rope.hip"),
-    "kv_tiles": (["kv_tile_kernel"], "rope.hip"),
-    "readout": (["readout_kernel"], "attn.hip"),
-    "e2etv_clear": (["e2etv_fuse_clear"], "e2etv.hip"),
-    "e2etv_fused": (["e2etv_fused_team_kernel"], "e2etv.hip"),
-    "e2etv_loss": (["e2etv_loss_kernel"], "e2etv.hip"),
-    "e2etv_stats": (["e2etv_team_clear", "e2etv_stats_team_kernel", "e2etv_stats_kernel"], "e2etv.hip"),
-    "e2etv_scan": (["e2etv_scan_kernel"], "e2etv.hip"),
-    "e2etv_grad": (["e2etv_grad_kernel"], "e2etv.hip"),
+    "tree_attn": (["tree_attn_tiled_kernel", "tree_attn_bf16_kernel", "tree_attn_f32_kernel"],
+                  ("attn.hip", "rope.hip")),
+    "rope_k": (["rope_k_kernel"], ("rope.hip",)),
+    "kv_tiles": (["kv_tile_kernel"], ("rope.hip",)),
+    "readout": (["readout_kernel"], ("attn.hip",)),
+    "e2etv_clear": (["e2etv_fuse_clear"], ("e2etv.hip",)),
+    "e2etv_fused": (["e2etv_fused_team_kernel"], ("e2etv.hip",)),
+    "e2etv_loss": (["e2etv_loss_kernel"], ("e2etv.hip",)),
+    "e2etv_stats": (["e2etv_team_clear", "e2etv_stats_team_kernel", "e2etv_stats_kernel"], ("e2etv.hip",)),
+    "e2etv_scan": (["e2etv_scan_kernel"], ("e2etv.hip",)),
+    "e2etv_grad": (["e2etv_grad_kernel"], ("e2etv.hip",)),
 }
 
 
@@ -100,7 +103,7 @@ def write_traffic(fetch_db, write_db, copy_fetch_db, copy_write_db, workload):
             continue
         fk = sum(v.get("FETCH_SIZE", {}).get("mean", 0.0) for v in ks)
         wk = sum(v.get("WRITE_SIZE", {}).get("mean", 0.0) for v in ks)
-        out[mark] = {"source_hash": source_hash(src), "workload": workload,
+        out[mark] = {"source_hash": source_hash(*src), "workload": workload,
                      "fetch_bytes": fk * 1024 * fs, "write_bytes": wk * 1024 * ws,
                      "bytes_per_launch": fk * 1024 * fs + wk * 1024 * ws,
                      "fetch_kib_raw": fk, "write_kib_raw": wk}
@@ -355,17 +358,19 @@ def main():
         "e2etv": {"bound": "hbm", "ms": t_e2e, "kernels": e2e_kernels, "algorithmic_bytes": e2e_bytes,
                   "achieved": e2e_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": e2e_gbs / PEAK_HBM_GBS},
     }
-    # The dominant stage by time. E2E-TV is one operation split over three
-    # kernels (statistics, scan, gradient); its algorithmic bytes (each logit
-    # read once, the gradient written once) belong to the operation, so its
-    # roofline is taken over the sum of the three kernels' launch durations.
+    # The dominant stage by time. E2E-TV is one operation that may span several
+    # kernels (the fused pass with its clear and loss kernels, or statistics,
+    # scan and gradient); its algorithmic bytes (each logit read once, the
+    # gradient written once) belong to the operation, so its roofline is taken
+    # over the sum of those kernels' launch durations.
     if t_attn >= t_e2e:
         roof = {"kernel": "tree_attn", "kernels": ["tree_attn"], "bound": "mfma",
                 "achieved": attn_tflops, "peak": attn_peak, "unit": "TFLOP/s",
                 "frac": attn_tflops / attn_peak, "algorithmic_flop_per_launch": attn_flop,
-                "traffic": measured_traffic("tree_attn", source_hash("attn.hip"))}
+                "traffic": measured_traffic("tree_attn", source_hash(*MARK_KERNELS["tree_attn"][1]), args.config)}
     else:
-        traffic = [measured_traffic(n, source_hash("e2etv.hip")) for n in e2e_kernels]
+        traffic = [measured_traffic(n, source_hash(*MARK_KERNELS[n][1]), args.config)
+                   for n in e2e_kernels]
         roof = {"kernel": "e2etv", "kernels": e2e_kernels, "bound": "hbm", "achieved": e2e_gbs,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": e2e_gbs / PEAK_HBM_GBS,
                 "algorithmic_bytes_per_launch": e2e_bytes,
