@@ -87,6 +87,45 @@ def test_attn_edge_trees():
         _full_compare(Case(cfg, structure=s), ATTN_ATOL)
 
 
+@pytest.mark.parametrize("head_dim", [128, 64])
+def test_attn_moving_reference_and_scale(head_dim):
+    """Scores that climb from key tile to key tile, with an explicit softmax scale.
+
+    The query has a constant component 16 and each key the component 0.5 * (row // 16) in the
+    slowest-turning RoPE pair (base 1e6, so that pair barely rotates): with scale 0.125 a query's
+    largest visible score grows by ~6 log2 units per 64-key tile, so the online softmax moves its
+    reference on most tiles. Trunk keys past a branch's anchor carry the largest scores of their
+    tiles and must be masked before the maximum is taken.
+    """
+    from specgen import f32_to_bf16_bits
+    say("attn parity: moving softmax reference, D=%d" % head_dim)
+    cfg = small_config("gqa8b", trunk=333, branches=14, width=9, width_mode="uniform", hq=8, hkv=2,
+                       head_dim=head_dim)
+    case = Case(cfg)
+    q, k, v = case.qkv()
+    lay = case.lay
+    j = head_dim // 2 - 1
+    qf, kf = widen(q).astype(np.float32), widen(k).astype(np.float32)
+    qf[:, :, j] = 16.0
+    kf[:, :, j] = 0.5 * (np.arange(case.N) // 16)[:, None]
+    q2, k2 = f32_to_bf16_bits(qf), f32_to_bf16_bits(kf)
+    assert np.array_equal(widen(k2)[:, 0, j], kf[:, 0, j])          # the climbing component is exact
+    import torch
+    import tree_attention_spec_amd as tas
+    s = case.s
+    tree = tas.spec_tree_pack(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"])
+    out, ro = tas.spec_tree_attn_fwd(tree, to_device(q2), to_device(k2), to_device(v), rope_base=1e6,
+                                     softmax_scale=0.125)
+    torch.cuda.synchronize()
+    got = from_device(out)
+    want = tree_attn_ref(lay, widen(q2), widen(k2), widen(v), 1e6, scale=0.125)
+    err = np.abs(got - want).max()
+    say("  max abs err %.3e (N=%d)" % (err, case.N))
+    assert np.isfinite(got).all()
+    assert err <= ATTN_ATOL
+    assert np.array_equal(from_device(ro), got[lay["step_pred_row"]])
+
+
 def test_attn_isolation_is_bitwise():
     """Changing the values of every row outside a branch's history leaves its rows bit-identical."""
     import torch
