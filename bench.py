@@ -196,40 +196,56 @@ def ablation(cfg, s, tree, qt, kt, vt, out, steps, warmup):
 
 
 def cpu_baseline(cfg, s, q, k, v, z_rows_fn, N, R, n_attn=24, n_e2e=6):
-    """Time the oracle on a bounded random sample and scale it to the full step."""
+    """Time the oracle on a bounded random sample and scale it to the full step.
+
+    The sample is spread over one thread per host CPU (at most 16): NumPy releases
+    the interpreter lock inside its array operations, so each thread runs the
+    oracle on its own share of rows. Every thread gets n_attn attention rows and
+    n_e2e logit rows, so the wall time stays near that of one thread on the
+    smaller sample while the sample grows with the thread count.
+    """
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
     from oracle import e2etv_coef_ref, e2etv_grad_ref, e2etv_row_stats_ref, pack_ref, rope_ref, tree_attn_ref
     from specgen import bf16_bits_to_f32
 
     def widen(a):
         return bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
 
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
     rng = np.random.default_rng(123)
     t0 = time.perf_counter()
     lay = pack_ref(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"])
     t_pack = time.perf_counter() - t0
     qd, kd, vd = widen(q), widen(k), widen(v)
-    t0 = time.perf_counter()
-    rope_ref(kd, lay["row_pos"][:, None], cfg.rope_base)
-    t_fixed = time.perf_counter() - t0
-    rows = rng.choice(N, size=min(n_attn, N), replace=False)
-    t0 = time.perf_counter()
-    tree_attn_ref(lay, qd, kd, vd, cfg.rope_base, rows=rows)
-    t_call = time.perf_counter() - t0
-    t_attn = t_fixed + (N / len(rows)) * max(t_call - t_fixed, 0.0)
-    srows = np.sort(rng.choice(R, size=min(n_e2e, R), replace=False))
-    zs, ys = z_rows_fn(srows)
-    t0 = time.perf_counter()
-    alpha, S, _, _, qq, pp = e2etv_row_stats_ref(zs.astype(np.float64), ys.astype(np.float64))
-    c = e2etv_coef_ref(alpha, [0, len(srows)])
-    e2etv_grad_ref(qq, pp, S, c)
-    t_e2e = (R / len(srows)) * (time.perf_counter() - t0)
+    with ThreadPoolExecutor(workers) as ex:
+        # the K rotation every attention call repeats, timed on its own
+        t0 = time.perf_counter()
+        rope_ref(kd, lay["row_pos"][:, None], cfg.rope_base)
+        t_fixed = time.perf_counter() - t0
+        rows = rng.choice(N, size=min(n_attn * workers, N), replace=False)
+        t0 = time.perf_counter()
+        list(ex.map(lambda part: tree_attn_ref(lay, qd, kd, vd, cfg.rope_base, rows=part),
+                    np.array_split(rows, workers)))
+        t_call = time.perf_counter() - t0
+        t_attn = t_fixed + (N / len(rows)) * max(t_call - t_fixed, 0.0)
+        srows = np.sort(rng.choice(R, size=min(n_e2e * workers, R), replace=False))
+        zs, ys = z_rows_fn(srows)
+
+        def e2e(part):
+            alpha, S, _, _, qq, pp = e2etv_row_stats_ref(zs[part].astype(np.float64), ys[part].astype(np.float64))
+            c = e2etv_coef_ref(alpha, [0, len(part)])
+            e2etv_grad_ref(qq, pp, S, c)
+
+        t0 = time.perf_counter()
+        list(ex.map(e2e, np.array_split(np.arange(len(srows)), workers)))
+        t_e2e = (R / len(srows)) * (time.perf_counter() - t0)
     total = t_pack + t_attn + t_e2e
     return {
-        "value": R / total, "unit": "supervised rows/s", "cores": 1, "kind": "oracle",
+        "value": R / total, "unit": "supervised rows/s", "cores": workers, "kind": "oracle",
         "sample": "%d random packed rows of tree attention (plus the full K rotation) and %d random "
-                  "logit rows of E2E-TV stats+gradient, float64 NumPy, one thread; scaled to the "
-                  "full step (N=%d rows, R=%d steps)" % (len(rows), len(srows), N, R),
+                  "logit rows of E2E-TV stats+gradient, float64 NumPy, spread over %d threads; scaled "
+                  "to the full step (N=%d rows, R=%d steps)" % (len(rows), len(srows), workers, N, R),
         "seconds_full_step_estimate": total,
         "host_cpus": len(os.sched_getaffinity(0)),
     }
