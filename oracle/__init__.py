@@ -2,8 +2,8 @@
 
 A plain, slow, obviously correct NumPy float64 statement of what the path
 computes: the proposal-tree pack, tree-masked GQA attention with RoPE at
-semantic positions, predecessor-row readout and the E2E-TV surrogate with its
-gradient. It shares no code with the HIP library and imports nothing from it;
+semantic positions, predecessor-row readout, the E2E-TV surrogate with its
+gradient, and indexed GDN state replay for linear-attention targets. It shares no code with the HIP library and imports nothing from it;
 the only shared module is ``specgen`` (seeded inputs, no method arithmetic).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
@@ -12,7 +12,7 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 Sources, cited by page title and section throughout:
   * [SpecOPD paper page] "SpecOPD: Branch-Parallel On-Policy Distillation for
     Speculative Decoding" (thelatestinai.com paper page): abstract and the
-    captions of Figures 2, 3, 4 and 13.
+    captions of Figures 2, 3, 4, 5 and 13.
   * [SpecOPD notes page] "SpecOPD: independent supervision branches and
     acceptance-prefix optimization" (daiwk auto-research notes): sections
     "Equations", "Inputs and code mapping" and "Checks, negative controls,
@@ -36,4 +36,15 @@ from .e2etv_ref import (  # noqa: F401
     e2etv_loss_ref,
     e2etv_ref,
     e2etv_row_stats_ref,
+)
+from .gdn_ref import (  # noqa: F401
+    ancestors_ref,
+    conv_ancestry_ref,
+    gdn_branch_brute_ref,
+    gdn_checkpoints_ref,
+    gdn_features_ref,
+    gdn_replay_ref,
+    gdn_step_ref,
+    silu,
+    trunk_len_ref,
 )

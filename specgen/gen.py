@@ -23,6 +23,7 @@ QKV_CHUNK_ROWS = 128
 LOGIT_CHUNK_ROWS = 8
 
 _S_STRUCT, _S_Q, _S_K, _S_V, _S_DRAFT, _S_TEACHER = range(6)
+_S_GDN_Q, _S_GDN_K, _S_GDN_V, _S_GDN_TAPS, _S_GDN_GATES, _S_GDN_STATE = range(6, 12)
 
 
 def _workers() -> int:
@@ -179,3 +180,45 @@ def gen_logit_rows(cfg: Config, n_steps: int, rows):
         out_z[i] = z[int(r) - c * LOGIT_CHUNK_ROWS]
         out_y[i] = y[int(r) - c * LOGIT_CHUNK_ROWS]
     return out_z, out_y
+
+
+# ----------------------------------------------------------------------------- GDN replay inputs
+
+def gen_gdn(seed: int, n_rows: int, heads: int, head_dim: int, conv_width: int):
+    """Inputs of the indexed GDN replay on a packed tree of n_rows rows.
+
+    Returns a dict:
+      xq, xk, xv  [N, H, D] uint16 bfloat16 bits, N(0,1): projections before the
+                  short convolution, for every packed row;
+      taps        [3, H, D, K] float32, N(0, 0.5^2): convolution taps of q, k, v
+                  (tap j on the j-th ancestor);
+      alpha       [N, H] float32, U(0.9, 1.0): per-token decay;
+      beta        [N, H] float32, U(0.05, 0.95): per-token write strength.
+    """
+    out = {}
+    for name, stream in (("xq", _S_GDN_Q), ("xk", _S_GDN_K), ("xv", _S_GDN_V)):
+        arr = np.empty((n_rows, heads, head_dim), dtype=np.uint16)
+        jobs = [(arr[r0:r0 + QKV_CHUNK_ROWS], c) for c, r0 in enumerate(range(0, n_rows, QKV_CHUNK_ROWS))]
+        with ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(lambda j, st=stream: _fill_normal(j[0], seed, st, j[1], True), jobs))
+        out[name] = arr
+    g = _rng(seed, _S_GDN_TAPS)
+    out["taps"] = (0.5 * g.standard_normal((3, heads, head_dim, conv_width))).astype(np.float32)
+    g = _rng(seed, _S_GDN_GATES)
+    out["alpha"] = g.uniform(0.9, 1.0, size=(n_rows, heads)).astype(np.float32)
+    out["beta"] = g.uniform(0.05, 0.95, size=(n_rows, heads)).astype(np.float32)
+    return out
+
+
+def gen_gdn_states(seed: int, n_states: int, heads: int, head_dim: int, std: float = 0.2):
+    """n_states synthetic float32 GDN states [n_states, H, D, D], N(0, std^2), as
+    stand-in checkpoints where a trunk pass is not run."""
+    st = np.empty((n_states, heads, head_dim, head_dim), dtype=np.float32)
+
+    def fill(i):
+        st[i] = np.float32(std) * _rng(seed, _S_GDN_STATE, i).standard_normal(
+            (heads, head_dim, head_dim), dtype=np.float32)
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(fill, range(n_states)))
+    return st
