@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define SPEC_TREE_ABI_VERSION 1
+#define SPEC_TREE_ABI_VERSION 2
 #define SPEC_MAX_BRANCH_LEN 64 /* largest supported branch width W_b */
 
 typedef enum spec_status {
@@ -88,7 +88,7 @@ typedef struct spec_tree_layout {
   int64_t n_rows;          /* N */
   int64_t n_steps;         /* R */
   int32_t n_attn_items;    /* query blocks in attn_items */
-  int32_t reserved0;
+  int32_t max_trunk_len;   /* largest trunk length T_t */
 
   /* per tree */
   int32_t *tree_off;        /* [n_trees+1] first packed row of each tree; last = N */
@@ -229,6 +229,57 @@ spec_status spec_e2etv_fwd_bwd(const spec_tree_layout *layout, int64_t vocab,
                                const void *d_teacher, float inv_norm, float *d_alpha,
                                float *d_loss, float *d_grad, void *d_work, size_t *work_bytes,
                                spec_stream stream);
+
+/*
+ * spec_gdn_replay_fwd -- indexed GDN state replay: the linear-attention
+ * (GDN) outputs of every branch row.
+ *
+ * Defines: [SpecOPD paper page, Figure 5] (branch-parallel scoring with linear
+ * attention): a shared trunk pass keeps an FP32 GDN state at every
+ * chunk-token boundary; a branch starts from the checkpoint at or below its
+ * anchor, advances it with the trunk tokens after that checkpoint through the
+ * anchor, then takes its own tokens, updating the state and reading it with
+ * each token's query; checkpoints are only read; the short causal
+ * convolution follows the branch's ancestry. [SpecOPD paper page, Figure 13]:
+ * GDN work includes that replay.
+ *
+ * The pages do not write the recurrence out; this is the gated delta rule,
+ * per head, with state S (D x D, value rows i, key columns j):
+ *   S_ij <- alpha S_ij + beta (v_i - alpha sum_j' S_ij' k_j') k_j,
+ *   o_i   = sum_j S_ij q_j   (after the update),
+ * on features that are, per token and head, a depthwise convolution of width
+ * K along the ancestry path (tap m on the m-th ancestor: the token itself,
+ * its parent, ...; nothing before the tree's first token), then SiLU, with q
+ * and k then L2-normalised over D and q scaled by 1/sqrt(D).
+ * Checkpoint c of tree t is S after trunk tokens 0 .. c*chunk-1 (c = 0: the
+ * zero state); a branch anchored at a starts from c = (a + 1) / chunk.
+ *
+ * Arguments:
+ *   layout      from spec_tree_pack (uses n_trees, n_branches, max_trunk_len,
+ *               tree_off, branch_tree, branch_anchor, branch_len, branch_off).
+ *   n_heads     H >= 1; head_dim D in {64, 128}; conv_width K in 1..4;
+ *               chunk >= 1 (the checkpoint spacing C).
+ *   d_xq, d_xk, d_xv  [N, H, D] bf16: q, k, v projections of every packed
+ *               row before the convolution.
+ *   d_taps      [3, H, D, K] float32: taps of the q, k and v convolutions.
+ *   d_alpha     [N, H] float32, the decay alpha in (0, 1]; d_beta [N, H]
+ *               float32, the write strength.
+ *   d_ckpt      [n_trees, max_trunk_len / chunk + 1, H, D, D] float32, each
+ *               state stored key-major (S_ij at j * D + i); slots a shorter
+ *               tree never reaches are not read.
+ *   d_out       [N, H, D] float32: the rows of branches are written; trunk
+ *               rows are left as they are (the trunk pass owns them).
+ * All buffers are the caller's; the call needs no workspace and allocates
+ * nothing. Data preconditions (not checked): inputs finite; the convolved q
+ * and k of every replayed token are not all zero (their norms divide).
+ * Errors: SPEC_ERR_INVALID_ARG, SPEC_ERR_UNSUPPORTED (head_dim, conv_width),
+ * SPEC_ERR_HIP.
+ */
+spec_status spec_gdn_replay_fwd(const spec_tree_layout *layout, int32_t n_heads,
+                                int32_t head_dim, int32_t conv_width, int32_t chunk,
+                                const void *d_xq, const void *d_xk, const void *d_xv,
+                                const float *d_taps, const float *d_alpha, const float *d_beta,
+                                const float *d_ckpt, float *d_out, spec_stream stream);
 
 /*
  * Measurement hook (benchmarks only; it changes no result).

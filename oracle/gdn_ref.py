@@ -125,16 +125,16 @@ def gdn_checkpoints_ref(layout, q, k, v, alpha, beta, C):
     return ck
 
 
-def gdn_replay_ref(layout, q, k, v, alpha, beta, ckpt, C):
+def gdn_replay_ref(layout, q, k, v, alpha, beta, ckpt, C, branches=None):
     """GDN outputs of every branch row by indexed replay, [N, H, D].
 
     Branch b copies checkpoint floor((a_b + 1) / C) of its tree, replays trunk
     tokens cC .. a_b, then steps through y_{b,1} .. y_{b,W_b-1} and reads each
     one's output (reading 2). Trunk rows are left at zero (the trunk pass owns
-    them)."""
+    them), and so are the rows of branches not in ``branches`` (default: all)."""
     N, H, D = q.shape
     out = np.zeros((N, H, D))
-    for b in range(layout["n_branches"]):
+    for b in (range(layout["n_branches"]) if branches is None else branches):
         t, a = int(layout["branch_tree"][b]), int(layout["branch_anchor"][b])
         off = int(layout["tree_off"][t])
         c = (a + 1) // C

@@ -151,3 +151,28 @@ def test_e2etv_size_query_and_checks(tas):
     big = ctypes.c_size_t(1 << 30)
     assert lib.spec_e2etv_fwd_bwd(ctypes.byref(L), 151936, 1, None, None, 0.0, None, None, None,
                                   ctypes.c_void_p(0x1000), ctypes.byref(big), None) == 1
+
+
+def test_gdn_argument_checks(tas):
+    """spec_gdn_replay_fwd rejects bad arguments before any launch (no GPU is touched)."""
+    from tree_attention_spec_amd import _lib
+    lib = tas.library()
+    L = _query_layout(tas)
+    assert L.max_trunk_len == CONFIGS["gqa8b"].trunk
+    P = ctypes.c_void_p(0x1000)
+
+    def call(H, D, K, C, p=P):
+        return lib.spec_gdn_replay_fwd(ctypes.byref(L), H, D, K, C, p, p, p, p, p, p, p, p, None)
+
+    assert call(32, 128, 4, 64) == 1                # the layout has no device arrays yet
+    fake = ctypes.cast(ctypes.c_void_p(0x1000), _lib._i32p)
+    for f in ("tree_off", "branch_tree", "branch_anchor", "branch_len", "branch_off"):
+        setattr(L, f, fake)
+    assert call(0, 128, 4, 64) == 1                 # no heads
+    assert call(32, 96, 4, 64) == 2                 # head_dim outside {64, 128}
+    assert call(32, 128, 5, 64) == 2                # convolution wider than 4
+    assert call(32, 128, 0, 64) == 2
+    assert call(32, 128, 4, 0) == 1                 # checkpoint spacing
+    assert call(32, 128, 4, 64, None) == 1          # NULL buffers
+    assert call(32, 128, 4, 64, ctypes.c_void_p(0x1004)) == 1
+    assert "aligned" in lib.spec_last_error().decode()

@@ -1,0 +1,122 @@
+"""GPU parity: spec_gdn_replay_fwd against the float64 oracle (indexed replay from
+the same float32 checkpoints), plus each branch scored as its own sequence."""
+import numpy as np
+import pytest
+
+from _util import say, to_device, widen
+from oracle import (gdn_branch_brute_ref, gdn_checkpoints_ref, gdn_features_ref, gdn_replay_ref,
+                    pack_ref)
+from specgen import CONFIGS, gen_gdn, gen_gdn_states, gen_structure
+
+pytestmark = pytest.mark.gpu
+
+# float32 state and features against float64, relative to the largest output: the
+# recurrence's rounding over at most C - 1 + W - 1 steps of D-term float32 sums gives
+# ~1e-6 (measured <= 4e-7 on the small cases)
+GDN_RTOL = 1e-5
+
+
+def _run(s, lay, H, D, K, C, ckpt_kmajor, inp):
+    import torch
+    import tree_attention_spec_amd as tas
+    tree = tas.spec_tree_pack(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"])
+    assert tree.max_trunk_len == int(np.max(s["trunk_len"]))
+    dev = lambda a: to_device(np.ascontiguousarray(a))
+    out = torch.full((lay["n_rows"], H, D), 7.0, dtype=torch.float32, device="cuda")
+    tas.spec_gdn_replay_fwd(tree, dev(inp["xq"]), dev(inp["xk"]), dev(inp["xv"]), dev(inp["taps"]),
+                            dev(inp["alpha"]), dev(inp["beta"]), dev(ckpt_kmajor), chunk=C, out=out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def _features(lay, inp):
+    t = inp["taps"].astype(np.float64)
+    return gdn_features_ref(lay, widen(inp["xq"]), widen(inp["xk"]), widen(inp["xv"]), t[0], t[1], t[2])
+
+
+def _compare(s, H, D, K, C, seed, brute=True):
+    lay = pack_ref(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"])
+    inp = gen_gdn(seed, lay["n_rows"], H, D, K)
+    q, k, v = _features(lay, inp)
+    al, be = inp["alpha"].astype(np.float64), inp["beta"].astype(np.float64)
+    ck = gdn_checkpoints_ref(lay, q, k, v, al, be, C).astype(np.float32)      # the trunk pass's states
+    got = _run(s, lay, H, D, K, C, np.swapaxes(ck, -1, -2), inp)
+    want = gdn_replay_ref(lay, q, k, v, al, be, ck.astype(np.float64), C)
+    br = lay["row_branch"] >= 0
+    scale = max(np.abs(want[br]).max(), 1e-30) if br.any() else 1.0
+    err = np.abs(got[br] - want[br]).max() if br.any() else 0.0
+    say("  N=%d H=%d D=%d K=%d C=%d: max abs err %.3e (max |o| %.3e)" % (lay["n_rows"], H, D, K, C, err, scale))
+    assert err <= GDN_RTOL * scale
+    assert np.all(got[~br] == 7.0)                                              # trunk rows untouched
+    if brute:   # the GPU against each branch as its own sequence (no checkpoints, no parent array)
+        t = inp["taps"].astype(np.float64)
+        for b in range(lay["n_branches"]):
+            W = int(lay["branch_len"][b])
+            if W < 2:
+                continue
+            r0 = int(lay["branch_off"][b])
+            ref = gdn_branch_brute_ref(lay, widen(inp["xq"]), widen(inp["xk"]), widen(inp["xv"]),
+                                       t[0], t[1], t[2], al, be, b)
+            # the checkpoints went through float32, so allow their rounding too
+            assert np.abs(got[r0:r0 + W - 1] - ref).max() <= 2 * GDN_RTOL * scale
+
+
+CASES = [
+    # (tag, trunk lengths, anchors per tree, widths, H, D, K, C)
+    ("d128_k4_c64", [200], [[0, 62, 63, 64, 127, 199, 63, 17]], [[5, 3, 9, 2, 1, 16, 4, 7]], 2, 128, 4, 64),
+    ("d64_k4_c16", [90], [[0, 15, 16, 47, 89, 30, 30]], [[3, 6, 2, 1, 9, 4, 4]], 3, 64, 4, 16),
+    ("d128_k1_c8", [41], [[0, 7, 8, 40, 21]], [[4, 2, 6, 3, 1]], 1, 128, 1, 8),
+    ("d64_k2_c4_2trees", [23, 9], [[0, 3, 4, 22, 11], [8, 0, 5]], [[2, 5, 3, 6, 1], [4, 3, 2]], 2, 64, 2, 4),
+    ("d128_k3_c64_shortT", [30, 70], [[29, 0, 10], [69, 63, 64]], [[6, 3, 2], [4, 5, 8]], 1, 128, 3, 64),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_gdn_small(case):
+    tag, T, anchors, widths, H, D, K, C = case
+    say("gdn parity: %s" % tag)
+    s = dict(trunk_len=np.array(T, np.int32), n_branches=np.array([len(a) for a in anchors], np.int32),
+             anchors=np.concatenate([np.array(a, np.int32) for a in anchors]),
+             branch_len=np.concatenate([np.array(w, np.int32) for w in widths]))
+    _compare(s, H, D, K, C, seed=len(tag))
+
+
+def test_gdn_no_branch_rows():
+    """Only one-token branches (no rows): nothing is written."""
+    say("gdn parity: one-token branches only")
+    s = dict(trunk_len=np.array([50], np.int32), n_branches=np.array([3], np.int32),
+             anchors=np.array([0, 20, 49], np.int32), branch_len=np.array([1, 1, 1], np.int32))
+    _compare(s, 2, 64, 4, 16, seed=3, brute=False)
+
+
+@pytest.mark.slow
+def test_gdn_workload_sampled():
+    """The 8B-like tree (trunk 4096, 256 branches of width 16) with 32 heads of 128, width-4
+    convolution and checkpoints every 64 tokens, in the benchmarked launch; stand-in
+    checkpoint states; sampled branches against the oracle."""
+    import torch
+    import tree_attention_spec_amd as tas
+    cfg = CONFIGS["gqa8b"]
+    s = gen_structure(cfg)
+    lay = pack_ref(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"])
+    H, D, K, C = 32, 128, 4, 64
+    say("gdn parity: 8B-like tree full size, sampled branches")
+    inp = gen_gdn(cfg.seed, lay["n_rows"], H, D, K)
+    tree = tas.spec_tree_pack(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"])
+    slots = tas.gdn_checkpoint_slots(tree, C)
+    st = gen_gdn_states(cfg.seed, slots, H, D)[None]                            # [1, slots, H, D, D]
+    got = _run(s, lay, H, D, K, C, st, inp)
+    q, k, v = _features(lay, inp)
+    al, be = inp["alpha"].astype(np.float64), inp["beta"].astype(np.float64)
+    pick = np.random.default_rng(0).choice(lay["n_branches"], size=8, replace=False).tolist()
+    pick += [int(np.argmax(lay["branch_anchor"])), int(np.argmin(lay["branch_anchor"]))]
+    want = gdn_replay_ref(lay, q, k, v, al, be, np.swapaxes(st, -1, -2).astype(np.float64), C,
+                          branches=pick)
+    for b in pick:
+        r0, W = int(lay["branch_off"][b]), int(lay["branch_len"][b])
+        rows = slice(r0, r0 + W - 1)
+        scale = np.abs(want[rows]).max()
+        err = np.abs(got[rows] - want[rows]).max()
+        assert err <= GDN_RTOL * scale, (b, err, scale)
+    say("  sampled %d branches ok" % len(pick))
+    torch.cuda.synchronize()

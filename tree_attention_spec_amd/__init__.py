@@ -20,7 +20,8 @@ from ._lib import (LAYOUT_ARRAYS, SPEC_BF16, SPEC_F32, SPEC_MAX_BRANCH_LEN, Spec
                    spec_tree_layout)
 
 __all__ = ["spec_tree_pack", "spec_tree_pack_query", "spec_tree_attn_fwd", "spec_e2etv_fwd_bwd",
-           "PackedTree", "SpecError", "library", "KernelTimer"]
+           "spec_gdn_replay_fwd", "gdn_checkpoint_slots", "PackedTree", "SpecError", "library",
+           "KernelTimer"]
 
 _LIB = None
 
@@ -67,6 +68,7 @@ class PackedTree:
     max_branch_len = property(lambda s: s.layout.max_branch_len)
     max_pos = property(lambda s: s.layout.max_pos)
     n_attn_items = property(lambda s: s.layout.n_attn_items)
+    max_trunk_len = property(lambda s: s.layout.max_trunk_len)
     device = property(lambda s: s.mem.device)
 
     def arrays(self) -> dict:
@@ -207,6 +209,49 @@ def spec_e2etv_fwd_bwd(tree: PackedTree, draft: torch.Tensor, teacher: torch.Ten
                                            ptr(grad_out), ptr(work), ctypes.byref(nbytes),
                                            ctypes.c_void_p(_stream(dev))))
     return alpha_out, loss_out, grad_out
+
+
+def gdn_checkpoint_slots(tree: PackedTree, chunk: int) -> int:
+    """Checkpoint slots per tree that spec_gdn_replay_fwd indexes: max_trunk_len // chunk + 1."""
+    return tree.max_trunk_len // chunk + 1
+
+
+def spec_gdn_replay_fwd(tree: PackedTree, xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor,
+                        taps: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+                        ckpt: torch.Tensor, chunk: int = 64, out: torch.Tensor = None):
+    """Indexed GDN state replay for the branch rows.
+
+    xq/xk/xv [N,H,D] bf16, taps [3,H,D,K] fp32, alpha/beta [N,H] fp32, ckpt
+    [n_trees, slots, H, D, D] fp32 (key-major states, slots = gdn_checkpoint_slots).
+    Returns out [N,H,D] fp32 with the branch rows written (trunk rows as passed in,
+    zero for a new tensor).
+    """
+    N, H, D = xq.shape
+    if xk.shape != (N, H, D) or xv.shape != (N, H, D) or N != tree.n_rows:
+        raise ValueError("xq/xk/xv must be [n_rows, H, D]")
+    if not (xq.dtype == xk.dtype == xv.dtype == torch.bfloat16):
+        raise TypeError("xq, xk and xv must be bfloat16")
+    K = taps.shape[-1]
+    if taps.shape != (3, H, D, K) or taps.dtype != torch.float32:
+        raise ValueError("taps must be float32 [3, H, D, K]")
+    if alpha.shape != (N, H) or beta.shape != (N, H) or alpha.dtype != torch.float32 \
+            or beta.dtype != torch.float32:
+        raise ValueError("alpha and beta must be float32 [n_rows, H]")
+    slots = gdn_checkpoint_slots(tree, chunk)
+    if ckpt.shape != (tree.n_trees, slots, H, D, D) or ckpt.dtype != torch.float32:
+        raise ValueError("ckpt must be float32 [n_trees, %d, H, D, D]" % slots)
+    for t in (xq, xk, xv, taps, alpha, beta, ckpt):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    if out is None:
+        out = torch.zeros((N, H, D), dtype=torch.float32, device=xq.device)
+    lib = library()
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = lib.spec_gdn_replay_fwd(ctypes.byref(tree.layout), H, D, K, chunk, ptr(xq), ptr(xk), ptr(xv),
+                                 ptr(taps), ptr(alpha), ptr(beta), ptr(ckpt), ptr(out),
+                                 ctypes.c_void_p(_stream(xq.device)))
+    _lib.check(lib, st)
+    return out
 
 
 class KernelTimer:

@@ -1,0 +1,306 @@
+// Indexed GDN state replay for the branch rows of a packed proposal tree.
+//
+// [SpecOPD paper page, Figure 5]: a shared trunk pass keeps an FP32 GDN state
+// at every `chunk`-token boundary. For a branch, a block copies the state of
+// the checkpoint at or below the anchor into registers, advances it with the
+// trunk tokens after that checkpoint through the anchor, then takes the
+// branch's own tokens, updating the state and reading it with each token's
+// query. Checkpoints are only read; the short causal convolution follows the
+// branch's ancestry. [SpecOPD paper page, Figure 13]: GDN work includes that
+// replay.
+//
+// Recurrence (gated delta rule, per head; state S is D x D with value rows i
+// and key columns j):
+//   u_i  = sum_j S_ij k_j
+//   S_ij = alpha S_ij + beta (v_i - alpha u_i) k_j
+//   o_i  = sum_j S_ij q_j
+// Row i of S moves with its own v_i and the token's shared k, q, alpha and
+// beta only. So one lane owns one row, in registers, and the update needs no
+// cross-lane traffic: a workgroup is one wavefront holding 64 rows (D / 64
+// workgroups per branch and head). The same wave builds each token's
+// features: for the q and k channels lane and lane + 64 and for its own v row,
+// a convolution over the token and its K-1 nearest ancestors, SiLU, then the
+// L2 norms of q and k as wave sums; q~ and k~ reach every lane through LDS as
+// uniform (broadcast) reads. Along a branch's path the ancestors of a position
+// are simply the positions before it: trunk token p for p <= a, then the
+// branch's rows in depth order.
+//
+// The work is fp32 VALU (three D-long row operations per token per lane);
+// the only sizable memory traffic is the checkpoint (D * D * 4 bytes per
+// branch and head), read once with each load instruction covering 64
+// consecutive value rows of one key column (key-major storage).
+#include "common.h"
+
+namespace spec {
+
+namespace {
+
+template <int CTRL>
+__device__ inline float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Sum over the wave, the same bits in every lane: within rows of 16 by DPP,
+// then across rows and halves by permlane swaps.
+__device__ inline float wave_sum(float x) {
+  x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f<0x141>(x);  // row_half_mirror
+  x += dpp_f<0x140>(x);  // row_mirror
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ inline float silu_f(float x) { return x / (1.f + __expf(-x)); }
+
+// 8 consecutive floats of an LDS array, read with two 128-bit loads (the same
+// address in every lane: a broadcast)
+struct Chunk {
+  float v[8];
+};
+__device__ inline Chunk load_chunk(const float *lds, int at) {
+  const float4 x = *reinterpret_cast<const float4 *>(lds + at);
+  const float4 y = *reinterpret_cast<const float4 *>(lds + at + 4);
+  return Chunk{{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w}};
+}
+
+template <int D, int K>
+__global__ __launch_bounds__(64) void gdn_replay_kernel(
+    const int32_t *__restrict__ tree_off, const int32_t *__restrict__ branch_tree,
+    const int32_t *__restrict__ branch_anchor, const int32_t *__restrict__ branch_len,
+    const int32_t *__restrict__ branch_off, const __bf16 *__restrict__ xq,
+    const __bf16 *__restrict__ xk, const __bf16 *__restrict__ xv, const float *__restrict__ taps,
+    const float *__restrict__ alpha, const float *__restrict__ beta, const float *__restrict__ ckpt,
+    float *__restrict__ out, int H, int chunk, int n_ckpt) {
+  constexpr int RB = D / 64;  // row blocks (workgroups) per branch and head
+  constexpr int CPL = D / 64; // q and k channels per lane
+  __shared__ __attribute__((aligned(16))) float kq[2 * D]; // k~ of the current token, then q~
+
+  const int lane = threadIdx.x;
+  const int rb = blockIdx.x % RB;
+  const int h = (blockIdx.x / RB) % H;
+  const int b = blockIdx.x / (RB * H);
+  const int W = branch_len[b];
+  if (W < 2) return;  // the branch has no rows (workgroup-uniform, before any barrier)
+  const int t = branch_tree[b], a = branch_anchor[b];
+  const int off = tree_off[t], r0 = branch_off[b];
+  const int c = (a + 1) / chunk;
+  const int p_end = a + W;  // path positions c*chunk .. a + W - 1
+  const int i = rb * 64 + lane;
+  auto row_of = [&](int p) { return p <= a ? off + p : r0 + (p - a - 1); };
+
+  // this lane's state row from checkpoint c (key-major: column j of row i at j*D + i)
+  float S[D];
+  {
+    const float *cp = ckpt + (((int64_t)t * n_ckpt + c) * H + h) * (int64_t)D * D + i;
+#pragma unroll
+    for (int j = 0; j < D; ++j) S[j] = cp[(int64_t)j * D];
+  }
+  // convolution taps: q and k channels lane + 64 m, v channel i
+  float tq[CPL][K], tk[CPL][K], tv[K];
+#pragma unroll
+  for (int m = 0; m < CPL; ++m)
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      tq[m][j] = taps[(((int64_t)0 * H + h) * D + lane + 64 * m) * K + j];
+      tk[m][j] = taps[(((int64_t)1 * H + h) * D + lane + 64 * m) * K + j];
+    }
+#pragma unroll
+  for (int j = 0; j < K; ++j) tv[j] = taps[(((int64_t)2 * H + h) * D + i) * K + j];
+  const float qscale = 1.f / sqrtf((float)D);
+
+  // Raw (pre-convolution) inputs of path positions p, p-1, .., p-K+1 (slot 0 =
+  // p), zero before position 0; each step loads only the next position, one
+  // step ahead, together with its gates.
+  struct Raw {
+    float q[CPL], k[CPL], v;
+  };
+  auto load_raw = [&](int pp) {
+    Raw x;
+#pragma unroll
+    for (int m = 0; m < CPL; ++m) x.q[m] = x.k[m] = 0.f;
+    x.v = 0.f;
+    if (pp >= 0 && pp < p_end) {  // wave-uniform
+      const int64_t base = ((int64_t)row_of(pp) * H + h) * D;
+#pragma unroll
+      for (int m = 0; m < CPL; ++m) {
+        x.q[m] = (float)xq[base + lane + 64 * m];
+        x.k[m] = (float)xk[base + lane + 64 * m];
+      }
+      x.v = (float)xv[base + i];
+    }
+    return x;
+  };
+  const int p0 = c * chunk;
+  Raw win[K];  // as of the step before p0 (slot j = position p0 - 1 - j); each step shifts it
+#pragma unroll
+  for (int j = 0; j + 1 < K; ++j) win[j] = load_raw(p0 - 1 - j);
+  Raw nxt = load_raw(p0);
+  float n_al = alpha[(int64_t)row_of(p0) * H + h], n_be = beta[(int64_t)row_of(p0) * H + h];
+
+  for (int p = p0; p < p_end; ++p) {
+    const int r = row_of(p);
+#pragma unroll
+    for (int j = K - 1; j > 0; --j) win[j] = win[j - 1];
+    win[0] = nxt;
+    const float al = n_al, be = n_be;
+    if (p + 1 < p_end) {  // the next position's inputs and gates, in flight during this step
+      nxt = load_raw(p + 1);
+      const int64_t g = (int64_t)row_of(p + 1) * H + h;
+      n_al = alpha[g];
+      n_be = beta[g];
+    }
+    // features: the convolution over the window, SiLU, norms
+    float aq[CPL], ak[CPL], av = 0.f;
+#pragma unroll
+    for (int m = 0; m < CPL; ++m) aq[m] = ak[m] = 0.f;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+#pragma unroll
+      for (int m = 0; m < CPL; ++m) {
+        aq[m] = fmaf(tq[m][j], win[j].q[m], aq[m]);
+        ak[m] = fmaf(tk[m][j], win[j].k[m], ak[m]);
+      }
+      av = fmaf(tv[j], win[j].v, av);
+    }
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int m = 0; m < CPL; ++m) {
+      aq[m] = silu_f(aq[m]);
+      ak[m] = silu_f(ak[m]);
+      sq = fmaf(aq[m], aq[m], sq);
+      sk = fmaf(ak[m], ak[m], sk);
+    }
+    av = silu_f(av);
+    const float nq = qscale / sqrtf(wave_sum(sq)), nk = 1.f / sqrtf(wave_sum(sk));
+    __syncthreads();  // every lane is done reading the previous token's q~, k~
+#pragma unroll
+    for (int m = 0; m < CPL; ++m) {
+      kq[lane + 64 * m] = ak[m] * nk;
+      kq[D + lane + 64 * m] = aq[m] * nq;
+    }
+    __syncthreads();
+    // The three row passes read k~ (and q~) as uniform LDS broadcasts in chunks
+    // of 8 keys, the next chunk's reads in flight beside this chunk's FMAs; the
+    // scheduling barriers keep the compiler from hoisting all 2D reads into
+    // registers at once.
+    float u = 0.f;
+    {
+      Chunk cur = load_chunk(kq, 0), nxt;
+#pragma unroll
+      for (int j0 = 0; j0 < D; j0 += 8) {
+        if (j0 + 8 < D) nxt = load_chunk(kq, j0 + 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) u = fmaf(S[j0 + e], cur.v[e], u);
+        __builtin_amdgcn_sched_barrier(0);
+        cur = nxt;
+      }
+    }
+    const float w = be * (av - al * u);
+    if (p > a) {  // a branch token: update and read out
+      float o = 0.f;
+      Chunk ck = load_chunk(kq, 0), cq = load_chunk(kq, D), nk, nq;
+#pragma unroll
+      for (int j0 = 0; j0 < D; j0 += 8) {
+        if (j0 + 8 < D) {
+          nk = load_chunk(kq, j0 + 8);
+          nq = load_chunk(kq, D + j0 + 8);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          S[j0 + e] = fmaf(w, ck.v[e], al * S[j0 + e]);
+          o = fmaf(S[j0 + e], cq.v[e], o);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        ck = nk;
+        cq = nq;
+      }
+      out[((int64_t)r * H + h) * D + i] = o;
+    } else {  // a replayed trunk token: update only
+      Chunk cur = load_chunk(kq, 0), nxt;
+#pragma unroll
+      for (int j0 = 0; j0 < D; j0 += 8) {
+        if (j0 + 8 < D) nxt = load_chunk(kq, j0 + 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) S[j0 + e] = fmaf(w, cur.v[e], al * S[j0 + e]);
+        __builtin_amdgcn_sched_barrier(0);
+        cur = nxt;
+      }
+    }
+  }
+}
+
+template <int D, int K>
+hipError_t launch_gdn(const spec_tree_layout &L, int H, int chunk, int n_ckpt, const void *xq,
+                      const void *xk, const void *xv, const float *taps, const float *alpha,
+                      const float *beta, const float *ckpt, float *out, hipStream_t s) {
+  const int64_t blocks = (int64_t)L.n_branches * H * (D / 64);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((gdn_replay_kernel<D, K>), dim3((unsigned)blocks), dim3(64), 0, s, L.tree_off,
+                     L.branch_tree, L.branch_anchor, L.branch_len, L.branch_off,
+                     static_cast<const __bf16 *>(xq), static_cast<const __bf16 *>(xk),
+                     static_cast<const __bf16 *>(xv), taps, alpha, beta, ckpt, out, H, chunk, n_ckpt);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_gdn_d(int K, const spec_tree_layout &L, int H, int chunk, int n_ckpt,
+                        const void *xq, const void *xk, const void *xv, const float *taps,
+                        const float *alpha, const float *beta, const float *ckpt, float *out,
+                        hipStream_t s) {
+  switch (K) {
+    case 1: return launch_gdn<D, 1>(L, H, chunk, n_ckpt, xq, xk, xv, taps, alpha, beta, ckpt, out, s);
+    case 2: return launch_gdn<D, 2>(L, H, chunk, n_ckpt, xq, xk, xv, taps, alpha, beta, ckpt, out, s);
+    case 3: return launch_gdn<D, 3>(L, H, chunk, n_ckpt, xq, xk, xv, taps, alpha, beta, ckpt, out, s);
+    case 4: return launch_gdn<D, 4>(L, H, chunk, n_ckpt, xq, xk, xv, taps, alpha, beta, ckpt, out, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+}  // namespace spec
+
+using namespace spec;
+
+extern "C" spec_status spec_gdn_replay_fwd(const spec_tree_layout *layout, int32_t n_heads,
+                                           int32_t head_dim, int32_t conv_width, int32_t chunk,
+                                           const void *d_xq, const void *d_xk, const void *d_xv,
+                                           const float *d_taps, const float *d_alpha,
+                                           const float *d_beta, const float *d_ckpt, float *d_out,
+                                           spec_stream stream) {
+  clear_error();
+  if (!layout) return fail(SPEC_ERR_INVALID_ARG, "layout must be non-NULL");
+  const spec_tree_layout &L = *layout;
+  if (L.n_trees < 1 || L.n_rows < 1 || L.n_branches < 0 || L.max_trunk_len < 1)
+    return fail(SPEC_ERR_INVALID_ARG, "layout scalars are not those of a packed tree");
+  if (L.n_branches > 0 && (!L.tree_off || !L.branch_tree || !L.branch_anchor || !L.branch_len ||
+                           !L.branch_off))
+    return fail(SPEC_ERR_INVALID_ARG, "layout device arrays are missing (pack with a buffer first)");
+  if (n_heads < 1) return fail(SPEC_ERR_INVALID_ARG, "n_heads must be >= 1 (got %d)", n_heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SPEC_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", head_dim);
+  if (conv_width < 1 || conv_width > 4)
+    return fail(SPEC_ERR_UNSUPPORTED, "conv_width %d not in 1..4", conv_width);
+  if (chunk < 1) return fail(SPEC_ERR_INVALID_ARG, "chunk must be >= 1 (got %d)", chunk);
+  if ((int64_t)L.n_branches * n_heads * (head_dim / 64) > INT32_MAX)
+    return fail(SPEC_ERR_UNSUPPORTED, "too many branches x heads");
+  if (!d_xq || !d_xk || !d_xv || !d_taps || !d_alpha || !d_beta || !d_ckpt || !d_out)
+    return fail(SPEC_ERR_INVALID_ARG, "device buffers must be non-NULL");
+  if (!aligned16(d_xq) || !aligned16(d_xk) || !aligned16(d_xv) || !aligned16(d_taps) ||
+      !aligned16(d_alpha) || !aligned16(d_beta) || !aligned16(d_ckpt) || !aligned16(d_out))
+    return fail(SPEC_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  const int n_ckpt = L.max_trunk_len / chunk + 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  prof_mark(s, "gdn:begin");
+  const hipError_t e =
+      head_dim == 64
+          ? launch_gdn_d<64>(conv_width, L, n_heads, chunk, n_ckpt, d_xq, d_xk, d_xv, d_taps,
+                             d_alpha, d_beta, d_ckpt, d_out, s)
+          : launch_gdn_d<128>(conv_width, L, n_heads, chunk, n_ckpt, d_xq, d_xk, d_xv, d_taps,
+                              d_alpha, d_beta, d_ckpt, d_out, s);
+  if (e != hipSuccess) return hip_fail(e, "gdn_replay_kernel launch");
+  prof_mark(s, "gdn_replay");
+  return SPEC_OK;
+}

@@ -298,6 +298,7 @@ extern "C" spec_status spec_tree_pack(int32_t n_trees, const int32_t *h_trunk_le
   L.n_rows = p.N;
   L.n_steps = p.R;
   L.n_attn_items = (int32_t)p.items.size();
+  L.max_trunk_len = p.max_trunk;
   if (!d_mem) {  // size query: scalars only, no HIP call
     *mem_bytes = c.total;
     *layout = L;
