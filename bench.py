@@ -83,20 +83,28 @@ MARK_KERNELS = {
     "e2etv_stats": (["e2etv_team_clear", "e2etv_stats_team_kernel", "e2etv_stats_kernel"], ("e2etv.hip",)),
     "e2etv_scan": (["e2etv_scan_kernel"], ("e2etv.hip",)),
     "e2etv_grad": (["e2etv_grad_kernel"], ("e2etv.hip",)),
+    "gdn_replay": (["gdn_replay_kernel"], ("gdn.hip",)),
 }
 
 
 def write_traffic(fetch_db, write_db, copy_fetch_db, copy_write_db, workload):
-    """profiles/traffic.json from FETCH_SIZE / WRITE_SIZE runs, scaled by a 1 GiB copy."""
+    """profiles/traffic.json from FETCH_SIZE / WRITE_SIZE runs, scaled by a 1 GiB copy.
+
+    Entries for kernels the runs did not launch are kept as they were."""
     pm = summarize_pmc([fetch_db, write_db])
     cp = summarize_pmc([copy_fetch_db, copy_write_db])
     copy = next(v for k, v in cp.items() if "copyBuffer" in k)
     n = 1 << 30
     fs = n / (copy["FETCH_SIZE"]["mean"] * 1024.0)
     ws = n / (copy["WRITE_SIZE"]["mean"] * 1024.0)
-    out = {"_calibration": {"copy_bytes": n, "fetch_kib": copy["FETCH_SIZE"]["mean"],
+    try:
+        with open(TRAFFIC_FILE) as f:
+            out = json.load(f)
+    except (OSError, ValueError):
+        out = {}
+    out["_calibration"] = {"copy_bytes": n, "fetch_kib": copy["FETCH_SIZE"]["mean"],
                             "write_kib": copy["WRITE_SIZE"]["mean"], "fetch_scale": fs, "write_scale": ws,
-                            "note": "1 GiB device copy (bench.py --copy-calibration)"}}
+                            "note": "1 GiB device copy (bench.py --copy-calibration)"}
     for mark, (subs, src) in MARK_KERNELS.items():
         ks = [v for k, v in pm.items() if any(sub in k for sub in subs)]
         if not ks:
@@ -251,6 +259,92 @@ def cpu_baseline(cfg, s, q, k, v, z_rows_fn, N, R, n_attn=24, n_e2e=6):
     }
 
 
+GDN_CONV_WIDTH, GDN_CHUNK = 4, 64
+
+
+def gdn_work(s, C):
+    """Replayed trunk tokens and branch tokens over all branches (one head)."""
+    import numpy as np
+    a = np.asarray(s["anchors"], np.int64)
+    w = np.asarray(s["branch_len"], np.int64)
+    replay = a - ((a + 1) // C) * C + 1
+    return int(replay.sum()), int(np.maximum(w - 1, 0).sum())
+
+
+def gdn_bench(args, cfg, s, dev):
+    """Indexed GDN state replay on the workload's tree: cfg.hq heads of cfg.head_dim, a
+    width-4 convolution, checkpoints every 64 trunk tokens (stand-in states)."""
+    import numpy as np
+    import torch
+    import tree_attention_spec_amd as tas
+    from specgen import gen_gdn, gen_gdn_states
+
+    H, D, K, C = cfg.hq, cfg.head_dim, GDN_CONV_WIDTH, GDN_CHUNK
+    tree = tas.spec_tree_pack(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"])
+    N = tree.n_rows
+    log("GDN replay: N=%d rows, %d branches, H=%d, D=%d, K=%d, C=%d; generating inputs"
+        % (N, tree.n_branches, H, D, K, C))
+    inp = gen_gdn(cfg.seed, N, H, D, K)
+    slots = tas.gdn_checkpoint_slots(tree, C)
+    st = gen_gdn_states(cfg.seed, tree.n_trees * slots, H, D).reshape(tree.n_trees, slots, H, D, D)
+    t = {}
+    for name in ("xq", "xk", "xv"):
+        t[name] = torch.from_numpy(inp[name].view(np.int16)).to(dev).view(torch.bfloat16)
+    for name in ("taps", "alpha", "beta"):
+        t[name] = torch.from_numpy(inp[name]).to(dev)
+    ckpt = torch.from_numpy(st).to(dev)
+    del st
+    out = torch.zeros((N, H, D), dtype=torch.float32, device=dev)
+
+    def call():
+        tas.spec_gdn_replay_fwd(tree, t["xq"], t["xk"], t["xv"], t["taps"], t["alpha"], t["beta"],
+                                ckpt, chunk=C, out=out)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    timers = [tas.KernelTimer(capacity=4) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        with timers[i]:
+            call()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = [d for tm in timers for n, d in tm.durations() if n == "gdn_replay"]
+    t_k = sum(ms) / len(ms)
+    n_replay, n_branch = gdn_work(s, C)
+    # per token and head: u = S k (D^2 FMA), S <- alpha S + w k^T (D^2 mul + D^2 FMA), and for a
+    # branch token o = S q (D^2 FMA); an FMA counts two flops
+    flop = float(H) * D * D * (5 * n_replay + 7 * n_branch)
+    achieved = flop / (t_k * 1e-3) / 1e12
+    ckpt_bytes = float(tree.n_branches) * H * D * D * 4
+    log("gdn_replay %.4f ms (%.1f TFLOP/s), %d replayed + %d branch tokens per head"
+        % (t_k, achieved, n_replay, n_branch))
+    return {
+        "metric": "GDN replay branch rows/s (indexed state replay, all heads)",
+        "value": n_branch / (ms_per_step * 1e-3),
+        "unit": "branch rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded inputs; stand-in checkpoint states)",
+        "config": {"workload": cfg.name + " tree, GDN replay", "n_rows": N, "branches": tree.n_branches,
+                   "heads": H, "head_dim": D, "conv_width": K, "chunk": C,
+                   "replayed_tokens": n_replay, "branch_tokens": n_branch, "parallelism": "single GPU"},
+        "roofline": {"kernel": "gdn_replay", "bound": "alu", "achieved": achieved,
+                     "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_F32_TFLOPS,
+                     "algorithmic_flop_per_launch": flop, "checkpoint_bytes_per_launch": ckpt_bytes,
+                     "traffic": measured_traffic("gdn_replay", source_hash(*MARK_KERNELS["gdn_replay"][1]),
+                                                 args.config)},
+        "kernel_ms": {"gdn_replay": t_k},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -261,6 +355,9 @@ def main():
     ap.add_argument("--ablation", action="store_true",
                     help="also time every branch scored as its own causal sequence (uncached independent "
                          "scoring) with the same kernels, and report the ratio to the shared-prefix layout")
+    ap.add_argument("--gdn", action="store_true",
+                    help="time the indexed GDN state replay (spec_gdn_replay_fwd) on the workload's tree "
+                         "instead of the attention + E2E-TV step, and print its own JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM counters) and exit")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DB",
@@ -302,6 +399,9 @@ def main():
     torch.cuda.set_device(dev)
     log("config %s: %s" % (cfg.name, cfg.description))
     s = gen_structure(cfg)
+    if args.gdn:
+        print(json.dumps(gdn_bench(args, cfg, s, dev)), flush=True)
+        return
     layout, mem_bytes = tas.spec_tree_pack_query(s["trunk_len"], s["n_branches"], s["anchors"],
                                                  s["branch_len"])
     N, R = layout.n_rows, layout.n_steps

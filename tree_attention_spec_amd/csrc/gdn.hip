@@ -52,7 +52,8 @@ __device__ inline float wave_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ inline float silu_f(float x) { return x / (1.f + __expf(-x)); }
+// x * sigmoid(x) with the hardware exponential and reciprocal (about 1 ulp each)
+__device__ inline float silu_f(float x) { return x * __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
 // 8 consecutive floats of an LDS array, read with two 128-bit loads (the same
 // address in every lane: a broadcast)
@@ -65,6 +66,17 @@ __device__ inline Chunk load_chunk(const float *lds, int at) {
   return Chunk{{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w}};
 }
 
+// Lanes per state row: a row of D <= 64 columns sits in one lane; a row of 128
+// in two (lanes l and l + 32, 64 columns each), which keeps a lane's share of
+// the state, with the rest of the step, within the 256 architectural VGPRs.
+template <int D>
+struct GdnShape {
+  static constexpr int CW = D > 64 ? 64 : D;  // columns per lane
+  static constexpr int LPR = D / CW;          // lanes per row
+  static constexpr int RPW = 64 / LPR;        // rows per wave (= per workgroup)
+  static constexpr int RB = D / RPW;          // workgroups per branch and head
+};
+
 template <int D, int K>
 __global__ __launch_bounds__(64) void gdn_replay_kernel(
     const int32_t *__restrict__ tree_off, const int32_t *__restrict__ branch_tree,
@@ -73,9 +85,10 @@ __global__ __launch_bounds__(64) void gdn_replay_kernel(
     const __bf16 *__restrict__ xk, const __bf16 *__restrict__ xv, const float *__restrict__ taps,
     const float *__restrict__ alpha, const float *__restrict__ beta, const float *__restrict__ ckpt,
     float *__restrict__ out, int H, int chunk, int n_ckpt) {
-  constexpr int RB = D / 64;  // row blocks (workgroups) per branch and head
-  constexpr int CPL = D / 64; // q and k channels per lane
-  __shared__ __attribute__((aligned(16))) float kq[2 * D]; // k~ of the current token, then q~
+  using G = GdnShape<D>;
+  constexpr int CW = G::CW, LPR = G::LPR, RPW = G::RPW, RB = G::RB;
+  constexpr int CPL = D / 64;  // q and k channels per lane (lane + 64 m)
+  __shared__ __attribute__((aligned(16))) float kq[2 * D];  // k~ of the current token, then q~
 
   const int lane = threadIdx.x;
   const int rb = blockIdx.x % RB;
@@ -87,15 +100,22 @@ __global__ __launch_bounds__(64) void gdn_replay_kernel(
   const int off = tree_off[t], r0 = branch_off[b];
   const int c = (a + 1) / chunk;
   const int p_end = a + W;  // path positions c*chunk .. a + W - 1
-  const int i = rb * 64 + lane;
+  const int i = rb * RPW + lane % RPW;  // this lane's state row
+  const int cb = (lane / RPW) * CW;     // and its first column
   auto row_of = [&](int p) { return p <= a ? off + p : r0 + (p - a - 1); };
+  // sum over the lanes of a row
+  auto row_sum = [](float x) {
+    if (LPR == 1) return x;
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  };
 
-  // this lane's state row from checkpoint c (key-major: column j of row i at j*D + i)
-  float S[D];
+  // this lane's columns of row i from checkpoint c (key-major: column j of row i at j*D + i)
+  float S[CW];
   {
-    const float *cp = ckpt + (((int64_t)t * n_ckpt + c) * H + h) * (int64_t)D * D + i;
+    const float *cp = ckpt + (((int64_t)t * n_ckpt + c) * H + h) * (int64_t)D * D + (int64_t)cb * D + i;
 #pragma unroll
-    for (int j = 0; j < D; ++j) S[j] = cp[(int64_t)j * D];
+    for (int j = 0; j < CW; ++j) S[j] = cp[(int64_t)j * D];
   }
   // convolution taps: q and k channels lane + 64 m, v channel i
   float tq[CPL][K], tk[CPL][K], tv[K];
@@ -173,7 +193,7 @@ __global__ __launch_bounds__(64) void gdn_replay_kernel(
       sk = fmaf(ak[m], ak[m], sk);
     }
     av = silu_f(av);
-    const float nq = qscale / sqrtf(wave_sum(sq)), nk = 1.f / sqrtf(wave_sum(sk));
+    const float nq = qscale * __builtin_amdgcn_rsqf(wave_sum(sq)), nk = __builtin_amdgcn_rsqf(wave_sum(sk));
     __syncthreads();  // every lane is done reading the previous token's q~, k~
 #pragma unroll
     for (int m = 0; m < CPL; ++m) {
@@ -181,51 +201,67 @@ __global__ __launch_bounds__(64) void gdn_replay_kernel(
       kq[D + lane + 64 * m] = aq[m] * nq;
     }
     __syncthreads();
-    // The three row passes read k~ (and q~) as uniform LDS broadcasts in chunks
-    // of 8 keys, the next chunk's reads in flight beside this chunk's FMAs; the
-    // scheduling barriers keep the compiler from hoisting all 2D reads into
-    // registers at once.
-    float u = 0.f;
+    // The row passes read this lane's columns of k~ (and q~) as LDS broadcasts
+    // (one address per row half) in chunks of 8, PD chunks ahead of the FMAs
+    // that use them; the scheduling barriers keep the compiler from hoisting
+    // every read into registers at once. Row sums keep 8 partial sums, so their
+    // FMAs do not wait on one another, then add the row's other lane.
+    constexpr int NC = CW / 8, PD = 4, PD2 = 2;  // chunks in flight: one stream, two streams
+    float up[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) up[e] = 0.f;
     {
-      Chunk cur = load_chunk(kq, 0), nxt;
+      Chunk ring[PD];
 #pragma unroll
-      for (int j0 = 0; j0 < D; j0 += 8) {
-        if (j0 + 8 < D) nxt = load_chunk(kq, j0 + 8);
+      for (int c0 = 0; c0 < PD; ++c0) ring[c0] = load_chunk(kq, cb + 8 * c0);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) u = fmaf(S[j0 + e], cur.v[e], u);
+      for (int cc = 0; cc < NC; ++cc) {
+        const Chunk cur = ring[cc % PD];
+        if (cc + PD < NC) ring[cc % PD] = load_chunk(kq, cb + 8 * (cc + PD));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) up[e] = fmaf(S[8 * cc + e], cur.v[e], up[e]);
         __builtin_amdgcn_sched_barrier(0);
-        cur = nxt;
       }
     }
+    const float u = row_sum(((up[0] + up[1]) + (up[2] + up[3])) + ((up[4] + up[5]) + (up[6] + up[7])));
     const float w = be * (av - al * u);
     if (p > a) {  // a branch token: update and read out
-      float o = 0.f;
-      Chunk ck = load_chunk(kq, 0), cq = load_chunk(kq, D), nk, nq;
+      float op[8];
 #pragma unroll
-      for (int j0 = 0; j0 < D; j0 += 8) {
-        if (j0 + 8 < D) {
-          nk = load_chunk(kq, j0 + 8);
-          nq = load_chunk(kq, D + j0 + 8);
+      for (int e = 0; e < 8; ++e) op[e] = 0.f;
+      Chunk rk[PD2], rq[PD2];
+#pragma unroll
+      for (int c0 = 0; c0 < PD2; ++c0) {
+        rk[c0] = load_chunk(kq, cb + 8 * c0);
+        rq[c0] = load_chunk(kq, D + cb + 8 * c0);
+      }
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        const Chunk ck = rk[cc % PD2], cq = rq[cc % PD2];
+        if (cc + PD2 < NC) {
+          rk[cc % PD2] = load_chunk(kq, cb + 8 * (cc + PD2));
+          rq[cc % PD2] = load_chunk(kq, D + cb + 8 * (cc + PD2));
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          S[j0 + e] = fmaf(w, ck.v[e], al * S[j0 + e]);
-          o = fmaf(S[j0 + e], cq.v[e], o);
+          S[8 * cc + e] = fmaf(w, ck.v[e], al * S[8 * cc + e]);
+          op[e] = fmaf(S[8 * cc + e], cq.v[e], op[e]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        ck = nk;
-        cq = nq;
       }
-      out[((int64_t)r * H + h) * D + i] = o;
+      const float o = row_sum(((op[0] + op[1]) + (op[2] + op[3])) + ((op[4] + op[5]) + (op[6] + op[7])));
+      if (cb == 0) out[((int64_t)r * H + h) * D + i] = o;
     } else {  // a replayed trunk token: update only
-      Chunk cur = load_chunk(kq, 0), nxt;
+      Chunk ring[PD];
 #pragma unroll
-      for (int j0 = 0; j0 < D; j0 += 8) {
-        if (j0 + 8 < D) nxt = load_chunk(kq, j0 + 8);
+      for (int c0 = 0; c0 < PD; ++c0) ring[c0] = load_chunk(kq, cb + 8 * c0);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) S[j0 + e] = fmaf(w, cur.v[e], al * S[j0 + e]);
+      for (int cc = 0; cc < NC; ++cc) {
+        const Chunk cur = ring[cc % PD];
+        if (cc + PD < NC) ring[cc % PD] = load_chunk(kq, cb + 8 * (cc + PD));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) S[8 * cc + e] = fmaf(w, cur.v[e], al * S[8 * cc + e]);
         __builtin_amdgcn_sched_barrier(0);
-        cur = nxt;
       }
     }
   }
@@ -235,7 +271,7 @@ template <int D, int K>
 hipError_t launch_gdn(const spec_tree_layout &L, int H, int chunk, int n_ckpt, const void *xq,
                       const void *xk, const void *xv, const float *taps, const float *alpha,
                       const float *beta, const float *ckpt, float *out, hipStream_t s) {
-  const int64_t blocks = (int64_t)L.n_branches * H * (D / 64);
+  const int64_t blocks = (int64_t)L.n_branches * H * GdnShape<D>::RB;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((gdn_replay_kernel<D, K>), dim3((unsigned)blocks), dim3(64), 0, s, L.tree_off,
                      L.branch_tree, L.branch_anchor, L.branch_len, L.branch_off,
@@ -284,7 +320,7 @@ extern "C" spec_status spec_gdn_replay_fwd(const spec_tree_layout *layout, int32
   if (conv_width < 1 || conv_width > 4)
     return fail(SPEC_ERR_UNSUPPORTED, "conv_width %d not in 1..4", conv_width);
   if (chunk < 1) return fail(SPEC_ERR_INVALID_ARG, "chunk must be >= 1 (got %d)", chunk);
-  if ((int64_t)L.n_branches * n_heads * (head_dim / 64) > INT32_MAX)
+  if ((int64_t)L.n_branches * n_heads * (head_dim / 32) > INT32_MAX)
     return fail(SPEC_ERR_UNSUPPORTED, "too many branches x heads");
   if (!d_xq || !d_xk || !d_xv || !d_taps || !d_alpha || !d_beta || !d_ckpt || !d_out)
     return fail(SPEC_ERR_INVALID_ARG, "device buffers must be non-NULL");
