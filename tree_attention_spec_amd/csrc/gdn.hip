@@ -84,16 +84,22 @@ __global__ __launch_bounds__(64) void gdn_replay_kernel(
     const int32_t *__restrict__ branch_off, const __bf16 *__restrict__ xq,
     const __bf16 *__restrict__ xk, const __bf16 *__restrict__ xv, const float *__restrict__ taps,
     const float *__restrict__ alpha, const float *__restrict__ beta, const float *__restrict__ ckpt,
-    float *__restrict__ out, int H, int chunk, int n_ckpt) {
+    float *__restrict__ out, int H, int chunk, int n_ckpt, int n_pairs) {
   using G = GdnShape<D>;
   constexpr int CW = G::CW, LPR = G::LPR, RPW = G::RPW, RB = G::RB;
   constexpr int CPL = D / 64;  // q and k channels per lane (lane + 64 m)
   __shared__ __attribute__((aligned(16))) float kq[2 * D];  // k~ of the current token, then q~
 
   const int lane = threadIdx.x;
-  const int rb = blockIdx.x % RB;
-  const int h = (blockIdx.x / RB) % H;
-  const int b = blockIdx.x / (RB * H);
+  // Workgroups are dealt to the 8 XCDs round-robin; the RB row blocks of one
+  // (branch, head) pair take ids 8 apart, so they share an XCD and its L2 holds
+  // the token inputs they all read. Pairs are padded to a multiple of 8.
+  const int x8 = blockIdx.x % 8, y8 = blockIdx.x / 8;
+  const int rb = y8 % RB;
+  const int pair = x8 + 8 * (y8 / RB);
+  if (pair >= n_pairs) return;
+  const int h = pair % H;
+  const int b = pair / H;
   const int W = branch_len[b];
   if (W < 2) return;  // the branch has no rows (workgroup-uniform, before any barrier)
   const int t = branch_tree[b], a = branch_anchor[b];
@@ -271,12 +277,14 @@ template <int D, int K>
 hipError_t launch_gdn(const spec_tree_layout &L, int H, int chunk, int n_ckpt, const void *xq,
                       const void *xk, const void *xv, const float *taps, const float *alpha,
                       const float *beta, const float *ckpt, float *out, hipStream_t s) {
-  const int64_t blocks = (int64_t)L.n_branches * H * GdnShape<D>::RB;
-  if (blocks == 0) return hipSuccess;
+  const int64_t pairs = (int64_t)L.n_branches * H;
+  const int64_t blocks = (pairs + 7) / 8 * 8 * GdnShape<D>::RB;
+  if (pairs == 0) return hipSuccess;
   hipLaunchKernelGGL((gdn_replay_kernel<D, K>), dim3((unsigned)blocks), dim3(64), 0, s, L.tree_off,
                      L.branch_tree, L.branch_anchor, L.branch_len, L.branch_off,
                      static_cast<const __bf16 *>(xq), static_cast<const __bf16 *>(xk),
-                     static_cast<const __bf16 *>(xv), taps, alpha, beta, ckpt, out, H, chunk, n_ckpt);
+                     static_cast<const __bf16 *>(xv), taps, alpha, beta, ckpt, out, H, chunk, n_ckpt,
+                     (int)pairs);
   return hipGetLastError();
 }
 
@@ -320,7 +328,7 @@ extern "C" spec_status spec_gdn_replay_fwd(const spec_tree_layout *layout, int32
   if (conv_width < 1 || conv_width > 4)
     return fail(SPEC_ERR_UNSUPPORTED, "conv_width %d not in 1..4", conv_width);
   if (chunk < 1) return fail(SPEC_ERR_INVALID_ARG, "chunk must be >= 1 (got %d)", chunk);
-  if ((int64_t)L.n_branches * n_heads * (head_dim / 32) > INT32_MAX)
+  if (((int64_t)L.n_branches * n_heads + 7) / 8 * 8 * (head_dim / 32) > INT32_MAX)
     return fail(SPEC_ERR_UNSUPPORTED, "too many branches x heads");
   if (!d_xq || !d_xk || !d_xv || !d_taps || !d_alpha || !d_beta || !d_ckpt || !d_out)
     return fail(SPEC_ERR_INVALID_ARG, "device buffers must be non-NULL");
