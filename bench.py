@@ -293,7 +293,6 @@ def gdn_bench(args, cfg, s, dev):
     for name in ("taps", "alpha", "beta"):
         t[name] = torch.from_numpy(inp[name]).to(dev)
     ckpt = torch.from_numpy(st).to(dev)
-    del st
     out = torch.zeros((N, H, D), dtype=torch.float32, device=dev)
 
     def call():
@@ -342,7 +341,43 @@ def gdn_bench(args, cfg, s, dev):
                      "traffic": measured_traffic("gdn_replay", source_hash(*MARK_KERNELS["gdn_replay"][1]),
                                                  args.config)},
         "kernel_ms": {"gdn_replay": t_k},
+        **({} if args.no_cpu_baseline else
+           {"cpu_baseline": gdn_cpu_baseline(s, inp, st, C, n_branch)}),
     }
+
+
+def gdn_cpu_baseline(s, inp, st, C, n_branch_rows, per_thread=2):
+    """The GDN oracle on a bounded sample: features of every packed row (the fixed
+    part), then the replay of per_thread random branches per host thread, scaled to
+    all branches."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle import gdn_features_ref, gdn_replay_ref, pack_ref
+    from specgen import bf16_bits_to_f32
+
+    log("timing the GDN oracle on a bounded sample")
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    lay = pack_ref(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"])
+    wid = lambda a: bf16_bits_to_f32(a).astype(np.float64)
+    taps = inp["taps"].astype(np.float64)
+    t0 = time.perf_counter()
+    q, k, v = gdn_features_ref(lay, wid(inp["xq"]), wid(inp["xk"]), wid(inp["xv"]), taps[0], taps[1], taps[2])
+    t_feat = time.perf_counter() - t0
+    ck = np.swapaxes(st, -1, -2)                       # the oracle keeps states value-major
+    al, be = inp["alpha"].astype(np.float64), inp["beta"].astype(np.float64)
+    B = lay["n_branches"]
+    pick = np.random.default_rng(7).choice(B, size=min(B, per_thread * workers), replace=False)
+    with ThreadPoolExecutor(workers) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(lambda part: gdn_replay_ref(lay, q, k, v, al, be, ck, C, branches=part.tolist()),
+                    np.array_split(pick, workers)))
+        t_rep = (B / len(pick)) * (time.perf_counter() - t0)
+    total = t_feat + t_rep
+    return {"value": n_branch_rows / total, "unit": "branch rows/s", "cores": workers,
+            "kind": "oracle",
+            "sample": "features of all %d packed rows, then the replay of %d random branches of %d, "
+                      "float64 NumPy over %d threads; scaled to all branches" % (lay["n_rows"], len(pick), B, workers),
+            "seconds_full_estimate": total, "host_cpus": len(os.sched_getaffinity(0))}
 
 
 def main():
