@@ -23,6 +23,9 @@
 // line up with the keys its accumulator holds. Tiles that every query of the
 // block sees in full skip the mask; the rest compare the key against the
 // query's two visible intervals. Rows of Q are rotated in registers on load.
+// Head dims 32 and 64 stage K and V through registers (tree_attn_bf16_kernel);
+// head dim 128 copies 64-key tiles that a pre-pass laid out in the fragments'
+// LDS order straight into LDS (tree_attn_tiled_kernel, below).
 //
 // fp32 path: one wavefront per (row, head) walks the visible keys in order with
 // an exact float32 online softmax (no MFMA); it serves float32 inputs.
