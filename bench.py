@@ -9,6 +9,7 @@ is supervised rows per second; per-kernel durations come from HIP events
 recorded by the library on the stream it launches on, inside the timed steps.
 
     python bench.py [--steps K] [--warmup W] [--config gqa8b] [--no-cpu-baseline]
+    python bench.py --gdn [--config gqa8b]   # indexed GDN state replay on the tree
 
 Prints one JSON line. Only one GPU is supported (--gpus must be 1).
 """
