@@ -9,7 +9,7 @@ is supervised rows per second; per-kernel durations come from HIP events
 recorded by the library on the stream it launches on, inside the timed steps.
 
     python bench.py [--steps K] [--warmup W] [--config gqa8b] [--no-cpu-baseline]
-    python bench.py --gdn [--config gqa8b]   # indexed GDN state replay on the tree
+    python bench.py --gdn [--config gqa8b]   # GDN scoring: trunk pass + indexed replay
 
 Prints one JSON line. Only one GPU is supported (--gpus must be 1).
 """
@@ -84,6 +84,7 @@ MARK_KERNELS = {
     "e2etv_stats": (["e2etv_team_clear", "e2etv_stats_team_kernel", "e2etv_stats_kernel"], ("e2etv.hip",)),
     "e2etv_scan": (["e2etv_scan_kernel"], ("e2etv.hip",)),
     "e2etv_grad": (["e2etv_grad_kernel"], ("e2etv.hip",)),
+    "gdn_trunk": (["gdn_trunk_kernel"], ("gdn.hip",)),
     "gdn_replay": (["gdn_replay_kernel"], ("gdn.hip",)),
 }
 
@@ -273,57 +274,63 @@ def gdn_work(s, C):
 
 
 def gdn_bench(args, cfg, s, dev):
-    """Indexed GDN state replay on the workload's tree: cfg.hq heads of cfg.head_dim, a
-    width-4 convolution, checkpoints every 64 trunk tokens (stand-in states)."""
+    """GDN scoring of the workload's tree: the shared trunk pass (trunk outputs and
+    checkpoints every 64 tokens), then the indexed replay of every branch from those
+    checkpoints; cfg.hq heads of cfg.head_dim and a width-4 convolution."""
     import numpy as np
     import torch
     import tree_attention_spec_amd as tas
-    from specgen import gen_gdn, gen_gdn_states
+    from specgen import gen_gdn
 
     H, D, K, C = cfg.hq, cfg.head_dim, GDN_CONV_WIDTH, GDN_CHUNK
     tree = tas.spec_tree_pack(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"])
     N = tree.n_rows
-    log("GDN replay: N=%d rows, %d branches, H=%d, D=%d, K=%d, C=%d; generating inputs"
+    log("GDN scoring: N=%d rows, %d branches, H=%d, D=%d, K=%d, C=%d; generating inputs"
         % (N, tree.n_branches, H, D, K, C))
     inp = gen_gdn(cfg.seed, N, H, D, K)
     slots = tas.gdn_checkpoint_slots(tree, C)
-    st = gen_gdn_states(cfg.seed, tree.n_trees * slots, H, D).reshape(tree.n_trees, slots, H, D, D)
     t = {}
     for name in ("xq", "xk", "xv"):
         t[name] = torch.from_numpy(inp[name].view(np.int16)).to(dev).view(torch.bfloat16)
     for name in ("taps", "alpha", "beta"):
         t[name] = torch.from_numpy(inp[name]).to(dev)
-    ckpt = torch.from_numpy(st).to(dev)
+    x = [t[n] for n in ("xq", "xk", "xv", "taps", "alpha", "beta")]
+    ckpt = torch.zeros((tree.n_trees, slots, H, D, D), dtype=torch.float32, device=dev)
     out = torch.zeros((N, H, D), dtype=torch.float32, device=dev)
 
     def call():
-        tas.spec_gdn_replay_fwd(tree, t["xq"], t["xk"], t["xv"], t["taps"], t["alpha"], t["beta"],
-                                ckpt, chunk=C, out=out)
+        tas.spec_gdn_trunk_fwd(tree, *x, chunk=C, ckpt=ckpt, out=out)
+        tas.spec_gdn_replay_fwd(tree, *x, ckpt=ckpt, chunk=C, out=out)
 
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
-    timers = [tas.KernelTimer(capacity=4) for _ in range(args.steps)]
+    timers = [tas.KernelTimer(capacity=8) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         with timers[i]:
             call()
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    ms = [d for tm in timers for n, d in tm.durations() if n == "gdn_replay"]
-    t_k = sum(ms) / len(ms)
+    kms = {}
+    for name in ("gdn_trunk", "gdn_replay"):
+        ms = [d for tm in timers for n, d in tm.durations() if n == name]
+        kms[name] = sum(ms) / len(ms)
     n_replay, n_branch = gdn_work(s, C)
+    n_trunk = int(np.sum(s["trunk_len"]))
     # per token and head: u = S k (D^2 FMA), S <- alpha S + w k^T (D^2 mul + D^2 FMA), and for a
-    # branch token o = S q (D^2 FMA); an FMA counts two flops
-    flop = float(H) * D * D * (5 * n_replay + 7 * n_branch)
-    achieved = flop / (t_k * 1e-3) / 1e12
-    ckpt_bytes = float(tree.n_branches) * H * D * D * 4
-    log("gdn_replay %.4f ms (%.1f TFLOP/s), %d replayed + %d branch tokens per head"
-        % (t_k, achieved, n_replay, n_branch))
+    # token that is read out o = S q (D^2 FMA); an FMA counts two flops
+    flop = {"gdn_trunk": float(H) * D * D * 7 * n_trunk,
+            "gdn_replay": float(H) * D * D * (5 * n_replay + 7 * n_branch)}
+    tf = {k: flop[k] / (kms[k] * 1e-3) / 1e12 for k in kms}
+    for k in kms:
+        log("%s %.4f ms (%.1f TFLOP/s)" % (k, kms[k], tf[k]))
+    log("per head: %d trunk tokens, %d replayed + %d branch tokens" % (n_trunk, n_replay, n_branch))
+    dom = max(kms, key=kms.get)
     return {
-        "metric": "GDN replay branch rows/s (indexed state replay, all heads)",
-        "value": n_branch / (ms_per_step * 1e-3),
-        "unit": "branch rows/s",
+        "metric": "GDN tree scoring rows/s (trunk pass + indexed replay, all heads)",
+        "value": N / (ms_per_step * 1e-3),
+        "unit": "rows/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -332,28 +339,29 @@ def gdn_bench(args, cfg, s, dev):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded inputs; stand-in checkpoint states)",
-        "config": {"workload": cfg.name + " tree, GDN replay", "n_rows": N, "branches": tree.n_branches,
-                   "heads": H, "head_dim": D, "conv_width": K, "chunk": C,
+        "data": "synthetic (seeded inputs)",
+        "config": {"workload": cfg.name + " tree, GDN scoring", "n_rows": N, "branches": tree.n_branches,
+                   "heads": H, "head_dim": D, "conv_width": K, "chunk": C, "trunk_tokens": n_trunk,
                    "replayed_tokens": n_replay, "branch_tokens": n_branch, "parallelism": "single GPU"},
-        "roofline": {"kernel": "gdn_replay", "bound": "alu", "achieved": achieved,
-                     "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_F32_TFLOPS,
-                     "algorithmic_flop_per_launch": flop, "checkpoint_bytes_per_launch": ckpt_bytes,
-                     "traffic": measured_traffic("gdn_replay", source_hash(*MARK_KERNELS["gdn_replay"][1]),
-                                                 args.config)},
-        "kernel_ms": {"gdn_replay": t_k},
+        "roofline": {"kernel": dom, "bound": "alu", "achieved": tf[dom],
+                     "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s", "frac": tf[dom] / PEAK_F32_TFLOPS,
+                     "algorithmic_flop_per_launch": flop[dom],
+                     "traffic": measured_traffic(dom, source_hash(*MARK_KERNELS[dom][1]), args.config)},
+        "kernels": {k: {"ms": kms[k], "tflops": tf[k], "frac": tf[k] / PEAK_F32_TFLOPS,
+                        "traffic": measured_traffic(k, source_hash(*MARK_KERNELS[k][1]), args.config)}
+                    for k in kms},
         **({} if args.no_cpu_baseline else
-           {"cpu_baseline": gdn_cpu_baseline(s, inp, st, C, n_branch)}),
+           {"cpu_baseline": gdn_cpu_baseline(s, inp, C, N)}),
     }
 
 
-def gdn_cpu_baseline(s, inp, st, C, n_branch_rows, per_thread=2):
-    """The GDN oracle on a bounded sample: features of every packed row (the fixed
-    part), then the replay of per_thread random branches per host thread, scaled to
-    all branches."""
+def gdn_cpu_baseline(s, inp, C, n_rows, per_thread=2):
+    """The GDN oracle on a bounded sample: features of every packed row, the whole
+    trunk pass (heads split over the host threads), then the replay of per_thread
+    random branches per thread from the oracle's checkpoints, scaled to all branches."""
     import numpy as np
     from concurrent.futures import ThreadPoolExecutor
-    from oracle import gdn_features_ref, gdn_replay_ref, pack_ref
+    from oracle import gdn_features_ref, gdn_replay_ref, gdn_trunk_ref, pack_ref
     from specgen import bf16_bits_to_f32
 
     log("timing the GDN oracle on a bounded sample")
@@ -364,8 +372,15 @@ def gdn_cpu_baseline(s, inp, st, C, n_branch_rows, per_thread=2):
     t0 = time.perf_counter()
     q, k, v = gdn_features_ref(lay, wid(inp["xq"]), wid(inp["xk"]), wid(inp["xv"]), taps[0], taps[1], taps[2])
     t_feat = time.perf_counter() - t0
-    ck = np.swapaxes(st, -1, -2)                       # the oracle keeps states value-major
     al, be = inp["alpha"].astype(np.float64), inp["beta"].astype(np.float64)
+    H = q.shape[1]
+    parts = [p for p in np.array_split(np.arange(H), workers) if len(p)]
+    with ThreadPoolExecutor(workers) as ex:
+        t0 = time.perf_counter()
+        res = list(ex.map(lambda hs: gdn_trunk_ref(lay, q[:, hs], k[:, hs], v[:, hs], al[:, hs], be[:, hs], C)[0],
+                          parts))
+        t_trunk = time.perf_counter() - t0
+    ck = np.concatenate(res, axis=2)
     B = lay["n_branches"]
     pick = np.random.default_rng(7).choice(B, size=min(B, per_thread * workers), replace=False)
     with ThreadPoolExecutor(workers) as ex:
@@ -373,11 +388,12 @@ def gdn_cpu_baseline(s, inp, st, C, n_branch_rows, per_thread=2):
         list(ex.map(lambda part: gdn_replay_ref(lay, q, k, v, al, be, ck, C, branches=part.tolist()),
                     np.array_split(pick, workers)))
         t_rep = (B / len(pick)) * (time.perf_counter() - t0)
-    total = t_feat + t_rep
-    return {"value": n_branch_rows / total, "unit": "branch rows/s", "cores": workers,
+    total = t_feat + t_trunk + t_rep
+    return {"value": n_rows / total, "unit": "rows/s", "cores": workers,
             "kind": "oracle",
-            "sample": "features of all %d packed rows, then the replay of %d random branches of %d, "
-                      "float64 NumPy over %d threads; scaled to all branches" % (lay["n_rows"], len(pick), B, workers),
+            "sample": "features of all %d packed rows, the whole trunk pass, then the replay of %d random "
+                      "branches of %d, float64 NumPy over %d threads; the replay scaled to all branches"
+                      % (lay["n_rows"], len(pick), B, workers),
             "seconds_full_estimate": total, "host_cpus": len(os.sched_getaffinity(0))}
 
 
@@ -392,7 +408,7 @@ def main():
                     help="also time every branch scored as its own causal sequence (uncached independent "
                          "scoring) with the same kernels, and report the ratio to the shared-prefix layout")
     ap.add_argument("--gdn", action="store_true",
-                    help="time the indexed GDN state replay (spec_gdn_replay_fwd) on the workload's tree "
+                    help="time GDN scoring of the workload's tree (spec_gdn_trunk_fwd, then spec_gdn_replay_fwd) "
                          "instead of the attention + E2E-TV step, and print its own JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM counters) and exit")

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define SPEC_TREE_ABI_VERSION 2
+#define SPEC_TREE_ABI_VERSION 3
 #define SPEC_MAX_BRANCH_LEN 64 /* largest supported branch width W_b */
 
 typedef enum spec_status {
@@ -92,6 +92,7 @@ typedef struct spec_tree_layout {
 
   /* per tree */
   int32_t *tree_off;        /* [n_trees+1] first packed row of each tree; last = N */
+  int32_t *tree_trunk_len;  /* [n_trees] trunk length T_t */
   /* per packed row [N] */
   int32_t *row_tree;        /* tree index */
   int32_t *row_branch;      /* branch index b, -1 for trunk rows */
@@ -256,7 +257,8 @@ spec_status spec_e2etv_fwd_bwd(const spec_tree_layout *layout, int64_t vocab,
  *
  * Arguments:
  *   layout      from spec_tree_pack (uses n_trees, n_branches, max_trunk_len,
- *               tree_off, branch_tree, branch_anchor, branch_len, branch_off).
+ *               tree_off, branch_tree, branch_anchor, branch_len, branch_off;
+ *               the trunk pass also tree_trunk_len).
  *   n_heads     H >= 1; head_dim D in {64, 128}; conv_width K in 1..4;
  *               chunk >= 1 (the checkpoint spacing C).
  *   d_xq, d_xk, d_xv  [N, H, D] bf16: q, k, v projections of every packed
@@ -280,6 +282,27 @@ spec_status spec_gdn_replay_fwd(const spec_tree_layout *layout, int32_t n_heads,
                                 const void *d_xq, const void *d_xk, const void *d_xv,
                                 const float *d_taps, const float *d_alpha, const float *d_beta,
                                 const float *d_ckpt, float *d_out, spec_stream stream);
+
+/*
+ * spec_gdn_trunk_fwd -- the shared trunk pass of GDN scoring: the GDN outputs
+ * of every trunk row and the checkpoints spec_gdn_replay_fwd reads.
+ *
+ * Defines: [SpecOPD paper page, Figure 5] (a shared trunk pass keeps an FP32
+ * GDN state at every chunk-token boundary). Same recurrence, features and
+ * argument meanings as spec_gdn_replay_fwd, along each tree's trunk from the
+ * zero state: o is written for every trunk row, and slot c of d_ckpt (key-major
+ * state, layout as for spec_gdn_replay_fwd) receives the state after trunk
+ * tokens 0 .. c*chunk-1 for c = 0 .. T_t / chunk. Slots a shorter tree never
+ * reaches are left as they are. Branch rows of d_out are left as they are.
+ * The recurrence is sequential along a trunk; its work is one workgroup per
+ * (tree, head, row block).
+ * Errors: as spec_gdn_replay_fwd.
+ */
+spec_status spec_gdn_trunk_fwd(const spec_tree_layout *layout, int32_t n_heads, int32_t head_dim,
+                               int32_t conv_width, int32_t chunk, const void *d_xq,
+                               const void *d_xk, const void *d_xv, const float *d_taps,
+                               const float *d_alpha, const float *d_beta, float *d_ckpt,
+                               float *d_out, spec_stream stream);
 
 /*
  * Measurement hook (benchmarks only; it changes no result).

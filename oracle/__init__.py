@@ -42,6 +42,7 @@ from .gdn_ref import (  # noqa: F401
     conv_ancestry_ref,
     gdn_branch_brute_ref,
     gdn_checkpoints_ref,
+    gdn_trunk_ref,
     gdn_features_ref,
     gdn_replay_ref,
     gdn_step_ref,

@@ -11,6 +11,8 @@ Sources:
     it with each token's query to give the GDN outputs. Checkpoints are never
     written; the short causal convolution follows the branch's ancestry.
   * [SpecOPD paper page, Figure 13]: GDN work counts include that replay.
+    The trunk pass here also gives every trunk token's output, which is what
+    scoring the trunk needs.
   * [SpecOPD notes page, "Checks, negative controls, and limits"]: packed
     scoring must equal each branch's independent causal scoring.
 
@@ -106,23 +108,32 @@ def trunk_len_ref(layout):
     return T
 
 
-def gdn_checkpoints_ref(layout, q, k, v, alpha, beta, C):
-    """The trunk pass's checkpoints, [n_trees, max_T // C + 1, H, dv, dk].
+def gdn_trunk_ref(layout, q, k, v, alpha, beta, C):
+    """The shared trunk pass: (checkpoints, outputs).
 
-    Slot c of tree t holds S after trunk tokens 0 .. cC-1 (reading 2); slots a
-    shorter tree never reaches stay zero."""
+    Runs each tree's trunk from the zero state. Checkpoints [n_trees, max_T // C
+    + 1, H, dv, dk]: slot c of tree t holds S after trunk tokens 0 .. cC-1
+    (reading 2); slots a shorter tree never reaches stay zero. Outputs [N, H, D]:
+    o_j of every trunk row, branch rows zero."""
     T = trunk_len_ref(layout)
-    H, D = q.shape[1], q.shape[2]
+    N, H, D = q.shape
     n_ckpt = int(T.max()) // C + 1 if len(T) else 1
     ck = np.zeros((layout["n_trees"], n_ckpt, H, D, D))
+    out = np.zeros((N, H, D))
     for t in range(layout["n_trees"]):
         off = int(layout["tree_off"][t])
         S = np.zeros((H, D, D))
         for j in range(int(T[t])):
-            S, _ = gdn_step_ref(S, q[off + j], k[off + j], v[off + j], alpha[off + j], beta[off + j])
+            r = off + j
+            S, out[r] = gdn_step_ref(S, q[r], k[r], v[r], alpha[r], beta[r])
             if (j + 1) % C == 0:
                 ck[t, (j + 1) // C] = S
-    return ck
+    return ck, out
+
+
+def gdn_checkpoints_ref(layout, q, k, v, alpha, beta, C):
+    """The trunk pass's checkpoints alone (see gdn_trunk_ref)."""
+    return gdn_trunk_ref(layout, q, k, v, alpha, beta, C)[0]
 
 
 def gdn_replay_ref(layout, q, k, v, alpha, beta, ckpt, C, branches=None):

@@ -176,3 +176,27 @@ def test_gdn_argument_checks(tas):
     assert call(32, 128, 4, 64, None) == 1          # NULL buffers
     assert call(32, 128, 4, 64, ctypes.c_void_p(0x1004)) == 1
     assert "aligned" in lib.spec_last_error().decode()
+
+
+def test_gdn_trunk_argument_checks(tas):
+    """spec_gdn_trunk_fwd rejects bad arguments before any launch (no GPU is touched)."""
+    from tree_attention_spec_amd import _lib
+    lib = tas.library()
+    L = _query_layout(tas)
+    P = ctypes.c_void_p(0x1000)
+
+    def call(H, D, K, C, p=P):
+        return lib.spec_gdn_trunk_fwd(ctypes.byref(L), H, D, K, C, p, p, p, p, p, p, p, p, None)
+
+    assert call(32, 128, 4, 64) == 1                # the layout has no device arrays yet
+    fake = ctypes.cast(ctypes.c_void_p(0x1000), _lib._i32p)
+    L.tree_off = fake
+    assert call(32, 128, 4, 64) == 1                # the trunk pass needs the trunk lengths too
+    assert "device arrays" in lib.spec_last_error().decode()
+    L.tree_trunk_len = fake
+    assert call(0, 128, 4, 64) == 1
+    assert call(32, 64, 3, 0) == 1
+    assert call(32, 96, 4, 64) == 2
+    assert call(32, 128, 4, 64, None) == 1
+    assert call(32, 128, 4, 64, ctypes.c_void_p(0x1008)) == 1
+    assert "aligned" in lib.spec_last_error().decode()

@@ -1,11 +1,13 @@
 """GPU parity: spec_gdn_replay_fwd against the float64 oracle (indexed replay from
-the same float32 checkpoints), plus each branch scored as its own sequence."""
+the same float32 checkpoints), plus each branch scored as its own sequence;
+spec_gdn_trunk_fwd's outputs and checkpoints against the oracle's trunk pass, and
+the two entry points chained (trunk pass, then replay from its checkpoints)."""
 import numpy as np
 import pytest
 
 from _util import say, to_device, widen
 from oracle import (gdn_branch_brute_ref, gdn_checkpoints_ref, gdn_features_ref, gdn_replay_ref,
-                    pack_ref)
+                    gdn_trunk_ref, pack_ref)
 from specgen import CONFIGS, gen_gdn, gen_gdn_states, gen_structure
 
 pytestmark = pytest.mark.gpu
@@ -120,3 +122,86 @@ def test_gdn_workload_sampled():
         assert err <= GDN_RTOL * scale, (b, err, scale)
     say("  sampled %d branches ok" % len(pick))
     torch.cuda.synchronize()
+
+
+def _trunk_compare(s, H, D, K, C, seed, heads=None):
+    """Trunk pass then replay on the GPU; the oracle's trunk pass and replay in float64
+    (on the given subset of heads, default all)."""
+    import torch
+    import tree_attention_spec_amd as tas
+    lay = pack_ref(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"])
+    inp = gen_gdn(seed, lay["n_rows"], H, D, K)
+    tree = tas.spec_tree_pack(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"])
+    dev = lambda a: to_device(np.ascontiguousarray(a))
+    x = [dev(inp[n]) for n in ("xq", "xk", "xv", "taps", "alpha", "beta")]
+    slots = tas.gdn_checkpoint_slots(tree, C)
+    ck_g = torch.full((lay["n_trees"], slots, H, D, D), 5.0, dtype=torch.float32, device="cuda")
+    out_g = torch.full((lay["n_rows"], H, D), 7.0, dtype=torch.float32, device="cuda")
+    tas.spec_gdn_trunk_fwd(tree, *x, chunk=C, ckpt=ck_g, out=out_g)
+    trunk_out = out_g.clone()
+    tas.spec_gdn_replay_fwd(tree, *x, ckpt=ck_g, chunk=C, out=out_g)
+    torch.cuda.synchronize()
+    ck = np.swapaxes(ck_g.cpu().numpy().astype(np.float64), -1, -2)            # value-major, as the oracle
+    trunk_got = trunk_out.cpu().numpy().astype(np.float64)
+    got = out_g.cpu().numpy().astype(np.float64)
+
+    hs = list(range(H)) if heads is None else list(heads)
+    sub = lambda a: np.ascontiguousarray(a[:, hs])
+    t = inp["taps"].astype(np.float64)[:, hs]
+    q, k, v = gdn_features_ref(lay, sub(widen(inp["xq"])), sub(widen(inp["xk"])), sub(widen(inp["xv"])),
+                               t[0], t[1], t[2])
+    al, be = sub(inp["alpha"].astype(np.float64)), sub(inp["beta"].astype(np.float64))
+    ck_ref, o_ref = gdn_trunk_ref(lay, q, k, v, al, be, C)
+    tr = lay["row_branch"] < 0
+    T = np.asarray(s["trunk_len"])
+    # trunk outputs; branch rows untouched by the trunk pass
+    scale = np.abs(o_ref[tr]).max()
+    err = np.abs(trunk_got[:, hs][tr] - o_ref[tr]).max()
+    say("  trunk outputs: max abs err %.3e (max |o| %.3e)" % (err, scale))
+    assert err <= GDN_RTOL * scale
+    assert np.all(trunk_got[~tr] == 7.0)
+    # checkpoints every slot a tree reaches; the others untouched
+    for ti in range(lay["n_trees"]):
+        reach = int(T[ti]) // C + 1
+        cs = np.abs(ck_ref[ti, :reach]).max() if reach > 1 else 1.0
+        cerr = np.abs(ck[ti, :reach][:, hs] - ck_ref[ti, :reach]).max()
+        say("  tree %d: %d checkpoints, max abs err %.3e (max |S| %.3e)" % (ti, reach, cerr, cs))
+        assert cerr <= GDN_RTOL * cs
+        assert np.all(ck[ti, 0] == 0.0)
+        assert np.all(ck[ti, reach:] == 5.0)
+    # the replay from the GPU's checkpoints against the oracle's chained path
+    br = lay["row_branch"] >= 0
+    if br.any():
+        want = gdn_replay_ref(lay, q, k, v, al, be, ck_ref, C)
+        bs = np.abs(want[br]).max()
+        berr = np.abs(got[:, hs][br] - want[br]).max()
+        say("  chained replay: max abs err %.3e (max |o| %.3e)" % (berr, bs))
+        assert berr <= 2 * GDN_RTOL * bs
+    assert np.array_equal(got[tr], trunk_got[tr])                               # the replay leaves trunk rows
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_gdn_trunk_small(case):
+    tag, T, anchors, widths, H, D, K, C = case
+    say("gdn trunk pass: %s" % tag)
+    s = dict(trunk_len=np.array(T, np.int32), n_branches=np.array([len(a) for a in anchors], np.int32),
+             anchors=np.concatenate([np.array(a, np.int32) for a in anchors]),
+             branch_len=np.concatenate([np.array(w, np.int32) for w in widths]))
+    _trunk_compare(s, H, D, K, C, seed=len(tag) + 50)
+
+
+def test_gdn_trunk_edges():
+    """Trunks of one token, of exactly C and of C - 1 tokens, and a tree with no branches."""
+    say("gdn trunk pass: edge trunk lengths")
+    s = dict(trunk_len=np.array([1, 16, 15, 33], np.int32), n_branches=np.array([1, 2, 0, 1], np.int32),
+             anchors=np.array([0, 15, 3, 32], np.int32), branch_len=np.array([3, 2, 4, 5], np.int32))
+    _trunk_compare(s, 2, 64, 4, 16, seed=77)
+
+
+@pytest.mark.slow
+def test_gdn_trunk_workload_sampled_heads():
+    """The 8B-like tree with 32 heads of 128, width-4 convolution, checkpoints every 64
+    tokens: the whole trunk pass and replay on the GPU, 3 heads against the oracle."""
+    cfg = CONFIGS["gqa8b"]
+    say("gdn trunk pass + replay: 8B-like tree full size, heads 0, 17, 31")
+    _trunk_compare(gen_structure(cfg), 32, 128, 4, 64, seed=cfg.seed, heads=[0, 17, 31])

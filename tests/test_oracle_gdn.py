@@ -13,6 +13,7 @@ from oracle import (
     gdn_features_ref,
     gdn_replay_ref,
     gdn_step_ref,
+    gdn_trunk_ref,
     pack_ref,
     silu,
     trunk_len_ref,
@@ -168,3 +169,43 @@ def test_branch_isolation_and_future_trunk():
         x[others] = g.standard_normal(x[others].shape)
     moved = run(xs)
     assert np.array_equal(base[mine], moved[mine])
+
+
+def test_trunk_outputs_equal_brute_sequence():
+    """Trunk outputs against the brute-force scoring of a branch that copies the trunk:
+    a branch anchored at trunk token 0 whose rows repeat the inputs of trunk tokens
+    1 .. W-1 is the same sequence, so its outputs are the trunk's at those tokens."""
+    C, K, H, D = 4, 4, 2, 5
+    T, W = 13, 12
+    lay = pack_ref([T], [1], [0], [W])
+    N = lay["n_rows"]
+    (xq, xk, xv), (wq, wk, wv), al, be = _inputs(N, H, D, K, 21)
+    r0 = int(lay["branch_off"][0])
+    for x in (xq, xk, xv, al, be):
+        x[r0:r0 + W - 1] = x[1:W]
+    q, k, v = gdn_features_ref(lay, xq, xk, xv, wq, wk, wv)
+    ck, out = gdn_trunk_ref(lay, q, k, v, al, be, C)
+    want = gdn_branch_brute_ref(lay, xq, xk, xv, wq, wk, wv, al, be, 0)
+    assert np.abs(out[1:W] - want).max() <= 1e-12
+    assert np.all(out[r0:] == 0.0)                                # branch rows are not the trunk's
+    assert np.array_equal(ck, gdn_checkpoints_ref(lay, q, k, v, al, be, C))
+    assert np.all(ck[0, 0] == 0.0)                                # slot 0: the zero state
+
+
+@pytest.mark.parametrize("a,C", [(0, 4), (3, 4), (6, 4), (7, 8), (10, 4)])
+def test_trunk_output_equals_replayed_copy(a, C):
+    """A one-token-deeper branch at anchor a whose row copies trunk token a+1 has the
+    ancestry, features and state of that token: the replay from checkpoints must give
+    the trunk pass's output there (two routes: sequential vs checkpoint + replay)."""
+    K, H, D = 3, 2, 6
+    T = 12
+    lay = pack_ref([T], [1], [a], [2])
+    N = lay["n_rows"]
+    (xq, xk, xv), (wq, wk, wv), al, be = _inputs(N, H, D, K, 30 + a)
+    r0 = int(lay["branch_off"][0])
+    for x in (xq, xk, xv, al, be):
+        x[r0] = x[a + 1]
+    q, k, v = gdn_features_ref(lay, xq, xk, xv, wq, wk, wv)
+    ck, trunk = gdn_trunk_ref(lay, q, k, v, al, be, C)
+    rep = gdn_replay_ref(lay, q, k, v, al, be, ck, C)
+    assert np.abs(rep[r0] - trunk[a + 1]).max() <= 1e-13

@@ -20,7 +20,7 @@ from ._lib import (LAYOUT_ARRAYS, SPEC_BF16, SPEC_F32, SPEC_MAX_BRANCH_LEN, Spec
                    spec_tree_layout)
 
 __all__ = ["spec_tree_pack", "spec_tree_pack_query", "spec_tree_attn_fwd", "spec_e2etv_fwd_bwd",
-           "spec_gdn_replay_fwd", "gdn_checkpoint_slots", "PackedTree", "SpecError", "library",
+           "spec_gdn_trunk_fwd", "spec_gdn_replay_fwd", "gdn_checkpoint_slots", "PackedTree", "SpecError", "library",
            "KernelTimer"]
 
 _LIB = None
@@ -216,16 +216,7 @@ def gdn_checkpoint_slots(tree: PackedTree, chunk: int) -> int:
     return tree.max_trunk_len // chunk + 1
 
 
-def spec_gdn_replay_fwd(tree: PackedTree, xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor,
-                        taps: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
-                        ckpt: torch.Tensor, chunk: int = 64, out: torch.Tensor = None):
-    """Indexed GDN state replay for the branch rows.
-
-    xq/xk/xv [N,H,D] bf16, taps [3,H,D,K] fp32, alpha/beta [N,H] fp32, ckpt
-    [n_trees, slots, H, D, D] fp32 (key-major states, slots = gdn_checkpoint_slots).
-    Returns out [N,H,D] fp32 with the branch rows written (trunk rows as passed in,
-    zero for a new tensor).
-    """
+def _check_gdn(tree, xq, xk, xv, taps, alpha, beta, chunk):
     N, H, D = xq.shape
     if xk.shape != (N, H, D) or xv.shape != (N, H, D) or N != tree.n_rows:
         raise ValueError("xq/xk/xv must be [n_rows, H, D]")
@@ -237,12 +228,54 @@ def spec_gdn_replay_fwd(tree: PackedTree, xq: torch.Tensor, xk: torch.Tensor, xv
     if alpha.shape != (N, H) or beta.shape != (N, H) or alpha.dtype != torch.float32 \
             or beta.dtype != torch.float32:
         raise ValueError("alpha and beta must be float32 [n_rows, H]")
-    slots = gdn_checkpoint_slots(tree, chunk)
-    if ckpt.shape != (tree.n_trees, slots, H, D, D) or ckpt.dtype != torch.float32:
-        raise ValueError("ckpt must be float32 [n_trees, %d, H, D, D]" % slots)
-    for t in (xq, xk, xv, taps, alpha, beta, ckpt):
+    if chunk < 1:
+        raise ValueError("chunk must be >= 1")
+    for t in (xq, xk, xv, taps, alpha, beta):
         if not t.is_contiguous():
             raise ValueError("inputs must be contiguous")
+    return N, H, D, K, (tree.n_trees, gdn_checkpoint_slots(tree, chunk), H, D, D)
+
+
+def spec_gdn_trunk_fwd(tree: PackedTree, xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor,
+                       taps: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor, chunk: int = 64,
+                       ckpt: torch.Tensor = None, out: torch.Tensor = None):
+    """Shared GDN trunk pass: every trunk row's output and the checkpoints.
+
+    Inputs as for spec_gdn_replay_fwd. Returns (ckpt, out): ckpt [n_trees, slots,
+    H, D, D] fp32 key-major, slot c of tree t the state after its first c*chunk
+    trunk tokens (slots past floor(T_t / chunk) as passed in, zero for a new
+    tensor); out [N,H,D] fp32 with the trunk rows written (branch rows as passed
+    in, zero for a new tensor).
+    """
+    N, H, D, K, ck_shape = _check_gdn(tree, xq, xk, xv, taps, alpha, beta, chunk)
+    if ckpt is None:
+        ckpt = torch.zeros(ck_shape, dtype=torch.float32, device=xq.device)
+    elif ckpt.shape != ck_shape or ckpt.dtype != torch.float32 or not ckpt.is_contiguous():
+        raise ValueError("ckpt must be contiguous float32 %s" % (list(ck_shape),))
+    if out is None:
+        out = torch.zeros((N, H, D), dtype=torch.float32, device=xq.device)
+    lib = library()
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = lib.spec_gdn_trunk_fwd(ctypes.byref(tree.layout), H, D, K, chunk, ptr(xq), ptr(xk), ptr(xv),
+                                ptr(taps), ptr(alpha), ptr(beta), ptr(ckpt), ptr(out),
+                                ctypes.c_void_p(_stream(xq.device)))
+    _lib.check(lib, st)
+    return ckpt, out
+
+
+def spec_gdn_replay_fwd(tree: PackedTree, xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor,
+                        taps: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+                        ckpt: torch.Tensor, chunk: int = 64, out: torch.Tensor = None):
+    """Indexed GDN state replay for the branch rows.
+
+    xq/xk/xv [N,H,D] bf16, taps [3,H,D,K] fp32, alpha/beta [N,H] fp32, ckpt
+    [n_trees, slots, H, D, D] fp32 (key-major states, slots = gdn_checkpoint_slots,
+    as spec_gdn_trunk_fwd writes them). Returns out [N,H,D] fp32 with the branch
+    rows written (trunk rows as passed in, zero for a new tensor).
+    """
+    N, H, D, K, ck_shape = _check_gdn(tree, xq, xk, xv, taps, alpha, beta, chunk)
+    if ckpt.shape != ck_shape or ckpt.dtype != torch.float32 or not ckpt.is_contiguous():
+        raise ValueError("ckpt must be contiguous float32 %s" % (list(ck_shape),))
     if out is None:
         out = torch.zeros((N, H, D), dtype=torch.float32, device=xq.device)
     lib = library()

@@ -29,6 +29,7 @@ class spec_tree_layout(ctypes.Structure):
         ("n_attn_items", ctypes.c_int32),
         ("max_trunk_len", ctypes.c_int32),
         ("tree_off", _i32p),
+        ("tree_trunk_len", _i32p),
         ("row_tree", _i32p),
         ("row_branch", _i32p),
         ("row_anchor", _i32p),
@@ -64,6 +65,7 @@ class spec_profile(ctypes.Structure):
 # name -> (length as a function of the layout scalars)
 LAYOUT_ARRAYS = {
     "tree_off": lambda L: L.n_trees + 1,
+    "tree_trunk_len": lambda L: L.n_trees,
     "row_tree": lambda L: L.n_rows,
     "row_branch": lambda L: L.n_rows,
     "row_anchor": lambda L: L.n_rows,
@@ -83,8 +85,9 @@ LAYOUT_ARRAYS = {
     "attn_items": lambda L: L.n_attn_items * 8,
 }
 
-EXPORTS = ["spec_tree_pack", "spec_tree_attn_fwd", "spec_e2etv_fwd_bwd", "spec_gdn_replay_fwd",
-           "spec_status_string", "spec_last_error", "spec_abi_version", "spec_profile_attach"]
+EXPORTS = ["spec_tree_pack", "spec_tree_attn_fwd", "spec_e2etv_fwd_bwd", "spec_gdn_trunk_fwd",
+           "spec_gdn_replay_fwd", "spec_status_string", "spec_last_error", "spec_abi_version",
+           "spec_profile_attach"]
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -106,6 +109,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_e2etv_fwd_bwd.argtypes = [c.POINTER(spec_tree_layout), c.c_int64, c.c_int, c.c_void_p,
                                        c.c_void_p, c.c_float, c.c_void_p, c.c_void_p, c.c_void_p,
                                        c.c_void_p, c.POINTER(c.c_size_t), c.c_void_p]
+    lib.spec_gdn_trunk_fwd.restype = c.c_int
+    lib.spec_gdn_trunk_fwd.argtypes = [c.POINTER(spec_tree_layout), c.c_int32, c.c_int32, c.c_int32,
+                                       c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
+                                       c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p]
     lib.spec_gdn_replay_fwd.restype = c.c_int
     lib.spec_gdn_replay_fwd.argtypes = [c.POINTER(spec_tree_layout), c.c_int32, c.c_int32, c.c_int32,
                                         c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,

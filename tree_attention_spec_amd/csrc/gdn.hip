@@ -77,13 +77,18 @@ struct GdnShape {
   static constexpr int RB = D / RPW;          // workgroups per branch and head
 };
 
-template <int D, int K>
-__global__ __launch_bounds__(64) void gdn_replay_kernel(
-    const int32_t *__restrict__ tree_off, const int32_t *__restrict__ branch_tree,
+// TRUNK: the shared trunk pass instead of the replay. The path is then a
+// tree's whole trunk from the zero state (anchor = last trunk token, no branch
+// rows), every token's output is written, and the state after every `chunk`
+// tokens is stored as a checkpoint (slot 0: the zero state).
+template <int D, int K, bool TRUNK>
+__device__ __forceinline__ void gdn_path(
+    const int32_t *__restrict__ tree_off, const int32_t *__restrict__ tree_trunk_len,
+    const int32_t *__restrict__ branch_tree,
     const int32_t *__restrict__ branch_anchor, const int32_t *__restrict__ branch_len,
     const int32_t *__restrict__ branch_off, const __bf16 *__restrict__ xq,
     const __bf16 *__restrict__ xk, const __bf16 *__restrict__ xv, const float *__restrict__ taps,
-    const float *__restrict__ alpha, const float *__restrict__ beta, const float *__restrict__ ckpt,
+    const float *__restrict__ alpha, const float *__restrict__ beta, float *__restrict__ ckpt,
     float *__restrict__ out, int H, int chunk, int n_ckpt, int n_pairs) {
   using G = GdnShape<D>;
   constexpr int CW = G::CW, LPR = G::LPR, RPW = G::RPW, RB = G::RB;
@@ -99,12 +104,23 @@ __global__ __launch_bounds__(64) void gdn_replay_kernel(
   const int pair = x8 + 8 * (y8 / RB);
   if (pair >= n_pairs) return;
   const int h = pair % H;
-  const int b = pair / H;
-  const int W = branch_len[b];
-  if (W < 2) return;  // the branch has no rows (workgroup-uniform, before any barrier)
-  const int t = branch_tree[b], a = branch_anchor[b];
-  const int off = tree_off[t], r0 = branch_off[b];
-  const int c = (a + 1) / chunk;
+  int t, a, W, r0, c;
+  if (TRUNK) {  // pair = (tree, head)
+    t = pair / H;
+    a = tree_trunk_len[t] - 1;
+    W = 1;
+    r0 = 0;
+    c = 0;
+  } else {  // pair = (branch, head)
+    const int b = pair / H;
+    W = branch_len[b];
+    if (W < 2) return;  // the branch has no rows (workgroup-uniform, before any barrier)
+    t = branch_tree[b];
+    a = branch_anchor[b];
+    r0 = branch_off[b];
+    c = (a + 1) / chunk;
+  }
+  const int off = tree_off[t];
   const int p_end = a + W;  // path positions c*chunk .. a + W - 1
   const int i = rb * RPW + lane % RPW;  // this lane's state row
   const int cb = (lane / RPW) * CW;     // and its first column
@@ -118,8 +134,19 @@ __global__ __launch_bounds__(64) void gdn_replay_kernel(
 
   // this lane's columns of row i from checkpoint c (key-major: column j of row i at j*D + i)
   float S[CW];
-  {
-    const float *cp = ckpt + (((int64_t)t * n_ckpt + c) * H + h) * (int64_t)D * D + (int64_t)cb * D + i;
+  // this lane's part of checkpoint slot `slot` of its tree and head
+  auto slot_ptr = [&](int slot) {
+    return ckpt + (((int64_t)t * n_ckpt + slot) * H + h) * (int64_t)D * D + (int64_t)cb * D + i;
+  };
+  if (TRUNK) {
+    float *cp = slot_ptr(0);
+#pragma unroll
+    for (int j = 0; j < CW; ++j) {
+      S[j] = 0.f;
+      cp[(int64_t)j * D] = 0.f;
+    }
+  } else {
+    const float *cp = slot_ptr(c);
 #pragma unroll
     for (int j = 0; j < CW; ++j) S[j] = cp[(int64_t)j * D];
   }
@@ -231,7 +258,7 @@ __global__ __launch_bounds__(64) void gdn_replay_kernel(
     }
     const float u = row_sum(((up[0] + up[1]) + (up[2] + up[3])) + ((up[4] + up[5]) + (up[6] + up[7])));
     const float w = be * (av - al * u);
-    if (p > a) {  // a branch token: update and read out
+    if (TRUNK || p > a) {  // a branch token (or any trunk-pass token): update and read out
       float op[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) op[e] = 0.f;
@@ -257,6 +284,11 @@ __global__ __launch_bounds__(64) void gdn_replay_kernel(
       }
       const float o = row_sum(((op[0] + op[1]) + (op[2] + op[3])) + ((op[4] + op[5]) + (op[6] + op[7])));
       if (cb == 0) out[((int64_t)r * H + h) * D + i] = o;
+      if (TRUNK && (p + 1) % chunk == 0) {  // state after tokens 0 .. p: checkpoint (p + 1) / chunk
+        float *cp = slot_ptr((p + 1) / chunk);
+#pragma unroll
+        for (int j = 0; j < CW; ++j) cp[(int64_t)j * D] = S[j];
+      }
     } else {  // a replayed trunk token: update only
       Chunk ring[PD];
 #pragma unroll
@@ -273,14 +305,37 @@ __global__ __launch_bounds__(64) void gdn_replay_kernel(
   }
 }
 
+#define SPEC_GDN_PARAMS                                                                            \
+  const int32_t *__restrict__ tree_off, const int32_t *__restrict__ tree_trunk_len,                \
+      const int32_t *__restrict__ branch_tree, const int32_t *__restrict__ branch_anchor,          \
+      const int32_t *__restrict__ branch_len, const int32_t *__restrict__ branch_off,              \
+      const __bf16 *__restrict__ xq, const __bf16 *__restrict__ xk, const __bf16 *__restrict__ xv, \
+      const float *__restrict__ taps, const float *__restrict__ alpha,                             \
+      const float *__restrict__ beta, float *__restrict__ ckpt, float *__restrict__ out, int H,    \
+      int chunk, int n_ckpt, int n_pairs
+#define SPEC_GDN_ARGS                                                                         \
+  tree_off, tree_trunk_len, branch_tree, branch_anchor, branch_len, branch_off, xq, xk, xv, \
+      taps, alpha, beta, ckpt, out, H, chunk, n_ckpt, n_pairs
+
+// The trunk pass and the replay as kernels of their own names.
 template <int D, int K>
+__global__ __launch_bounds__(64) void gdn_trunk_kernel(SPEC_GDN_PARAMS) {
+  gdn_path<D, K, true>(SPEC_GDN_ARGS);
+}
+template <int D, int K>
+__global__ __launch_bounds__(64) void gdn_replay_kernel(SPEC_GDN_PARAMS) {
+  gdn_path<D, K, false>(SPEC_GDN_ARGS);
+}
+
+template <int D, int K, bool TRUNK>
 hipError_t launch_gdn(const spec_tree_layout &L, int H, int chunk, int n_ckpt, const void *xq,
                       const void *xk, const void *xv, const float *taps, const float *alpha,
-                      const float *beta, const float *ckpt, float *out, hipStream_t s) {
-  const int64_t pairs = (int64_t)L.n_branches * H;
+                      const float *beta, float *ckpt, float *out, hipStream_t s) {
+  const int64_t pairs = (int64_t)(TRUNK ? L.n_trees : L.n_branches) * H;
   const int64_t blocks = (pairs + 7) / 8 * 8 * GdnShape<D>::RB;
   if (pairs == 0) return hipSuccess;
-  hipLaunchKernelGGL((gdn_replay_kernel<D, K>), dim3((unsigned)blocks), dim3(64), 0, s, L.tree_off,
+  auto kern = TRUNK ? gdn_trunk_kernel<D, K> : gdn_replay_kernel<D, K>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64), 0, s, L.tree_off, L.tree_trunk_len,
                      L.branch_tree, L.branch_anchor, L.branch_len, L.branch_off,
                      static_cast<const __bf16 *>(xq), static_cast<const __bf16 *>(xk),
                      static_cast<const __bf16 *>(xv), taps, alpha, beta, ckpt, out, H, chunk, n_ckpt,
@@ -288,18 +343,73 @@ hipError_t launch_gdn(const spec_tree_layout &L, int H, int chunk, int n_ckpt, c
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool TRUNK>
 hipError_t launch_gdn_d(int K, const spec_tree_layout &L, int H, int chunk, int n_ckpt,
                         const void *xq, const void *xk, const void *xv, const float *taps,
-                        const float *alpha, const float *beta, const float *ckpt, float *out,
+                        const float *alpha, const float *beta, float *ckpt, float *out,
                         hipStream_t s) {
   switch (K) {
-    case 1: return launch_gdn<D, 1>(L, H, chunk, n_ckpt, xq, xk, xv, taps, alpha, beta, ckpt, out, s);
-    case 2: return launch_gdn<D, 2>(L, H, chunk, n_ckpt, xq, xk, xv, taps, alpha, beta, ckpt, out, s);
-    case 3: return launch_gdn<D, 3>(L, H, chunk, n_ckpt, xq, xk, xv, taps, alpha, beta, ckpt, out, s);
-    case 4: return launch_gdn<D, 4>(L, H, chunk, n_ckpt, xq, xk, xv, taps, alpha, beta, ckpt, out, s);
+    case 1: return launch_gdn<D, 1, TRUNK>(L, H, chunk, n_ckpt, xq, xk, xv, taps, alpha, beta, ckpt, out, s);
+    case 2: return launch_gdn<D, 2, TRUNK>(L, H, chunk, n_ckpt, xq, xk, xv, taps, alpha, beta, ckpt, out, s);
+    case 3: return launch_gdn<D, 3, TRUNK>(L, H, chunk, n_ckpt, xq, xk, xv, taps, alpha, beta, ckpt, out, s);
+    case 4: return launch_gdn<D, 4, TRUNK>(L, H, chunk, n_ckpt, xq, xk, xv, taps, alpha, beta, ckpt, out, s);
   }
   return hipErrorInvalidValue;
+}
+
+// Argument checks shared by the trunk pass and the replay.
+spec_status check_gdn(const spec_tree_layout *layout, bool trunk, int32_t n_heads, int32_t head_dim,
+                      int32_t conv_width, int32_t chunk, const void *const *bufs, int n_bufs) {
+  if (!layout) return fail(SPEC_ERR_INVALID_ARG, "layout must be non-NULL");
+  const spec_tree_layout &L = *layout;
+  if (L.n_trees < 1 || L.n_rows < 1 || L.n_branches < 0 || L.max_trunk_len < 1)
+    return fail(SPEC_ERR_INVALID_ARG, "layout scalars are not those of a packed tree");
+  const bool need = trunk ? true : L.n_branches > 0;
+  if (need && (!L.tree_off || (trunk && !L.tree_trunk_len) ||
+               (!trunk && (!L.branch_tree || !L.branch_anchor || !L.branch_len || !L.branch_off))))
+    return fail(SPEC_ERR_INVALID_ARG, "layout device arrays are missing (pack with a buffer first)");
+  if (n_heads < 1) return fail(SPEC_ERR_INVALID_ARG, "n_heads must be >= 1 (got %d)", n_heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SPEC_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", head_dim);
+  if (conv_width < 1 || conv_width > 4)
+    return fail(SPEC_ERR_UNSUPPORTED, "conv_width %d not in 1..4", conv_width);
+  if (chunk < 1) return fail(SPEC_ERR_INVALID_ARG, "chunk must be >= 1 (got %d)", chunk);
+  const int64_t pairs = (int64_t)(trunk ? L.n_trees : L.n_branches) * n_heads;
+  if ((pairs + 7) / 8 * 8 * (head_dim / 32) > INT32_MAX)
+    return fail(SPEC_ERR_UNSUPPORTED, "too many %s x heads", trunk ? "trees" : "branches");
+  for (int k = 0; k < n_bufs; ++k)
+    if (!bufs[k]) return fail(SPEC_ERR_INVALID_ARG, "device buffers must be non-NULL");
+  for (int k = 0; k < n_bufs; ++k)
+    if (!aligned16(bufs[k])) return fail(SPEC_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  return SPEC_OK;
+}
+
+spec_status run_gdn(bool trunk, const spec_tree_layout *layout, int32_t n_heads, int32_t head_dim,
+                    int32_t conv_width, int32_t chunk, const void *d_xq, const void *d_xk,
+                    const void *d_xv, const float *d_taps, const float *d_alpha, const float *d_beta,
+                    float *d_ckpt, float *d_out, spec_stream stream) {
+  clear_error();
+  const void *bufs[] = {d_xq, d_xk, d_xv, d_taps, d_alpha, d_beta, d_ckpt, d_out};
+  spec_status st = check_gdn(layout, trunk, n_heads, head_dim, conv_width, chunk, bufs, 8);
+  if (st != SPEC_OK) return st;
+  const spec_tree_layout &L = *layout;
+  const int n_ckpt = L.max_trunk_len / chunk + 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  prof_mark(s, trunk ? "gdn_trunk:begin" : "gdn:begin");
+  hipError_t e;
+  if (trunk)
+    e = head_dim == 64 ? launch_gdn_d<64, true>(conv_width, L, n_heads, chunk, n_ckpt, d_xq, d_xk, d_xv,
+                                                d_taps, d_alpha, d_beta, d_ckpt, d_out, s)
+                       : launch_gdn_d<128, true>(conv_width, L, n_heads, chunk, n_ckpt, d_xq, d_xk,
+                                                 d_xv, d_taps, d_alpha, d_beta, d_ckpt, d_out, s);
+  else
+    e = head_dim == 64 ? launch_gdn_d<64, false>(conv_width, L, n_heads, chunk, n_ckpt, d_xq, d_xk,
+                                                 d_xv, d_taps, d_alpha, d_beta, d_ckpt, d_out, s)
+                       : launch_gdn_d<128, false>(conv_width, L, n_heads, chunk, n_ckpt, d_xq, d_xk,
+                                                  d_xv, d_taps, d_alpha, d_beta, d_ckpt, d_out, s);
+  if (e != hipSuccess) return hip_fail(e, trunk ? "gdn_trunk_kernel launch" : "gdn_replay_kernel launch");
+  prof_mark(s, trunk ? "gdn_trunk" : "gdn_replay");
+  return SPEC_OK;
 }
 
 }  // namespace
@@ -314,37 +424,17 @@ extern "C" spec_status spec_gdn_replay_fwd(const spec_tree_layout *layout, int32
                                            const float *d_taps, const float *d_alpha,
                                            const float *d_beta, const float *d_ckpt, float *d_out,
                                            spec_stream stream) {
-  clear_error();
-  if (!layout) return fail(SPEC_ERR_INVALID_ARG, "layout must be non-NULL");
-  const spec_tree_layout &L = *layout;
-  if (L.n_trees < 1 || L.n_rows < 1 || L.n_branches < 0 || L.max_trunk_len < 1)
-    return fail(SPEC_ERR_INVALID_ARG, "layout scalars are not those of a packed tree");
-  if (L.n_branches > 0 && (!L.tree_off || !L.branch_tree || !L.branch_anchor || !L.branch_len ||
-                           !L.branch_off))
-    return fail(SPEC_ERR_INVALID_ARG, "layout device arrays are missing (pack with a buffer first)");
-  if (n_heads < 1) return fail(SPEC_ERR_INVALID_ARG, "n_heads must be >= 1 (got %d)", n_heads);
-  if (head_dim != 64 && head_dim != 128)
-    return fail(SPEC_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", head_dim);
-  if (conv_width < 1 || conv_width > 4)
-    return fail(SPEC_ERR_UNSUPPORTED, "conv_width %d not in 1..4", conv_width);
-  if (chunk < 1) return fail(SPEC_ERR_INVALID_ARG, "chunk must be >= 1 (got %d)", chunk);
-  if (((int64_t)L.n_branches * n_heads + 7) / 8 * 8 * (head_dim / 32) > INT32_MAX)
-    return fail(SPEC_ERR_UNSUPPORTED, "too many branches x heads");
-  if (!d_xq || !d_xk || !d_xv || !d_taps || !d_alpha || !d_beta || !d_ckpt || !d_out)
-    return fail(SPEC_ERR_INVALID_ARG, "device buffers must be non-NULL");
-  if (!aligned16(d_xq) || !aligned16(d_xk) || !aligned16(d_xv) || !aligned16(d_taps) ||
-      !aligned16(d_alpha) || !aligned16(d_beta) || !aligned16(d_ckpt) || !aligned16(d_out))
-    return fail(SPEC_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
-  const int n_ckpt = L.max_trunk_len / chunk + 1;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  prof_mark(s, "gdn:begin");
-  const hipError_t e =
-      head_dim == 64
-          ? launch_gdn_d<64>(conv_width, L, n_heads, chunk, n_ckpt, d_xq, d_xk, d_xv, d_taps,
-                             d_alpha, d_beta, d_ckpt, d_out, s)
-          : launch_gdn_d<128>(conv_width, L, n_heads, chunk, n_ckpt, d_xq, d_xk, d_xv, d_taps,
-                              d_alpha, d_beta, d_ckpt, d_out, s);
-  if (e != hipSuccess) return hip_fail(e, "gdn_replay_kernel launch");
-  prof_mark(s, "gdn_replay");
-  return SPEC_OK;
+  // the replay only reads the checkpoints
+  return run_gdn(false, layout, n_heads, head_dim, conv_width, chunk, d_xq, d_xk, d_xv, d_taps, d_alpha,
+                 d_beta, const_cast<float *>(d_ckpt), d_out, stream);
+}
+
+extern "C" spec_status spec_gdn_trunk_fwd(const spec_tree_layout *layout, int32_t n_heads,
+                                          int32_t head_dim, int32_t conv_width, int32_t chunk,
+                                          const void *d_xq, const void *d_xk, const void *d_xv,
+                                          const float *d_taps, const float *d_alpha,
+                                          const float *d_beta, float *d_ckpt, float *d_out,
+                                          spec_stream stream) {
+  return run_gdn(true, layout, n_heads, head_dim, conv_width, chunk, d_xq, d_xk, d_xv, d_taps, d_alpha,
+                 d_beta, d_ckpt, d_out, stream);
 }

@@ -314,6 +314,7 @@ extern "C" spec_status spec_tree_pack(int32_t n_trees, const int32_t *h_trunk_le
   char *base = static_cast<char *>(d_mem);
   auto at = [&](size_t off) { return reinterpret_cast<int32_t *>(base + off); };
   L.tree_off = at(c.off_tree_off);
+  L.tree_trunk_len = at(c.off_tree_len);
   L.branch_tree = at(c.off_branch_tree);
   L.branch_anchor = at(c.off_branch_anchor);
   L.branch_len = at(c.off_branch_len);
