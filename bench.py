@@ -16,6 +16,7 @@ Prints one JSON line. Only one GPU is supported (--gpus must be 1).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -84,8 +85,11 @@ MARK_KERNELS = {
     "e2etv_stats": (["e2etv_team_clear", "e2etv_stats_team_kernel", "e2etv_stats_kernel"], ("e2etv.hip",)),
     "e2etv_scan": (["e2etv_scan_kernel"], ("e2etv.hip",)),
     "e2etv_grad": (["e2etv_grad_kernel"], ("e2etv.hip",)),
-    "gdn_trunk": (["gdn_trunk_kernel"], ("gdn.hip",)),
-    "gdn_replay": (["gdn_replay_kernel"], ("gdn.hip",)),
+    "gdn_trunk": (["gdn_trunk_kernel"], ("gdn.hip", "gdn_util.h")),
+    "gdn_chunk_prep": (["gdn_chunk_prep_kernel"], ("gdn_chunk.hip", "gdn_util.h")),
+    "gdn_chunk_scan": (["gdn_chunk_scan_kernel"], ("gdn_chunk.hip", "gdn_util.h")),
+    "gdn_chunk_out": (["gdn_chunk_out_kernel"], ("gdn_chunk.hip", "gdn_util.h")),
+    "gdn_replay": (["gdn_replay_kernel"], ("gdn.hip", "gdn_util.h")),
 }
 
 
@@ -273,6 +277,40 @@ def gdn_work(s, C):
     return int(replay.sum()), int(np.maximum(w - 1, 0).sum())
 
 
+def gdn_trunk_work_bytes(tree, H, D, K, C):
+    import tree_attention_spec_amd as tas
+    lib = tas.library()
+    n = ctypes.c_size_t(0)
+    st = lib.spec_gdn_trunk_fwd(ctypes.byref(tree.layout), H, D, K, C, None, None, None, None, None, None,
+                                None, None, None, ctypes.byref(n), None)
+    assert st == 0
+    return n.value
+
+
+def gdn_flops(s, H, D, C):
+    """Algorithmic flops of each GDN kernel (an FMA counts two).
+
+    Token-at-a-time (trunk pass with C > 64, and the replay): per token and head
+    u = S k (D^2 FMA) and S <- alpha S + w k^T (D^2 mul + D^2 FMA), plus o = S q
+    (D^2 FMA) for a token whose output is read. Chunked trunk pass, per chunk of
+    L tokens and head: prep forms A (L(L-1)/2 dots of length D) and P (L(L+1)/2
+    dots), solves for the 2D columns of [U | W] (L(L-1)/2 FMAs each) and forms
+    P [U | W] (L(L+1)/2 FMAs per column); scan (full chunks only) forms
+    U - W S^T and delta^T Kd (L D^2 FMAs each); out forms Q' S^T (L D^2 FMAs)."""
+    import numpy as np
+    T = np.asarray(s["trunk_len"], np.int64)
+    n_replay, n_branch = gdn_work(s, C)
+    f = {"gdn_replay": float(H) * D * D * (5 * n_replay + 7 * n_branch),
+         "gdn_trunk": float(H) * D * D * 7 * int(T.sum())}
+    Ls = np.concatenate([np.minimum(C, t - np.arange(0, t, C)) for t in T]).astype(np.float64)
+    full = Ls[Ls == C]
+    tri = Ls * (Ls - 1) / 2 + Ls * (Ls + 1) / 2            # entries of A and P
+    f["gdn_chunk_prep"] = float(H) * float(np.sum(2 * D * tri + 2 * 2 * D * tri))
+    f["gdn_chunk_scan"] = float(H) * float(np.sum(2 * 2 * full * D * D))
+    f["gdn_chunk_out"] = float(H) * float(np.sum(2 * Ls * D * D))
+    return f
+
+
 def gdn_bench(args, cfg, s, dev):
     """GDN scoring of the workload's tree: the shared trunk pass (trunk outputs and
     checkpoints every 64 tokens), then the indexed replay of every branch from those
@@ -297,9 +335,10 @@ def gdn_bench(args, cfg, s, dev):
     x = [t[n] for n in ("xq", "xk", "xv", "taps", "alpha", "beta")]
     ckpt = torch.zeros((tree.n_trees, slots, H, D, D), dtype=torch.float32, device=dev)
     out = torch.zeros((N, H, D), dtype=torch.float32, device=dev)
+    work = torch.empty(gdn_trunk_work_bytes(tree, H, D, K, C), dtype=torch.uint8, device=dev)
 
     def call():
-        tas.spec_gdn_trunk_fwd(tree, *x, chunk=C, ckpt=ckpt, out=out)
+        tas.spec_gdn_trunk_fwd(tree, *x, chunk=C, ckpt=ckpt, out=out, work=work)
         tas.spec_gdn_replay_fwd(tree, *x, ckpt=ckpt, chunk=C, out=out)
 
     for _ in range(args.warmup):
@@ -312,19 +351,19 @@ def gdn_bench(args, cfg, s, dev):
             call()
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    kms = {}
-    for name in ("gdn_trunk", "gdn_replay"):
-        ms = [d for tm in timers for n, d in tm.durations() if n == name]
-        kms[name] = sum(ms) / len(ms)
+    per = {}
+    for tm in timers:
+        for n, d in tm.durations():
+            per.setdefault(n, []).append(d)
+    kms = {n: sum(v) / len(v) for n, v in per.items()}
     n_replay, n_branch = gdn_work(s, C)
     n_trunk = int(np.sum(s["trunk_len"]))
-    # per token and head: u = S k (D^2 FMA), S <- alpha S + w k^T (D^2 mul + D^2 FMA), and for a
-    # token that is read out o = S q (D^2 FMA); an FMA counts two flops
-    flop = {"gdn_trunk": float(H) * D * D * 7 * n_trunk,
-            "gdn_replay": float(H) * D * D * (5 * n_replay + 7 * n_branch)}
+    flop = gdn_flops(s, H, D, C)
     tf = {k: flop[k] / (kms[k] * 1e-3) / 1e12 for k in kms}
     for k in kms:
         log("%s %.4f ms (%.1f TFLOP/s)" % (k, kms[k], tf[k]))
+    log("trunk pass %.4f ms, replay %.4f ms" % (sum(v for k, v in kms.items() if k != "gdn_replay"),
+                                               kms["gdn_replay"]))
     log("per head: %d trunk tokens, %d replayed + %d branch tokens" % (n_trunk, n_replay, n_branch))
     dom = max(kms, key=kms.get)
     return {

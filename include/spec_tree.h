@@ -294,15 +294,29 @@ spec_status spec_gdn_replay_fwd(const spec_tree_layout *layout, int32_t n_heads,
  * state, layout as for spec_gdn_replay_fwd) receives the state after trunk
  * tokens 0 .. c*chunk-1 for c = 0 .. T_t / chunk. Slots a shorter tree never
  * reaches are left as they are. Branch rows of d_out are left as they are.
- * The recurrence is sequential along a trunk; its work is one workgroup per
- * (tree, head, row block).
- * Errors: as spec_gdn_replay_fwd.
+ *
+ * For chunk <= 64 the pass runs a chunk at a time: the chunks' S0-independent
+ * parts (features, the in-chunk triangular system, the output and state
+ * coefficients) in parallel, then one ordered pass over the chunks per head
+ * that carries the state, then the outputs in parallel; the result equals the
+ * token-at-a-time recurrence up to float32 rounding. For chunk > 64 one
+ * workgroup per (tree, head, row block) walks the trunk a token at a time.
+ *
+ * Arguments: as spec_gdn_replay_fwd, plus
+ *   d_ckpt      [n_trees, max_trunk_len / chunk + 1, H, D, D] float32, written.
+ *   d_out       [N, H, D] float32; trunk rows written.
+ *   d_work      workspace of *work_bytes bytes (16-byte aligned), or NULL for a
+ *               size query (then nothing else is read). The chunked pass keeps
+ *               five 64 x D float32 tiles per (tree, chunk, head) there.
+ * Calls that share a workspace must not overlap in time.
+ * Errors: as spec_gdn_replay_fwd, plus SPEC_ERR_WORKSPACE.
  */
 spec_status spec_gdn_trunk_fwd(const spec_tree_layout *layout, int32_t n_heads, int32_t head_dim,
                                int32_t conv_width, int32_t chunk, const void *d_xq,
                                const void *d_xk, const void *d_xv, const float *d_taps,
                                const float *d_alpha, const float *d_beta, float *d_ckpt,
-                               float *d_out, spec_stream stream);
+                               float *d_out, void *d_work, size_t *work_bytes,
+                               spec_stream stream);
 
 /*
  * Measurement hook (benchmarks only; it changes no result).

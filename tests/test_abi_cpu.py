@@ -179,14 +179,32 @@ def test_gdn_argument_checks(tas):
 
 
 def test_gdn_trunk_argument_checks(tas):
-    """spec_gdn_trunk_fwd rejects bad arguments before any launch (no GPU is touched)."""
+    """spec_gdn_trunk_fwd: workspace size queries, then argument checks before any launch
+    (no GPU is touched)."""
     from tree_attention_spec_amd import _lib
     lib = tas.library()
     L = _query_layout(tas)
     P = ctypes.c_void_p(0x1000)
+    n = ctypes.c_size_t(0)
 
-    def call(H, D, K, C, p=P):
-        return lib.spec_gdn_trunk_fwd(ctypes.byref(L), H, D, K, C, p, p, p, p, p, p, p, p, None)
+    def query(H, D, C):
+        n.value = 0
+        st = lib.spec_gdn_trunk_fwd(ctypes.byref(L), H, D, 4, C, None, None, None, None, None, None,
+                                    None, None, None, ctypes.byref(n), None)
+        return st, n.value
+
+    # five 64 x D float32 tiles per (tree, chunk, head), plus one float each, rounded to 256 B
+    chunks = -(-CONFIGS["gqa8b"].trunk // 64)
+    items = chunks * 32
+    assert query(32, 128, 64) == (0, items * 5 * 64 * 128 * 4 + -(-items * 4 // 256) * 256)
+    assert query(32, 128, 128) == (0, 256)          # the token-at-a-time pass keeps nothing
+    assert query(32, 96, 64)[0] == 1
+    assert query(32, 128, 0)[0] == 1
+
+    def call(H, D, K, C, p=P, work=P, nbytes=1 << 40):
+        n.value = nbytes
+        return lib.spec_gdn_trunk_fwd(ctypes.byref(L), H, D, K, C, p, p, p, p, p, p, p, p, work,
+                                      ctypes.byref(n), None)
 
     assert call(32, 128, 4, 64) == 1                # the layout has no device arrays yet
     fake = ctypes.cast(ctypes.c_void_p(0x1000), _lib._i32p)
@@ -200,3 +218,6 @@ def test_gdn_trunk_argument_checks(tas):
     assert call(32, 128, 4, 64, None) == 1
     assert call(32, 128, 4, 64, ctypes.c_void_p(0x1008)) == 1
     assert "aligned" in lib.spec_last_error().decode()
+    assert call(32, 128, 4, 64, nbytes=1000) == 3   # SPEC_ERR_WORKSPACE: too small
+    assert n.value == query(32, 128, 64)[1]
+    assert call(32, 128, 4, 64, work=ctypes.c_void_p(0x1004)) == 1

@@ -198,6 +198,39 @@ def test_gdn_trunk_edges():
     _trunk_compare(s, 2, 64, 4, 16, seed=77)
 
 
+def test_gdn_trunk_token_at_a_time():
+    """Checkpoints every 128 tokens take the token-at-a-time trunk pass."""
+    say("gdn trunk pass: chunk 128 (token at a time)")
+    s = dict(trunk_len=np.array([300, 128], np.int32), n_branches=np.array([3, 1], np.int32),
+             anchors=np.array([127, 128, 299, 127], np.int32), branch_len=np.array([4, 3, 5, 2], np.int32))
+    _trunk_compare(s, 2, 128, 4, 128, seed=91)
+
+
+def test_gdn_trunk_work_reuse():
+    """One workspace and checkpoint buffer reused for two trees in a row (the second
+    smaller) gives the same results as fresh buffers."""
+    import torch
+    import tree_attention_spec_amd as tas
+    say("gdn trunk pass: workspace reuse")
+    H, D, K, C = 2, 64, 4, 16
+    outs = []
+    work = None
+    for T in ([150, 40], [33]):
+        s = dict(trunk_len=np.array(T, np.int32), n_branches=np.zeros(len(T), np.int32),
+                 anchors=np.zeros(0, np.int32), branch_len=np.zeros(0, np.int32))
+        tree = tas.spec_tree_pack(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"])
+        inp = gen_gdn(5, tree.n_rows, H, D, K)
+        x = [to_device(np.ascontiguousarray(inp[n])) for n in ("xq", "xk", "xv", "taps", "alpha", "beta")]
+        if work is None:
+            work = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+        ck1, o1 = tas.spec_gdn_trunk_fwd(tree, *x, chunk=C, work=work)
+        ck2, o2 = tas.spec_gdn_trunk_fwd(tree, *x, chunk=C)
+        torch.cuda.synchronize()
+        assert torch.equal(ck1, ck2) and torch.equal(o1, o2)
+        outs.append(o1)
+    say("  bit-identical with a reused workspace")
+
+
 @pytest.mark.slow
 def test_gdn_trunk_workload_sampled_heads():
     """The 8B-like tree with 32 heads of 128, width-4 convolution, checkpoints every 64

@@ -238,14 +238,15 @@ def _check_gdn(tree, xq, xk, xv, taps, alpha, beta, chunk):
 
 def spec_gdn_trunk_fwd(tree: PackedTree, xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor,
                        taps: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor, chunk: int = 64,
-                       ckpt: torch.Tensor = None, out: torch.Tensor = None):
+                       ckpt: torch.Tensor = None, out: torch.Tensor = None, work: torch.Tensor = None):
     """Shared GDN trunk pass: every trunk row's output and the checkpoints.
 
     Inputs as for spec_gdn_replay_fwd. Returns (ckpt, out): ckpt [n_trees, slots,
     H, D, D] fp32 key-major, slot c of tree t the state after its first c*chunk
     trunk tokens (slots past floor(T_t / chunk) as passed in, zero for a new
     tensor); out [N,H,D] fp32 with the trunk rows written (branch rows as passed
-    in, zero for a new tensor).
+    in, zero for a new tensor). ``work`` is an optional uint8 device workspace
+    reused across calls (allocated when missing or too small).
     """
     N, H, D, K, ck_shape = _check_gdn(tree, xq, xk, xv, taps, alpha, beta, chunk)
     if ckpt is None:
@@ -256,9 +257,14 @@ def spec_gdn_trunk_fwd(tree: PackedTree, xq: torch.Tensor, xk: torch.Tensor, xv:
         out = torch.zeros((N, H, D), dtype=torch.float32, device=xq.device)
     lib = library()
     ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    nbytes = ctypes.c_size_t(0)
+    _lib.check(lib, lib.spec_gdn_trunk_fwd(ctypes.byref(tree.layout), H, D, K, chunk, None, None, None,
+                                           None, None, None, None, None, None, ctypes.byref(nbytes), None))
+    if work is None or work.numel() < nbytes.value:
+        work = torch.empty(nbytes.value, dtype=torch.uint8, device=xq.device)
     st = lib.spec_gdn_trunk_fwd(ctypes.byref(tree.layout), H, D, K, chunk, ptr(xq), ptr(xk), ptr(xv),
-                                ptr(taps), ptr(alpha), ptr(beta), ptr(ckpt), ptr(out),
-                                ctypes.c_void_p(_stream(xq.device)))
+                                ptr(taps), ptr(alpha), ptr(beta), ptr(ckpt), ptr(out), ptr(work),
+                                ctypes.byref(nbytes), ctypes.c_void_p(_stream(xq.device)))
     _lib.check(lib, st)
     return ckpt, out
 

@@ -112,7 +112,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_gdn_trunk_fwd.restype = c.c_int
     lib.spec_gdn_trunk_fwd.argtypes = [c.POINTER(spec_tree_layout), c.c_int32, c.c_int32, c.c_int32,
                                        c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
-                                       c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p]
+                                       c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
+                                       c.POINTER(c.c_size_t), c.c_void_p]
     lib.spec_gdn_replay_fwd.restype = c.c_int
     lib.spec_gdn_replay_fwd.argtypes = [c.POINTER(spec_tree_layout), c.c_int32, c.c_int32, c.c_int32,
                                         c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,

@@ -30,30 +30,21 @@
 // branch and head), read once with each load instruction covering 64
 // consecutive value rows of one key column (key-major storage).
 #include "common.h"
+#include "gdn_util.h"
 
 namespace spec {
 
+// the chunkwise trunk pass (gdn_chunk.hip), for chunk <= 64
+size_t gdn_chunk_work_bytes(const spec_tree_layout &L, int H, int D, int chunk);
+hipError_t launch_gdn_chunked(const spec_tree_layout &L, int H, int D, int K, int chunk, int n_ckpt,
+                              const void *xq, const void *xk, const void *xv, const float *taps,
+                              const float *alpha, const float *beta, float *ckpt, float *out,
+                              void *work, hipStream_t s);
+
 namespace {
 
-template <int CTRL>
-__device__ inline float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-// Sum over the wave, the same bits in every lane: within rows of 16 by DPP,
-// then across rows and halves by permlane swaps.
-__device__ inline float wave_sum(float x) {
-  x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
-  x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
-  x += dpp_f<0x141>(x);  // row_half_mirror
-  x += dpp_f<0x140>(x);  // row_mirror
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// x * sigmoid(x) with the hardware exponential and reciprocal (about 1 ulp each)
-__device__ inline float silu_f(float x) { return x * __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+using gdn::silu_f;
+using gdn::wave_sum;
 
 // 8 consecutive floats of an LDS array, read with two 128-bit loads (the same
 // address in every lane: a broadcast)
@@ -387,14 +378,41 @@ spec_status check_gdn(const spec_tree_layout *layout, bool trunk, int32_t n_head
 spec_status run_gdn(bool trunk, const spec_tree_layout *layout, int32_t n_heads, int32_t head_dim,
                     int32_t conv_width, int32_t chunk, const void *d_xq, const void *d_xk,
                     const void *d_xv, const float *d_taps, const float *d_alpha, const float *d_beta,
-                    float *d_ckpt, float *d_out, spec_stream stream) {
+                    float *d_ckpt, float *d_out, void *d_work, size_t *work_bytes, spec_stream stream) {
   clear_error();
+  if (trunk && !work_bytes) return fail(SPEC_ERR_INVALID_ARG, "work_bytes must be non-NULL");
+  if (trunk && !d_work) {  // size query
+    if (!layout) return fail(SPEC_ERR_INVALID_ARG, "layout must be non-NULL");
+    if (chunk < 1) return fail(SPEC_ERR_INVALID_ARG, "chunk must be >= 1 (got %d)", chunk);
+    if (n_heads < 1 || (head_dim != 64 && head_dim != 128))
+      return fail(SPEC_ERR_INVALID_ARG, "need n_heads >= 1 and head_dim in {64, 128}");
+    *work_bytes = gdn_chunk_work_bytes(*layout, n_heads, head_dim, chunk);
+    return SPEC_OK;
+  }
   const void *bufs[] = {d_xq, d_xk, d_xv, d_taps, d_alpha, d_beta, d_ckpt, d_out};
   spec_status st = check_gdn(layout, trunk, n_heads, head_dim, conv_width, chunk, bufs, 8);
   if (st != SPEC_OK) return st;
   const spec_tree_layout &L = *layout;
   const int n_ckpt = L.max_trunk_len / chunk + 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (trunk) {
+    const size_t need = gdn_chunk_work_bytes(L, n_heads, head_dim, chunk);
+    if (*work_bytes < need) {
+      const size_t have = *work_bytes;
+      *work_bytes = need;
+      return fail(SPEC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", have, need);
+    }
+    if (!aligned16(d_work)) return fail(SPEC_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  }
+  if (trunk && chunk <= 64) {
+    if ((int64_t)L.n_trees * ((L.max_trunk_len + chunk - 1) / chunk) * n_heads > INT32_MAX)
+      return fail(SPEC_ERR_UNSUPPORTED, "too many trees x chunks x heads");
+    prof_mark(s, "gdn_trunk:begin");
+    const hipError_t e = launch_gdn_chunked(L, n_heads, head_dim, conv_width, chunk, n_ckpt, d_xq, d_xk,
+                                            d_xv, d_taps, d_alpha, d_beta, d_ckpt, d_out, d_work, s);
+    if (e != hipSuccess) return hip_fail(e, "chunkwise GDN trunk pass launch");
+    return SPEC_OK;
+  }
   prof_mark(s, trunk ? "gdn_trunk:begin" : "gdn:begin");
   hipError_t e;
   if (trunk)
@@ -426,7 +444,7 @@ extern "C" spec_status spec_gdn_replay_fwd(const spec_tree_layout *layout, int32
                                            spec_stream stream) {
   // the replay only reads the checkpoints
   return run_gdn(false, layout, n_heads, head_dim, conv_width, chunk, d_xq, d_xk, d_xv, d_taps, d_alpha,
-                 d_beta, const_cast<float *>(d_ckpt), d_out, stream);
+                 d_beta, const_cast<float *>(d_ckpt), d_out, nullptr, nullptr, stream);
 }
 
 extern "C" spec_status spec_gdn_trunk_fwd(const spec_tree_layout *layout, int32_t n_heads,
@@ -434,7 +452,7 @@ extern "C" spec_status spec_gdn_trunk_fwd(const spec_tree_layout *layout, int32_
                                           const void *d_xq, const void *d_xk, const void *d_xv,
                                           const float *d_taps, const float *d_alpha,
                                           const float *d_beta, float *d_ckpt, float *d_out,
-                                          spec_stream stream) {
+                                          void *d_work, size_t *work_bytes, spec_stream stream) {
   return run_gdn(true, layout, n_heads, head_dim, conv_width, chunk, d_xq, d_xk, d_xv, d_taps, d_alpha,
-                 d_beta, d_ckpt, d_out, stream);
+                 d_beta, d_ckpt, d_out, d_work, work_bytes, stream);
 }
