@@ -22,7 +22,8 @@
 //   prep (tree, chunk, head): features of the chunk's tokens (convolution along
 //        the trunk, SiLU, L2 norms), A and P, the triangular solve, Q', O', Kd.
 //   scan (tree, head, 16 value rows): S <- gamma S + (U - W S^T)^T Kd over the
-//        full chunks in order, storing each end state as the next checkpoint.
+//        full chunks in order on the fp32 matrix cores, storing each end state
+//        as the next checkpoint.
 //   out  (tree, chunk, head): o = Q' S_c^T + O' from checkpoint c.
 // A chunk tile always has 64 rows; rows past the chunk's tokens are zero.
 // Intermediates live in a caller-provided workspace.
@@ -79,9 +80,12 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(
   const int off = tree_off[t];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
-  // features before the norms: the convolution along the trunk, then SiLU
+  // features before the norms: the convolution along the trunk, then SiLU.
+  // Thread (d, group) takes channel d of CT / G consecutive tokens; the raw
+  // rows they read (K - 1 more before the first) are all loaded up front.
   {
-    const int d = tid % D;
+    constexpr int G = 256 / D, TPG = CT / G, NR = TPG + K - 1;
+    const int d = tid % D, s0 = (tid / D) * TPG;
     float tq[K], tk[K], tv[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) {
@@ -89,26 +93,30 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(
       tk[j] = taps[(((int64_t)1 * H + h) * D + d) * K + j];
       tv[j] = taps[(((int64_t)2 * H + h) * D + d) * K + j];
     }
-    for (int s = tid / D; s < CT; s += 256 / D) {
-      float aq = 0.f, ak = 0.f, av = 0.f;
-      if (s < L) {
+    float rq[NR], rk[NR], rv[NR];
 #pragma unroll
-        for (int j = 0; j < K; ++j) {
-          const int p = p0 + s - j;
-          if (p >= 0) {
-            const int64_t at = ((int64_t)(off + p) * H + h) * D + d;
-            aq = fmaf(tq[j], (float)xq[at], aq);
-            ak = fmaf(tk[j], (float)xk[at], ak);
-            av = fmaf(tv[j], (float)xv[at], av);
-          }
-        }
-        aq = silu_f(aq);
-        ak = silu_f(ak);
-        av = silu_f(av);
+    for (int i = 0; i < NR; ++i) {  // raw row i is trunk position p0 + s0 - (K - 1) + i
+      const int p = p0 + s0 - (K - 1) + i;
+      const bool ok = p >= 0 && p < p0 + L;
+      const int64_t at = ((int64_t)(off + (ok ? p : 0)) * H + h) * D + d;
+      const float q = (float)xq[at], k = (float)xk[at], v = (float)xv[at];
+      rq[i] = ok ? q : 0.f;
+      rk[i] = ok ? k : 0.f;
+      rv[i] = ok ? v : 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < TPG; ++s) {
+      float aq = 0.f, ak = 0.f, av = 0.f;
+#pragma unroll
+      for (int j = 0; j < K; ++j) {  // tap j reads position p0 + s0 + s - j
+        aq = fmaf(tq[j], rq[s + K - 1 - j], aq);
+        ak = fmaf(tk[j], rk[s + K - 1 - j], ak);
+        av = fmaf(tv[j], rv[s + K - 1 - j], av);
       }
-      qf[s][d] = aq;
-      kf[s][d] = ak;
-      vf[s][d] = av;
+      const bool live = s0 + s < L;
+      qf[s0 + s][d] = live ? silu_f(aq) : 0.f;
+      kf[s0 + s][d] = live ? silu_f(ak) : 0.f;
+      vf[s0 + s][d] = live ? silu_f(av) : 0.f;
     }
   }
   // gates: running sum of log alpha (a wave scan); rows past L have alpha = 1, beta = 0
@@ -225,7 +233,6 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(
         acc = fmaf(-a.w, x[r0 + 3], acc);
       }
       x[s] = bt[s] * acc;
-      __builtin_amdgcn_sched_barrier(0);
     }
     float *dst_x = isv ? rec_part<D>(ws, item, RU) + j : rec_part<D>(ws, item, RW) + (j - D);
 #pragma unroll
@@ -244,128 +251,141 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(
       }
       const float qv = qcol[s * LD];
       dst_y[s * D] = isv ? acc : eg[s] * qv - acc;  // O' = P U; Q' = e^g Q - P W
-      __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // Kd_s = e^{g_{L-1} - g_s} k_s (g is flat past L, so g[CT-1] = g[L-1])
+  // Kd_s = e^{g_{L-1} - g_s} k_s (g is flat past L, so g[CT-1] = g[L-1]),
+  // stored transposed: key-major, CT tokens per key
   {
     float *kd = rec_part<D>(ws, item, RKD);
     const float gl = g[CT - 1];
     for (int i = tid; i < CT * D; i += 256) {
-      const int s = i / D, d = i % D;
-      kd[i] = __expf(gl - g[s]) * kf[s][d];
+      const int key = i / CT, s = i % CT;
+      kd[i] = __expf(gl - g[s]) * kf[s][key];
     }
   }
   if (tid == 0) gam[item] = eg[CT - 1];
 }
 
 // ---------------------------------------------------------------------------
-// scan: one workgroup of 256 per (tree, head, 16 value rows). The D / 16 row
+// scan: one workgroup of 256 per (tree, head, 16 value rows), on the fp32
+// matrix cores (v_mfma_f32_16x16x4_f32: lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16] and holds C[4 (l / 16) + r][l % 16], r = 0..3). Per chunk:
+//   delta (64 tokens x 16 rows) = U - W S^T: wave w takes tokens 16w..16w+15,
+//        K runs over the keys, lane group g taking keys g D/4 .. (g+1) D/4 - 1;
+//   S (16 rows x D keys) = gamma S + delta^T Kd: wave w owns D/64 tiles of 16
+//        keys in registers, K runs over the tokens, group g taking 16g .. 16g+15.
+// W, Kd (stored key-major) and U reach registers straight from the workspace
+// one chunk ahead; delta and S pass between waves through LDS. The D / 16 row
 // blocks of one (tree, head) take workgroup ids 8 apart, so they run on one
 // XCD and share its L2 for W and Kd.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 template <int D>
 __global__ __launch_bounds__(256) void gdn_chunk_scan_kernel(
     const int32_t *__restrict__ tree_trunk_len, const float *__restrict__ ws,
     const float *__restrict__ gam, float *__restrict__ ckpt, int H, int chunk, int n_chunks,
     int n_ckpt, int n_pairs) {
-  constexpr int RB = 16, NB = D / RB, KPT = D / 16, LD = D + 4;
-  constexpr int NW4 = CT * D / 4 / 256;  // float4 pieces of a CT x D tile per thread
-  __shared__ __attribute__((aligned(16))) float Wl[CT][LD];
-  __shared__ __attribute__((aligned(16))) float Kl[CT][LD];
-  __shared__ __attribute__((aligned(16))) float Ul[CT][RB];
-  __shared__ __attribute__((aligned(16))) float Sl[RB][LD];
-  __shared__ float Dl[CT][RB + 1];
+  constexpr int RB = 16, NB = D / RB;
+  constexpr int KW = D / 4;   // keys per lane group in the delta product
+  constexpr int NT = D / 64;  // 16-key state tiles per wave
+  __shared__ __attribute__((aligned(16))) float Sl[RB][D + 4];    // S of the block
+  __shared__ __attribute__((aligned(16))) float DlT[RB][CT + 4];  // delta, row-major by value row
 
   const int x8 = blockIdx.x % 8, y8 = blockIdx.x / 8;
   const int vb = y8 % NB, pair = x8 + 8 * (y8 / NB);
   if (pair >= n_pairs) return;
   const int h = pair % H, t = pair / H;
   const int nfull = tree_trunk_len[t] / chunk;  // chunks whose end state is a checkpoint
-  const int tid = threadIdx.x;
-  const int sv = tid % RB, sk0 = (tid / RB) * KPT;  // state owner: row vb*RB + sv, KPT keys
-  const int dsg = tid / RB;                         // delta rows dsg + 16 i of row sv
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
 
   // key-major checkpoint: column k of value row v at k * D + v
+  float *ck = ckpt + ((int64_t)t * n_ckpt * H + h) * (int64_t)D * D + vb * RB;
   const int64_t slot_stride = (int64_t)H * D * D;
-  float *ck = ckpt + ((int64_t)t * n_ckpt * H + h) * (int64_t)D * D + vb * RB + sv;
-  float S[KPT];
+  f32x4 S[NT];
 #pragma unroll
-  for (int kk = 0; kk < KPT; ++kk) {
-    S[kk] = 0.f;
-    Sl[sv][sk0 + kk] = 0.f;
-    ck[(int64_t)(sk0 + kk) * D] = 0.f;  // slot 0: the zero state
-  }
+  for (int j = 0; j < NT; ++j) S[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = tid; i < RB * D; i += 256) Sl[i / D][i % D] = 0.f;
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) ck[(int64_t)(tid / 16 + 16 * i) * D + tid % 16] = 0.f;  // slot 0
 
-  // the next chunk's W, Kd and U columns, in flight in registers
-  float4 pw[NW4], pk[NW4], pu = make_float4(0.f, 0.f, 0.f, 0.f);
+  // one chunk's operands for this lane:
+  //   W[16w + c][g KW ..], KdT[16 (NT w + j) + c][16 g ..], U[16w + 4g + r][vb RB + c], gamma
+  float4 wn[KW / 4], kn[NT][4];
+  float un[4], gn = 0.f;
 #pragma unroll
-  for (int i = 0; i < NW4; ++i) pw[i] = pk[i] = pu;
-#define SPEC_GDN_FETCH(cc)                                                                         \
-  {                                                                                                \
-    const int64_t it_ = ((int64_t)t * n_chunks + (cc)) * H + h;                                    \
-    const float4 *w4_ = reinterpret_cast<const float4 *>(rec_part<D>(ws, it_, RW));                \
-    const float4 *k4_ = reinterpret_cast<const float4 *>(rec_part<D>(ws, it_, RKD));               \
-    _Pragma("unroll") for (int i = 0; i < NW4; ++i) {                                              \
-      pw[i] = w4_[tid + 256 * i];                                                                  \
-      pk[i] = k4_[tid + 256 * i];                                                                  \
-    }                                                                                              \
-    pu = ld4(rec_part<D>(ws, it_, RU) + (tid / 4) * D + vb * RB + (tid % 4) * 4); /* CT x RB */   \
+  for (int i = 0; i < KW / 4; ++i) wn[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kn[j][i] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) un[r] = 0.f;
+#define SPEC_GDN_LOAD(cc)                                                                  \
+  {                                                                                        \
+    const int64_t it_ = ((int64_t)t * n_chunks + (cc)) * H + h;                            \
+    const float *W_ = rec_part<D>(ws, it_, RW) + (16 * w + c) * D + g * KW;                \
+    const float *K_ = rec_part<D>(ws, it_, RKD) + 16 * g;                                  \
+    const float *U_ = rec_part<D>(ws, it_, RU) + (16 * w + 4 * g) * D + vb * RB + c;       \
+    _Pragma("unroll") for (int i = 0; i < KW / 4; ++i) wn[i] = ld4(W_ + 4 * i);            \
+    _Pragma("unroll") for (int j = 0; j < NT; ++j)                                         \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                        \
+        kn[j][i] = ld4(K_ + (16 * (NT * w + j) + c) * CT + 4 * i);                          \
+    _Pragma("unroll") for (int r = 0; r < 4; ++r) un[r] = U_[r * D];                       \
+    gn = gam[it_];                                                                         \
   }
-  if (nfull > 0) SPEC_GDN_FETCH(0)
-  for (int c = 0; c < nfull; ++c) {
+  if (nfull > 0) SPEC_GDN_LOAD(0)
+  for (int ci = 0; ci < nfull; ++ci) {
+    float4 wc[KW / 4], kc[NT][4];
 #pragma unroll
-    for (int i = 0; i < NW4; ++i) {
-      const int e = (tid + 256 * i) * 4;
-      *reinterpret_cast<float4 *>(&Wl[e / D][e % D]) = pw[i];
-      *reinterpret_cast<float4 *>(&Kl[e / D][e % D]) = pk[i];
+    for (int i = 0; i < KW / 4; ++i) wc[i] = wn[i];
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kc[j][i] = kn[j][i];
+    f32x4 d0 = {un[0], un[1], un[2], un[3]}, d1 = {0.f, 0.f, 0.f, 0.f};
+    const float gc = gn;
+    if (ci + 1 < nfull) SPEC_GDN_LOAD(ci + 1)
+    // delta = U - W S^T, two accumulation chains over the keys
+#pragma unroll
+    for (int i = 0; i < KW / 4; ++i) {
+      const float4 sb = ld4(&Sl[c][g * KW + 4 * i]);
+      d0 = __builtin_amdgcn_mfma_f32_16x16x4f32(-wc[i].x, sb.x, d0, 0, 0, 0);
+      d1 = __builtin_amdgcn_mfma_f32_16x16x4f32(-wc[i].y, sb.y, d1, 0, 0, 0);
+      d0 = __builtin_amdgcn_mfma_f32_16x16x4f32(-wc[i].z, sb.z, d0, 0, 0, 0);
+      d1 = __builtin_amdgcn_mfma_f32_16x16x4f32(-wc[i].w, sb.w, d1, 0, 0, 0);
     }
-    *reinterpret_cast<float4 *>(&Ul[tid / 4][(tid % 4) * 4]) = pu;
-    __syncthreads();
-    const float gl = gam[((int64_t)t * n_chunks + c) * H + h];
-    if (c + 1 < nfull) SPEC_GDN_FETCH(c + 1)
-    // delta = U - W S^T for this block's rows
-    float acc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = Ul[dsg + 16 * i][sv];
-#pragma unroll 8
-    for (int k = 0; k < D; k += 4) {
-      const float4 s4 = ld4(&Sl[sv][k]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 w4 = ld4(&Wl[dsg + 16 * i][k]);
-        acc[i] = fmaf(-w4.x, s4.x, acc[i]);
-        acc[i] = fmaf(-w4.y, s4.y, acc[i]);
-        acc[i] = fmaf(-w4.z, s4.z, acc[i]);
-        acc[i] = fmaf(-w4.w, s4.w, acc[i]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Dl[dsg + 16 * i][sv] = acc[i];
+    const f32x4 dl = d0 + d1;  // delta[16w + 4g + r][c]
+    *reinterpret_cast<float4 *>(&DlT[c][16 * w + 4 * g]) = make_float4(dl[0], dl[1], dl[2], dl[3]);
     __syncthreads();
     // S <- gamma S + delta^T Kd
 #pragma unroll
-    for (int kk = 0; kk < KPT; ++kk) S[kk] *= gl;
-#pragma unroll 8
-    for (int s = 0; s < CT; ++s) {
-      const float dl = Dl[s][sv];
+    for (int j = 0; j < NT; ++j) S[j] *= gc;
 #pragma unroll
-      for (int kk = 0; kk < KPT; kk += 4) {
-        const float4 k4 = ld4(&Kl[s][sk0 + kk]);
-        S[kk] = fmaf(dl, k4.x, S[kk]);
-        S[kk + 1] = fmaf(dl, k4.y, S[kk + 1]);
-        S[kk + 2] = fmaf(dl, k4.z, S[kk + 2]);
-        S[kk + 3] = fmaf(dl, k4.w, S[kk + 3]);
+    for (int i = 0; i < 4; ++i) {
+      const float4 da = ld4(&DlT[c][16 * g + 4 * i]);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        S[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(da.x, kc[j][i].x, S[j], 0, 0, 0);
+        S[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(da.y, kc[j][i].y, S[j], 0, 0, 0);
+        S[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(da.z, kc[j][i].z, S[j], 0, 0, 0);
+        S[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(da.w, kc[j][i].w, S[j], 0, 0, 0);
       }
     }
-    float *slot = ck + (c + 1) * slot_stride;
 #pragma unroll
-    for (int kk = 0; kk < KPT; ++kk) {
-      Sl[sv][sk0 + kk] = S[kk];
-      slot[(int64_t)(sk0 + kk) * D] = S[kk];
-    }
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Sl[4 * g + r][16 * (NT * w + j) + c] = S[j][r];
     __syncthreads();
+    // checkpoint ci + 1, 16 consecutive value rows per key
+    float *slot = ck + (int64_t)(ci + 1) * slot_stride;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      const int key = tid / 16 + 16 * i;
+      slot[(int64_t)key * D + tid % 16] = Sl[tid % 16][key];
+    }
   }
-#undef SPEC_GDN_FETCH
+#undef SPEC_GDN_LOAD
 }
 
 // ---------------------------------------------------------------------------
