@@ -16,7 +16,6 @@ Prints one JSON line. Only one GPU is supported (--gpus must be 1).
 from __future__ import annotations
 
 import argparse
-import ctypes
 import hashlib
 import json
 import os
@@ -90,6 +89,7 @@ MARK_KERNELS = {
     "gdn_chunk_scan": (["gdn_chunk_scan_kernel"], ("gdn_chunk.hip", "gdn_util.h")),
     "gdn_chunk_out": (["gdn_chunk_out_kernel"], ("gdn_chunk.hip", "gdn_util.h")),
     "gdn_replay": (["gdn_replay_kernel"], ("gdn.hip", "gdn_util.h")),
+    "gdn_replay_chunk": (["gdn_replay_chunk_kernel"], ("gdn_chunk.hip", "gdn_util.h")),
 }
 
 
@@ -277,16 +277,6 @@ def gdn_work(s, C):
     return int(replay.sum()), int(np.maximum(w - 1, 0).sum())
 
 
-def gdn_trunk_work_bytes(tree, H, D, K, C):
-    import tree_attention_spec_amd as tas
-    lib = tas.library()
-    n = ctypes.c_size_t(0)
-    st = lib.spec_gdn_trunk_fwd(ctypes.byref(tree.layout), H, D, K, C, None, None, None, None, None, None,
-                                None, None, None, ctypes.byref(n), None)
-    assert st == 0
-    return n.value
-
-
 def gdn_flops(s, H, D, C):
     """Algorithmic flops of each GDN kernel (an FMA counts two).
 
@@ -308,6 +298,15 @@ def gdn_flops(s, H, D, C):
     f["gdn_chunk_prep"] = float(H) * float(np.sum(2 * D * tri + 2 * 2 * D * tri))
     f["gdn_chunk_scan"] = float(H) * float(np.sum(2 * 2 * full * D * D))
     f["gdn_chunk_out"] = float(H) * float(np.sum(2 * Ls * D * D))
+    # replay from the cache, per branch (m = W - 1 tokens, j replayed trunk tokens) and head:
+    # the branch chunk's A, P, solve and P X as in prep, then Q' S_c^T (m D^2 FMAs),
+    # Q' K'^T (m j D) and Y Delta (m j D)
+    a = np.asarray(s["anchors"], np.int64)
+    m = np.maximum(np.asarray(s["branch_len"], np.int64) - 1, 0).astype(np.float64)
+    j = (a + 1 - ((a + 1) // C) * C).astype(np.float64)
+    tri_b = m * (m - 1) / 2 + m * (m + 1) / 2
+    f["gdn_replay_chunk"] = float(H) * float(np.sum((m > 0) * (6 * D * tri_b + 2 * m * D * D
+                                                                + 4 * m * j * D)))
     return f
 
 
@@ -335,11 +334,12 @@ def gdn_bench(args, cfg, s, dev):
     x = [t[n] for n in ("xq", "xk", "xv", "taps", "alpha", "beta")]
     ckpt = torch.zeros((tree.n_trees, slots, H, D, D), dtype=torch.float32, device=dev)
     out = torch.zeros((N, H, D), dtype=torch.float32, device=dev)
-    work = torch.empty(gdn_trunk_work_bytes(tree, H, D, K, C), dtype=torch.uint8, device=dev)
+    work = torch.empty(tas.gdn_trunk_work_bytes(tree, H, D, K, C), dtype=torch.uint8, device=dev)
 
     def call():
         tas.spec_gdn_trunk_fwd(tree, *x, chunk=C, ckpt=ckpt, out=out, work=work)
-        tas.spec_gdn_replay_fwd(tree, *x, ckpt=ckpt, chunk=C, out=out)
+        tas.spec_gdn_replay_fwd(tree, *x, ckpt=ckpt, chunk=C, out=out,
+                                trunk_work=None if args.gdn_token_replay else work)
 
     for _ in range(args.warmup):
         call()
@@ -362,8 +362,8 @@ def gdn_bench(args, cfg, s, dev):
     tf = {k: flop[k] / (kms[k] * 1e-3) / 1e12 for k in kms}
     for k in kms:
         log("%s %.4f ms (%.1f TFLOP/s)" % (k, kms[k], tf[k]))
-    log("trunk pass %.4f ms, replay %.4f ms" % (sum(v for k, v in kms.items() if k != "gdn_replay"),
-                                               kms["gdn_replay"]))
+    rk = "gdn_replay" if args.gdn_token_replay else "gdn_replay_chunk"
+    log("trunk pass %.4f ms, replay %.4f ms" % (sum(v for k, v in kms.items() if k != rk), kms[rk]))
     log("per head: %d trunk tokens, %d replayed + %d branch tokens" % (n_trunk, n_replay, n_branch))
     dom = max(kms, key=kms.get)
     return {
@@ -449,6 +449,8 @@ def main():
     ap.add_argument("--gdn", action="store_true",
                     help="time GDN scoring of the workload's tree (spec_gdn_trunk_fwd, then spec_gdn_replay_fwd) "
                          "instead of the attention + E2E-TV step, and print its own JSON line")
+    ap.add_argument("--gdn-token-replay", action="store_true",
+                    help="with --gdn: replay a token at a time instead of from the trunk pass's cache")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM counters) and exit")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DB",

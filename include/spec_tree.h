@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define SPEC_TREE_ABI_VERSION 3
+#define SPEC_TREE_ABI_VERSION 4
 #define SPEC_MAX_BRANCH_LEN 64 /* largest supported branch width W_b */
 
 typedef enum spec_status {
@@ -269,19 +269,29 @@ spec_status spec_e2etv_fwd_bwd(const spec_tree_layout *layout, int64_t vocab,
  *   d_ckpt      [n_trees, max_trunk_len / chunk + 1, H, D, D] float32, each
  *               state stored key-major (S_ij at j * D + i); slots a shorter
  *               tree never reaches are not read.
+ *   d_trunk_work  NULL, or the workspace of the spec_gdn_trunk_fwd call (same
+ *               layout, H, D, K and chunk <= 64) that wrote d_ckpt, unchanged
+ *               since. With it the replay runs a chunk at a time: the trunk
+ *               pass's per-token deltas of the anchor's chunk stand in for the
+ *               replayed trunk tokens (S after the anchor = e^G S_c + sum of
+ *               their decayed rank-one updates), and the branch's tokens form
+ *               one more chunk (same result up to float32 rounding). Without it
+ *               one workgroup per (branch, head, row block) walks the tokens one
+ *               at a time.
  *   d_out       [N, H, D] float32: the rows of branches are written; trunk
  *               rows are left as they are (the trunk pass owns them).
- * All buffers are the caller's; the call needs no workspace and allocates
- * nothing. Data preconditions (not checked): inputs finite; the convolved q
- * and k of every replayed token are not all zero (their norms divide).
- * Errors: SPEC_ERR_INVALID_ARG, SPEC_ERR_UNSUPPORTED (head_dim, conv_width),
- * SPEC_ERR_HIP.
+ * All buffers are the caller's; the call allocates nothing. Data
+ * preconditions (not checked): inputs finite; the convolved q and k of every
+ * replayed token are not all zero (their norms divide).
+ * Errors: SPEC_ERR_INVALID_ARG (also a trunk cache with chunk > 64),
+ * SPEC_ERR_UNSUPPORTED (head_dim, conv_width), SPEC_ERR_HIP.
  */
 spec_status spec_gdn_replay_fwd(const spec_tree_layout *layout, int32_t n_heads,
                                 int32_t head_dim, int32_t conv_width, int32_t chunk,
                                 const void *d_xq, const void *d_xk, const void *d_xv,
                                 const float *d_taps, const float *d_alpha, const float *d_beta,
-                                const float *d_ckpt, float *d_out, spec_stream stream);
+                                const float *d_ckpt, const void *d_trunk_work, float *d_out,
+                                spec_stream stream);
 
 /*
  * spec_gdn_trunk_fwd -- the shared trunk pass of GDN scoring: the GDN outputs
@@ -307,7 +317,8 @@ spec_status spec_gdn_replay_fwd(const spec_tree_layout *layout, int32_t n_heads,
  *   d_out       [N, H, D] float32; trunk rows written.
  *   d_work      workspace of *work_bytes bytes (16-byte aligned), or NULL for a
  *               size query (then nothing else is read). The chunked pass keeps
- *               five 64 x D float32 tiles per (tree, chunk, head) there.
+ *               seven 64 x D float32 tiles and 65 floats per (tree, chunk, head)
+ *               there; spec_gdn_replay_fwd can read them (d_trunk_work).
  * Calls that share a workspace must not overlap in time.
  * Errors: as spec_gdn_replay_fwd, plus SPEC_ERR_WORKSPACE.
  */

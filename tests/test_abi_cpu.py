@@ -162,7 +162,7 @@ def test_gdn_argument_checks(tas):
     P = ctypes.c_void_p(0x1000)
 
     def call(H, D, K, C, p=P):
-        return lib.spec_gdn_replay_fwd(ctypes.byref(L), H, D, K, C, p, p, p, p, p, p, p, p, None)
+        return lib.spec_gdn_replay_fwd(ctypes.byref(L), H, D, K, C, p, p, p, p, p, p, p, None, p, None)
 
     assert call(32, 128, 4, 64) == 1                # the layout has no device arrays yet
     fake = ctypes.cast(ctypes.c_void_p(0x1000), _lib._i32p)
@@ -193,10 +193,10 @@ def test_gdn_trunk_argument_checks(tas):
                                     None, None, None, ctypes.byref(n), None)
         return st, n.value
 
-    # five 64 x D float32 tiles per (tree, chunk, head), plus one float each, rounded to 256 B
+    # seven 64 x D float32 tiles per (tree, chunk, head), then 64 + 1 floats each, rounded to 256 B
     chunks = -(-CONFIGS["gqa8b"].trunk // 64)
     items = chunks * 32
-    assert query(32, 128, 64) == (0, items * 5 * 64 * 128 * 4 + -(-items * 4 // 256) * 256)
+    assert query(32, 128, 64) == (0, -(-(items * 7 * 64 * 128 + items * 65) * 4 // 256) * 256)
     assert query(32, 128, 128) == (0, 256)          # the token-at-a-time pass keeps nothing
     assert query(32, 96, 64)[0] == 1
     assert query(32, 128, 0)[0] == 1

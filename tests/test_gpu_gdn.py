@@ -137,13 +137,18 @@ def _trunk_compare(s, H, D, K, C, seed, heads=None):
     slots = tas.gdn_checkpoint_slots(tree, C)
     ck_g = torch.full((lay["n_trees"], slots, H, D, D), 5.0, dtype=torch.float32, device="cuda")
     out_g = torch.full((lay["n_rows"], H, D), 7.0, dtype=torch.float32, device="cuda")
-    tas.spec_gdn_trunk_fwd(tree, *x, chunk=C, ckpt=ck_g, out=out_g)
+    work = torch.empty(tas.gdn_trunk_work_bytes(tree, H, D, K, C), dtype=torch.uint8, device="cuda")
+    tas.spec_gdn_trunk_fwd(tree, *x, chunk=C, ckpt=ck_g, out=out_g, work=work)
     trunk_out = out_g.clone()
-    tas.spec_gdn_replay_fwd(tree, *x, ckpt=ck_g, chunk=C, out=out_g)
+    tas.spec_gdn_replay_fwd(tree, *x, ckpt=ck_g, chunk=C, out=out_g)              # token at a time
+    outs = [out_g]
+    if C <= 64:                                                                 # from the trunk cache
+        out_c = trunk_out.clone()
+        tas.spec_gdn_replay_fwd(tree, *x, ckpt=ck_g, chunk=C, out=out_c, trunk_work=work)
+        outs.append(out_c)
     torch.cuda.synchronize()
     ck = np.swapaxes(ck_g.cpu().numpy().astype(np.float64), -1, -2)            # value-major, as the oracle
     trunk_got = trunk_out.cpu().numpy().astype(np.float64)
-    got = out_g.cpu().numpy().astype(np.float64)
 
     hs = list(range(H)) if heads is None else list(heads)
     sub = lambda a: np.ascontiguousarray(a[:, hs])
@@ -169,15 +174,17 @@ def _trunk_compare(s, H, D, K, C, seed, heads=None):
         assert cerr <= GDN_RTOL * cs
         assert np.all(ck[ti, 0] == 0.0)
         assert np.all(ck[ti, reach:] == 5.0)
-    # the replay from the GPU's checkpoints against the oracle's chained path
+    # both replays from the GPU's checkpoints against the oracle's chained path
     br = lay["row_branch"] >= 0
-    if br.any():
-        want = gdn_replay_ref(lay, q, k, v, al, be, ck_ref, C)
-        bs = np.abs(want[br]).max()
-        berr = np.abs(got[:, hs][br] - want[br]).max()
-        say("  chained replay: max abs err %.3e (max |o| %.3e)" % (berr, bs))
-        assert berr <= 2 * GDN_RTOL * bs
-    assert np.array_equal(got[tr], trunk_got[tr])                               # the replay leaves trunk rows
+    want = gdn_replay_ref(lay, q, k, v, al, be, ck_ref, C) if br.any() else None
+    for name, o in zip(("token-at-a-time", "cached"), outs):
+        got = o.cpu().numpy().astype(np.float64)
+        if br.any():
+            bs = np.abs(want[br]).max()
+            berr = np.abs(got[:, hs][br] - want[br]).max()
+            say("  %s replay: max abs err %.3e (max |o| %.3e)" % (name, berr, bs))
+            assert berr <= 2 * GDN_RTOL * bs
+        assert np.array_equal(got[tr], trunk_got[tr])                           # the replay leaves trunk rows
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
@@ -196,6 +203,27 @@ def test_gdn_trunk_edges():
     s = dict(trunk_len=np.array([1, 16, 15, 33], np.int32), n_branches=np.array([1, 2, 0, 1], np.int32),
              anchors=np.array([0, 15, 3, 32], np.int32), branch_len=np.array([3, 2, 4, 5], np.int32))
     _trunk_compare(s, 2, 64, 4, 16, seed=77)
+
+
+CACHE_CASES = [
+    # (tag, trunk lengths, anchors, widths, H, D, K, C): widths past 17 and 33 take the 32- and
+    # 64-row branch tiles; anchors at cC - 1 (nothing to replay), cC (one token), cC + C - 2
+    # (63 tokens) and in a last partial chunk
+    ("w20_d128", [200], [63, 64, 126, 190, 5], [20, 18, 3, 20, 1], 2, 128, 4, 64),
+    ("w40_d64", [150], [0, 63, 127, 149, 100], [40, 34, 2, 40, 33], 2, 64, 3, 64),
+    ("w64_d128", [130], [64, 129, 10], [64, 64, 17], 1, 128, 2, 64),
+    ("c16_two_trees", [40, 70], [15, 16, 39, 0, 47, 69], [9, 5, 16, 2, 12, 7], 2, 64, 4, 16),
+]
+
+
+@pytest.mark.parametrize("case", CACHE_CASES, ids=[c[0] for c in CACHE_CASES])
+def test_gdn_replay_from_trunk_cache(case):
+    tag, T, anchors, widths, H, D, K, C = case
+    say("gdn replay from the trunk cache: %s" % tag)
+    nb = [len(anchors)] if len(T) == 1 else [3, 3]
+    s = dict(trunk_len=np.array(T, np.int32), n_branches=np.array(nb, np.int32),
+             anchors=np.array(anchors, np.int32), branch_len=np.array(widths, np.int32))
+    _trunk_compare(s, H, D, K, C, seed=len(tag) + 7)
 
 
 def test_gdn_trunk_token_at_a_time():

@@ -20,7 +20,7 @@ from ._lib import (LAYOUT_ARRAYS, SPEC_BF16, SPEC_F32, SPEC_MAX_BRANCH_LEN, Spec
                    spec_tree_layout)
 
 __all__ = ["spec_tree_pack", "spec_tree_pack_query", "spec_tree_attn_fwd", "spec_e2etv_fwd_bwd",
-           "spec_gdn_trunk_fwd", "spec_gdn_replay_fwd", "gdn_checkpoint_slots", "PackedTree", "SpecError", "library",
+           "spec_gdn_trunk_fwd", "spec_gdn_replay_fwd", "gdn_checkpoint_slots", "gdn_trunk_work_bytes", "PackedTree", "SpecError", "library",
            "KernelTimer"]
 
 _LIB = None
@@ -216,6 +216,17 @@ def gdn_checkpoint_slots(tree: PackedTree, chunk: int) -> int:
     return tree.max_trunk_len // chunk + 1
 
 
+def gdn_trunk_work_bytes(tree: PackedTree, n_heads: int, head_dim: int, conv_width: int,
+                         chunk: int) -> int:
+    """Bytes of the workspace spec_gdn_trunk_fwd needs (a size query; no GPU work)."""
+    lib = library()
+    n = ctypes.c_size_t(0)
+    _lib.check(lib, lib.spec_gdn_trunk_fwd(ctypes.byref(tree.layout), n_heads, head_dim, conv_width,
+                                           chunk, None, None, None, None, None, None, None, None, None,
+                                           ctypes.byref(n), None))
+    return n.value
+
+
 def _check_gdn(tree, xq, xk, xv, taps, alpha, beta, chunk):
     N, H, D = xq.shape
     if xk.shape != (N, H, D) or xv.shape != (N, H, D) or N != tree.n_rows:
@@ -257,11 +268,11 @@ def spec_gdn_trunk_fwd(tree: PackedTree, xq: torch.Tensor, xk: torch.Tensor, xv:
         out = torch.zeros((N, H, D), dtype=torch.float32, device=xq.device)
     lib = library()
     ptr = lambda t: ctypes.c_void_p(t.data_ptr())
-    nbytes = ctypes.c_size_t(0)
-    _lib.check(lib, lib.spec_gdn_trunk_fwd(ctypes.byref(tree.layout), H, D, K, chunk, None, None, None,
-                                           None, None, None, None, None, None, ctypes.byref(nbytes), None))
+    nbytes = ctypes.c_size_t(gdn_trunk_work_bytes(tree, H, D, K, chunk))
     if work is None or work.numel() < nbytes.value:
         work = torch.empty(nbytes.value, dtype=torch.uint8, device=xq.device)
+    elif work.device != xq.device or not work.is_contiguous():
+        raise ValueError("work must be a contiguous tensor on the inputs' device")
     st = lib.spec_gdn_trunk_fwd(ctypes.byref(tree.layout), H, D, K, chunk, ptr(xq), ptr(xk), ptr(xv),
                                 ptr(taps), ptr(alpha), ptr(beta), ptr(ckpt), ptr(out), ptr(work),
                                 ctypes.byref(nbytes), ctypes.c_void_p(_stream(xq.device)))
@@ -271,13 +282,17 @@ def spec_gdn_trunk_fwd(tree: PackedTree, xq: torch.Tensor, xk: torch.Tensor, xv:
 
 def spec_gdn_replay_fwd(tree: PackedTree, xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor,
                         taps: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
-                        ckpt: torch.Tensor, chunk: int = 64, out: torch.Tensor = None):
+                        ckpt: torch.Tensor, chunk: int = 64, out: torch.Tensor = None,
+                        trunk_work: torch.Tensor = None):
     """Indexed GDN state replay for the branch rows.
 
     xq/xk/xv [N,H,D] bf16, taps [3,H,D,K] fp32, alpha/beta [N,H] fp32, ckpt
     [n_trees, slots, H, D, D] fp32 (key-major states, slots = gdn_checkpoint_slots,
-    as spec_gdn_trunk_fwd writes them). Returns out [N,H,D] fp32 with the branch
-    rows written (trunk rows as passed in, zero for a new tensor).
+    as spec_gdn_trunk_fwd writes them). ``trunk_work``: the workspace of the
+    spec_gdn_trunk_fwd call that wrote ``ckpt`` (chunk <= 64), unchanged since;
+    the replay then runs a chunk at a time from its cache. Without it the replay
+    walks the tokens one at a time. Returns out [N,H,D] fp32 with the branch rows
+    written (trunk rows as passed in, zero for a new tensor).
     """
     N, H, D, K, ck_shape = _check_gdn(tree, xq, xk, xv, taps, alpha, beta, chunk)
     if ckpt.shape != ck_shape or ckpt.dtype != torch.float32 or not ckpt.is_contiguous():
@@ -286,8 +301,11 @@ def spec_gdn_replay_fwd(tree: PackedTree, xq: torch.Tensor, xk: torch.Tensor, xv
         out = torch.zeros((N, H, D), dtype=torch.float32, device=xq.device)
     lib = library()
     ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    if trunk_work is not None and (trunk_work.device != xq.device or not trunk_work.is_contiguous()):
+        raise ValueError("trunk_work must be a contiguous tensor on the inputs' device")
     st = lib.spec_gdn_replay_fwd(ctypes.byref(tree.layout), H, D, K, chunk, ptr(xq), ptr(xk), ptr(xv),
-                                 ptr(taps), ptr(alpha), ptr(beta), ptr(ckpt), ptr(out),
+                                 ptr(taps), ptr(alpha), ptr(beta), ptr(ckpt),
+                                 None if trunk_work is None else ptr(trunk_work), ptr(out),
                                  ctypes.c_void_p(_stream(xq.device)))
     _lib.check(lib, st)
     return out

@@ -117,7 +117,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_gdn_replay_fwd.restype = c.c_int
     lib.spec_gdn_replay_fwd.argtypes = [c.POINTER(spec_tree_layout), c.c_int32, c.c_int32, c.c_int32,
                                         c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
-                                        c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p]
+                                        c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
+                                        c.c_void_p]
     lib.spec_status_string.restype = c.c_char_p
     lib.spec_status_string.argtypes = [c.c_int]
     lib.spec_last_error.restype = c.c_char_p

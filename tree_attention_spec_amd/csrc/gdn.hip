@@ -40,6 +40,11 @@ hipError_t launch_gdn_chunked(const spec_tree_layout &L, int H, int D, int K, in
                               const void *xq, const void *xk, const void *xv, const float *taps,
                               const float *alpha, const float *beta, float *ckpt, float *out,
                               void *work, hipStream_t s);
+hipError_t launch_gdn_replay_chunked(const spec_tree_layout &L, int H, int D, int K, int chunk,
+                                     int n_ckpt, const void *xq, const void *xk, const void *xv,
+                                     const float *taps, const float *alpha, const float *beta,
+                                     const float *ckpt, const void *work, float *out,
+                                     hipStream_t s);
 
 namespace {
 
@@ -378,7 +383,8 @@ spec_status check_gdn(const spec_tree_layout *layout, bool trunk, int32_t n_head
 spec_status run_gdn(bool trunk, const spec_tree_layout *layout, int32_t n_heads, int32_t head_dim,
                     int32_t conv_width, int32_t chunk, const void *d_xq, const void *d_xk,
                     const void *d_xv, const float *d_taps, const float *d_alpha, const float *d_beta,
-                    float *d_ckpt, float *d_out, void *d_work, size_t *work_bytes, spec_stream stream) {
+                    float *d_ckpt, float *d_out, void *d_work, size_t *work_bytes, spec_stream stream,
+                    const void *d_trunk_work = nullptr) {
   clear_error();
   if (trunk && !work_bytes) return fail(SPEC_ERR_INVALID_ARG, "work_bytes must be non-NULL");
   if (trunk && !d_work) {  // size query
@@ -413,6 +419,19 @@ spec_status run_gdn(bool trunk, const spec_tree_layout *layout, int32_t n_heads,
     if (e != hipSuccess) return hip_fail(e, "chunkwise GDN trunk pass launch");
     return SPEC_OK;
   }
+  if (!trunk && d_trunk_work) {  // the replay from the trunk pass's cache
+    if (chunk > 64)
+      return fail(SPEC_ERR_INVALID_ARG, "a trunk-pass cache exists only for chunk <= 64 (got %d)", chunk);
+    if (!aligned16(d_trunk_work)) return fail(SPEC_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+    if (L.max_branch_len > 65) return fail(SPEC_ERR_UNSUPPORTED, "branches longer than 65 tokens");
+    prof_mark(s, "gdn:begin");
+    const hipError_t e = launch_gdn_replay_chunked(L, n_heads, head_dim, conv_width, chunk, n_ckpt, d_xq,
+                                                   d_xk, d_xv, d_taps, d_alpha, d_beta, d_ckpt,
+                                                   d_trunk_work, d_out, s);
+    if (e != hipSuccess) return hip_fail(e, "gdn_replay_chunk_kernel launch");
+    prof_mark(s, "gdn_replay_chunk");
+    return SPEC_OK;
+  }
   prof_mark(s, trunk ? "gdn_trunk:begin" : "gdn:begin");
   hipError_t e;
   if (trunk)
@@ -440,11 +459,12 @@ extern "C" spec_status spec_gdn_replay_fwd(const spec_tree_layout *layout, int32
                                            int32_t head_dim, int32_t conv_width, int32_t chunk,
                                            const void *d_xq, const void *d_xk, const void *d_xv,
                                            const float *d_taps, const float *d_alpha,
-                                           const float *d_beta, const float *d_ckpt, float *d_out,
+                                           const float *d_beta, const float *d_ckpt,
+                                           const void *d_trunk_work, float *d_out,
                                            spec_stream stream) {
-  // the replay only reads the checkpoints
+  // the replay only reads the checkpoints (and the trunk pass's cache)
   return run_gdn(false, layout, n_heads, head_dim, conv_width, chunk, d_xq, d_xk, d_xv, d_taps, d_alpha,
-                 d_beta, const_cast<float *>(d_ckpt), d_out, nullptr, nullptr, stream);
+                 d_beta, const_cast<float *>(d_ckpt), d_out, nullptr, nullptr, stream, d_trunk_work);
 }
 
 extern "C" spec_status spec_gdn_trunk_fwd(const spec_tree_layout *layout, int32_t n_heads,

@@ -26,7 +26,20 @@
 //        as the next checkpoint.
 //   out  (tree, chunk, head): o = Q' S_c^T + O' from checkpoint c.
 // A chunk tile always has 64 rows; rows past the chunk's tokens are zero.
-// Intermediates live in a caller-provided workspace.
+// Intermediates live in a caller-provided workspace, which also keeps, per
+// chunk, the deltas, the normalised keys and g for the branch replay below.
+//
+// Branch replay from that cache ([SpecOPD paper page, Figure 5]: a branch
+// copies the checkpoint at or below its anchor a, replays the trunk tokens
+// after it through a, then takes its own tokens). With c = floor((a+1)/C) and
+// j = a + 1 - cC replayed tokens of chunk c, the state after the anchor is
+//   S_a = e^{G} S_c + sum_{r<j} e^{G - g_r} delta_r k_r^T,   G = g_{j-1},
+// where delta_r are chunk c's own deltas (they depend only on tokens before r).
+// The branch's m = W - 1 tokens are one more chunk that starts from S_a: with
+// its Q', O' from the same in-chunk algebra, its outputs are
+//   o = Q' S_a^T + O' = e^{G} Q' S_c^T + (Q' K'^T) Delta + O',  K'_r = e^{G - g_r} k_r,
+// three small products on the fp32 matrix cores; S_a is never formed. One
+// workgroup per (branch, head) does it all (gdn_replay_chunk_kernel).
 #include "common.h"
 #include "gdn_util.h"
 
@@ -38,8 +51,13 @@ using gdn::silu_f;
 using gdn::wave_sum;
 
 constexpr int CT = 64;    // rows of a chunk tile (the chunk length is at most this)
-constexpr int NREC = 5;   // per (tree, chunk, head): W, U, Kd, Q', O', each CT x D
-enum { RW = 0, RU = 1, RKD = 2, RQ = 3, RO = 4 };
+constexpr int NREC = 7;   // per (tree, chunk, head): W, U, Kd, Q', O', delta, k~; each CT x D
+enum { RW = 0, RU = 1, RKD = 2, RQ = 3, RO = 4, RDL = 5, RKF = 6 };
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ inline f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 __device__ inline float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 
@@ -53,38 +71,36 @@ __device__ inline const float *rec_part(const float *ws, int64_t item, int part)
 }
 
 // ---------------------------------------------------------------------------
-// prep: one workgroup of 256 per (tree, chunk, head), item = (t * n_chunks + c) * H + h.
-template <int D, int K>
-__global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(
-    const int32_t *__restrict__ tree_off, const int32_t *__restrict__ tree_trunk_len,
-    const __bf16 *__restrict__ xq, const __bf16 *__restrict__ xk, const __bf16 *__restrict__ xv,
-    const float *__restrict__ taps, const float *__restrict__ alpha,
-    const float *__restrict__ beta, float *__restrict__ ws, float *__restrict__ gam, int H,
-    int chunk, int n_chunks) {
-  constexpr int LD = D + 4;  // padded rows: 16 consecutive rows start 4 banks apart
-  __shared__ __attribute__((aligned(16))) float kf[CT][LD];
-  __shared__ __attribute__((aligned(16))) float qf[CT][LD];
-  __shared__ __attribute__((aligned(16))) float vf[CT][D];
-  __shared__ __attribute__((aligned(16))) float Al[CT][CT + 4];
-  __shared__ __attribute__((aligned(16))) float Pl[CT][CT + 4];
-  __shared__ float g[CT], eg[CT], bt[CT], nk[CT], nq[CT];
+// The in-chunk algebra shared by the trunk prep and the branch replay: MT rows
+// (16, 32 or 64), 256 threads.
+// The arrays that unrolled code reads at many fixed offsets come first, so
+// that their addresses fit the 16-bit offset field of an LDS instruction.
+template <int D, int MT>
+struct ChunkLds {
+  float Al[MT][MT + 4];
+  float Pl[MT][MT + 4];
+  float g[64], eg[64], bt[64];  // running log decay, its exponential, beta
+  float nk[MT], nq[MT];
+  float kf[MT][D + 4];  // k~ (padded rows: 16 consecutive rows start 4 banks apart)
+  float qf[MT][D + 4];  // q~
+  float vf[MT][D + 4];  // v~ (padded like k~, so a column has one stride)
+};
 
-  const int64_t item = blockIdx.x;
-  const int h = (int)(item % H);
-  const int c = (int)((item / H) % n_chunks);
-  const int t = (int)(item / ((int64_t)H * n_chunks));
-  const int T = tree_trunk_len[t];
-  const int p0 = c * chunk;  // trunk position of the tile's row 0
-  if (p0 >= T) return;       // workgroup-uniform, before any barrier
-  const int L = min(chunk, T - p0);
-  const int off = tree_off[t];
+// Features of the tile's tokens: token s is path position P0 + s (s < L), the
+// convolution reads positions P0 + s - j, and row_of maps a position to its
+// packed row. Thread (d, group) takes channel d of MT / G consecutive tokens;
+// the raw rows they read (K - 1 more before the first) are loaded in one batch.
+// Then the gates (a wave scan of log alpha; alpha = 1, beta = 0 past L), the
+// norms, and k~ and q~ scaled in place. Ends with a barrier.
+template <int D, int K, int MT, class RowOf>
+__device__ __forceinline__ void chunk_features(ChunkLds<D, MT> &sm, RowOf row_of, int P0, int L,
+                                      const __bf16 *__restrict__ xq, const __bf16 *__restrict__ xk,
+                                      const __bf16 *__restrict__ xv, const float *__restrict__ taps,
+                                      const float *__restrict__ alpha,
+                                      const float *__restrict__ beta, int H, int h) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-
-  // features before the norms: the convolution along the trunk, then SiLU.
-  // Thread (d, group) takes channel d of CT / G consecutive tokens; the raw
-  // rows they read (K - 1 more before the first) are all loaded up front.
   {
-    constexpr int G = 256 / D, TPG = CT / G, NR = TPG + K - 1;
+    constexpr int G = 256 / D, TPG = MT / G, NR = TPG + K - 1;
     const int d = tid % D, s0 = (tid / D) * TPG;
     float tq[K], tk[K], tv[K];
 #pragma unroll
@@ -95,10 +111,10 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(
     }
     float rq[NR], rk[NR], rv[NR];
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {  // raw row i is trunk position p0 + s0 - (K - 1) + i
-      const int p = p0 + s0 - (K - 1) + i;
-      const bool ok = p >= 0 && p < p0 + L;
-      const int64_t at = ((int64_t)(off + (ok ? p : 0)) * H + h) * D + d;
+    for (int i = 0; i < NR; ++i) {  // raw row i is position P0 + s0 - (K - 1) + i
+      const int p = P0 + s0 - (K - 1) + i;
+      const bool ok = p >= 0 && p < P0 + L;
+      const int64_t at = ((int64_t)row_of(ok ? p : P0) * H + h) * D + d;
       const float q = (float)xq[at], k = (float)xk[at], v = (float)xv[at];
       rq[i] = ok ? q : 0.f;
       rk[i] = ok ? k : 0.f;
@@ -108,22 +124,21 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(
     for (int s = 0; s < TPG; ++s) {
       float aq = 0.f, ak = 0.f, av = 0.f;
 #pragma unroll
-      for (int j = 0; j < K; ++j) {  // tap j reads position p0 + s0 + s - j
+      for (int j = 0; j < K; ++j) {  // tap j reads position P0 + s0 + s - j
         aq = fmaf(tq[j], rq[s + K - 1 - j], aq);
         ak = fmaf(tk[j], rk[s + K - 1 - j], ak);
         av = fmaf(tv[j], rv[s + K - 1 - j], av);
       }
       const bool live = s0 + s < L;
-      qf[s0 + s][d] = live ? silu_f(aq) : 0.f;
-      kf[s0 + s][d] = live ? silu_f(ak) : 0.f;
-      vf[s0 + s][d] = live ? silu_f(av) : 0.f;
+      sm.qf[s0 + s][d] = live ? silu_f(aq) : 0.f;
+      sm.kf[s0 + s][d] = live ? silu_f(ak) : 0.f;
+      sm.vf[s0 + s][d] = live ? silu_f(av) : 0.f;
     }
   }
-  // gates: running sum of log alpha (a wave scan); rows past L have alpha = 1, beta = 0
   if (wv == 0) {
     float la = 0.f, b = 0.f;
     if (lane < L) {
-      const int64_t gi = (int64_t)(off + p0 + lane) * H + h;
+      const int64_t gi = (int64_t)row_of(P0 + lane) * H + h;
       la = __logf(alpha[gi]);
       b = beta[gi];
     }
@@ -132,138 +147,184 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(
       const float y = __shfl_up(la, o);
       if (lane >= o) la += y;
     }
-    g[lane] = la;
-    eg[lane] = __expf(la);
-    bt[lane] = b;
+    sm.g[lane] = la;
+    sm.eg[lane] = __expf(la);
+    sm.bt[lane] = b;
   }
   __syncthreads();
-  // L2 norms of k and q per token (wave wv takes tokens wv, wv + 4, ...)
   const float qscale = 1.f / sqrtf((float)D);
-  for (int s = wv; s < CT; s += 4) {
+  for (int s = wv; s < MT; s += 4) {
     float sk = 0.f, sq = 0.f;
 #pragma unroll
     for (int d = lane; d < D; d += 64) {
-      sk = fmaf(kf[s][d], kf[s][d], sk);
-      sq = fmaf(qf[s][d], qf[s][d], sq);
+      sk = fmaf(sm.kf[s][d], sm.kf[s][d], sk);
+      sq = fmaf(sm.qf[s][d], sm.qf[s][d], sq);
     }
     sk = wave_sum(sk);
     sq = wave_sum(sq);
     if (lane == 0) {
-      nk[s] = s < L ? __builtin_amdgcn_rsqf(sk) : 0.f;
-      nq[s] = s < L ? qscale * __builtin_amdgcn_rsqf(sq) : 0.f;
+      sm.nk[s] = s < L ? __builtin_amdgcn_rsqf(sk) : 0.f;
+      sm.nq[s] = s < L ? qscale * __builtin_amdgcn_rsqf(sq) : 0.f;
     }
   }
   __syncthreads();
-  for (int i = tid; i < CT * D; i += 256) {
+  for (int i = tid; i < MT * D; i += 256) {
     const int s = i / D, d = i % D;
-    kf[s][d] *= nk[s];
-    qf[s][d] *= nq[s];
+    sm.kf[s][d] *= sm.nk[s];
+    sm.qf[s][d] *= sm.nq[s];
   }
   __syncthreads();
+}
 
-  // A_sr (r < s) and P_sr (r <= s): lane r holds k_r in 32-column pieces, wave
-  // wv takes rows s = 16 wv .. 16 wv + 15, whose k_s and q_s are LDS broadcasts.
-  {
-    const int r = lane;
-    float accA[16], accP[16];
+// A_sr = e^{g_s-g_r} k_s.k_r (r < s) and P_sr = e^{g_s-g_r} q_s.k_r (r <= s):
+// lane r % MT holds k_r in 32-column pieces and each group of MT threads takes
+// MT * MT / 256 rows s, whose k_s and q_s are LDS broadcasts. Ends with a barrier.
+template <int D, int MT>
+__device__ __forceinline__ void chunk_ap(ChunkLds<D, MT> &sm) {
+  constexpr int RPG = MT * MT / 256;  // rows s per group
+  const int tid = threadIdx.x;
+  const int r = tid % MT, s0 = (tid / MT) * RPG;
+  float accA[RPG], accP[RPG];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) accA[i] = accP[i] = 0.f;
+  for (int i = 0; i < RPG; ++i) accA[i] = accP[i] = 0.f;
 #pragma unroll 1
-    for (int d0 = 0; d0 < D; d0 += 32) {
-      float kr[32];
+  for (int d0 = 0; d0 < D; d0 += 32) {
+    float kr[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 x = ld4(&sm.kf[r][d0 + 4 * i]);
+      kr[4 * i] = x.x;
+      kr[4 * i + 1] = x.y;
+      kr[4 * i + 2] = x.z;
+      kr[4 * i + 3] = x.w;
+    }
+#pragma unroll
+    for (int si = 0; si < RPG; ++si) {
+      const int s = s0 + si;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float4 x = ld4(&kf[r][d0 + 4 * i]);
-        kr[4 * i] = x.x;
-        kr[4 * i + 1] = x.y;
-        kr[4 * i + 2] = x.z;
-        kr[4 * i + 3] = x.w;
+        const float4 ks = ld4(&sm.kf[s][d0 + 4 * i]);
+        const float4 qs = ld4(&sm.qf[s][d0 + 4 * i]);
+        accA[si] = fmaf(ks.x, kr[4 * i], accA[si]);
+        accA[si] = fmaf(ks.y, kr[4 * i + 1], accA[si]);
+        accA[si] = fmaf(ks.z, kr[4 * i + 2], accA[si]);
+        accA[si] = fmaf(ks.w, kr[4 * i + 3], accA[si]);
+        accP[si] = fmaf(qs.x, kr[4 * i], accP[si]);
+        accP[si] = fmaf(qs.y, kr[4 * i + 1], accP[si]);
+        accP[si] = fmaf(qs.z, kr[4 * i + 2], accP[si]);
+        accP[si] = fmaf(qs.w, kr[4 * i + 3], accP[si]);
       }
-#pragma unroll
-      for (int si = 0; si < 16; ++si) {
-        const int s = 16 * wv + si;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float4 ks = ld4(&kf[s][d0 + 4 * i]);
-          const float4 qs = ld4(&qf[s][d0 + 4 * i]);
-          accA[si] = fmaf(ks.x, kr[4 * i], accA[si]);
-          accA[si] = fmaf(ks.y, kr[4 * i + 1], accA[si]);
-          accA[si] = fmaf(ks.z, kr[4 * i + 2], accA[si]);
-          accA[si] = fmaf(ks.w, kr[4 * i + 3], accA[si]);
-          accP[si] = fmaf(qs.x, kr[4 * i], accP[si]);
-          accP[si] = fmaf(qs.y, kr[4 * i + 1], accP[si]);
-          accP[si] = fmaf(qs.z, kr[4 * i + 2], accP[si]);
-          accP[si] = fmaf(qs.w, kr[4 * i + 3], accP[si]);
-        }
-        __builtin_amdgcn_sched_barrier(0);  // keeps the broadcast reads near their FMAs
-      }
+      __builtin_amdgcn_sched_barrier(0);  // keeps the broadcast reads near their FMAs
     }
+  }
 #pragma unroll
-    for (int si = 0; si < 16; ++si) {
-      const int s = 16 * wv + si;
-      const float e = __expf(g[s] - g[r]);  // used only where r <= s, so e <= 1
-      Al[s][r] = r < s ? e * accA[si] : 0.f;
-      Pl[s][r] = r <= s ? e * accP[si] : 0.f;
-    }
+  for (int si = 0; si < RPG; ++si) {
+    const int s = s0 + si;
+    const float e = __expf(sm.g[s] - sm.g[r]);  // used only where r <= s, so e <= 1
+    sm.Al[s][r] = r < s ? e * accA[si] : 0.f;
+    sm.Pl[s][r] = r <= s ? e * accP[si] : 0.f;
   }
   __syncthreads();
+}
 
-  // The triangular solve and P X, one column j of X = [U | W] per thread, in
-  // registers; rows of A and P are LDS broadcasts.
-  const int j = tid;
-  if (j < 2 * D) {
-    // column j of the right-hand side: v (j < D) or e^g k; branch-free so the
-    // whole solve stays one scheduling region
-    const bool isv = j < D;
-    const float *rhs = isv ? &vf[0][j] : &kf[0][j - D];
-    const int rstride = isv ? D : LD;
-    const float *qcol = &qf[0][isv ? 0 : j - D];
-    float x[CT];
+// The triangular solve for [U | W] and P [U | W], one column per thread:
+// thread j < D takes column j of U, thread D + j column j of W (rows of A and
+// P are LDS broadcasts). For each row s, epi_x(s, x) receives the thread's
+// entry x of U or W, then epi_y(s, val) receives val = O'[s][j] = (P U)[s][j]
+// or Q'[s][j] = e^{g_s} q_s[j] - (P W)[s][j]. Each thread touches only its own column of vf
+// (U threads) or of kf and qf (W threads), so epi may overwrite that column of
+// vf or qf. Threads 2D and up return at once.
+template <int D, int MT, class EpiX, class EpiY>
+__device__ __forceinline__ void chunk_solve(ChunkLds<D, MT> &sm, EpiX epi_x, EpiY epi_y) {
+  const int j = threadIdx.x;
+  if (j >= 2 * D) return;
+  // column j of the right-hand side: v (j < D) or e^g k; branch-free so the
+  // whole solve stays one scheduling region
+  const bool isv = j < D;
+  const int col = isv ? j : j - D;
+  const float *rhs = isv ? &sm.vf[0][col] : &sm.kf[0][col];
+  const float *qcol = isv ? &sm.kf[0][0] : &sm.qf[0][col];  // read only for W columns
+  float x[MT];
 #pragma unroll
-    for (int s = 0; s < CT; ++s) x[s] = 0.f;
+  for (int s = 0; s < MT; ++s) x[s] = 0.f;
 #pragma unroll
-    for (int s = 0; s < CT; ++s) {
-      float acc = rhs[s * rstride] * (isv ? 1.f : eg[s]);
+  for (int s = 0; s < MT; ++s) {
+    float acc = rhs[s * (D + 4)] * (isv ? 1.f : sm.eg[s]);
 #pragma unroll
-      for (int r0 = 0; r0 < s; r0 += 4) {  // A_sr = 0 and x_r = 0 for r >= s
-        const float4 a = ld4(&Al[s][r0]);
-        acc = fmaf(-a.x, x[r0], acc);
-        acc = fmaf(-a.y, x[r0 + 1], acc);
-        acc = fmaf(-a.z, x[r0 + 2], acc);
-        acc = fmaf(-a.w, x[r0 + 3], acc);
-      }
-      x[s] = bt[s] * acc;
+    for (int r0 = 0; r0 < s; r0 += 4) {  // A_sr = 0 and x_r = 0 for r >= s
+      const float4 a = ld4(&sm.Al[s][r0]);
+      acc = fmaf(-a.x, x[r0], acc);
+      acc = fmaf(-a.y, x[r0 + 1], acc);
+      acc = fmaf(-a.z, x[r0 + 2], acc);
+      acc = fmaf(-a.w, x[r0 + 3], acc);
     }
-    float *dst_x = isv ? rec_part<D>(ws, item, RU) + j : rec_part<D>(ws, item, RW) + (j - D);
-#pragma unroll
-    for (int s = 0; s < CT; ++s) dst_x[s * D] = x[s];
-    float *dst_y = isv ? rec_part<D>(ws, item, RO) + j : rec_part<D>(ws, item, RQ) + (j - D);
-#pragma unroll
-    for (int s = 0; s < CT; ++s) {
-      float acc = 0.f;
-#pragma unroll
-      for (int r0 = 0; r0 <= s; r0 += 4) {  // P_sr = 0 for r > s
-        const float4 p = ld4(&Pl[s][r0]);
-        acc = fmaf(p.x, x[r0], acc);
-        acc = fmaf(p.y, x[r0 + 1], acc);
-        acc = fmaf(p.z, x[r0 + 2], acc);
-        acc = fmaf(p.w, x[r0 + 3], acc);
-      }
-      const float qv = qcol[s * LD];
-      dst_y[s * D] = isv ? acc : eg[s] * qv - acc;  // O' = P U; Q' = e^g Q - P W
-    }
+    x[s] = sm.bt[s] * acc;
+    if (s % 8 == 7) __builtin_amdgcn_sched_barrier(0);  // bounds how far reads are hoisted
   }
-  // Kd_s = e^{g_{L-1} - g_s} k_s (g is flat past L, so g[CT-1] = g[L-1]),
-  // stored transposed: key-major, CT tokens per key
+#pragma unroll
+  for (int s = 0; s < MT; ++s) epi_x(s, x[s]);
+#pragma unroll
+  for (int s = 0; s < MT; ++s) {
+    float acc = 0.f;
+#pragma unroll
+    for (int r0 = 0; r0 <= s; r0 += 4) {  // P_sr = 0 for r > s
+      const float4 p = ld4(&sm.Pl[s][r0]);
+      acc = fmaf(p.x, x[r0], acc);
+      acc = fmaf(p.y, x[r0 + 1], acc);
+      acc = fmaf(p.z, x[r0 + 2], acc);
+      acc = fmaf(p.w, x[r0 + 3], acc);
+    }
+    const float qv = qcol[s * (D + 4)];
+    epi_y(s, isv ? acc : sm.eg[s] * qv - acc);
+    if (s % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// prep: one workgroup of 256 per (tree, chunk, head), item = (t * n_chunks + c) * H + h.
+template <int D, int K>
+__global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(
+    const int32_t *__restrict__ tree_off, const int32_t *__restrict__ tree_trunk_len,
+    const __bf16 *__restrict__ xq, const __bf16 *__restrict__ xk, const __bf16 *__restrict__ xv,
+    const float *__restrict__ taps, const float *__restrict__ alpha,
+    const float *__restrict__ beta, float *__restrict__ ws, float *__restrict__ gam,
+    float *__restrict__ glog, int H, int chunk, int n_chunks) {
+  __shared__ __attribute__((aligned(16))) ChunkLds<D, CT> sm;
+  const int64_t item = blockIdx.x;
+  const int h = (int)(item % H);
+  const int c = (int)((item / H) % n_chunks);
+  const int t = (int)(item / ((int64_t)H * n_chunks));
+  const int T = tree_trunk_len[t];
+  const int p0 = c * chunk;  // trunk position of the tile's row 0
+  if (p0 >= T) return;       // workgroup-uniform, before any barrier
+  const int L = min(chunk, T - p0);
+  const int off = tree_off[t];
+  const int tid = threadIdx.x;
+
+  chunk_features<D, K, CT>(sm, [&](int p) { return off + p; }, p0, L, xq, xk, xv, taps, alpha,
+                           beta, H, h);
+  chunk_ap<D, CT>(sm);
+  {
+    const bool isv = tid < D;
+    const int col = isv ? tid : tid - D;
+    float *dx = rec_part<D>(ws, item, isv ? RU : RW) + col;  // U or W
+    float *dv = rec_part<D>(ws, item, isv ? RO : RQ) + col;  // O' or Q'
+    chunk_solve<D, CT>(sm, [&](int s, float x) { dx[s * D] = x; }, [&](int s, float val) { dv[s * D] = val; });
+  }
+  // Kd_s = e^{g_{L-1} - g_s} k_s (g is flat past L, so g[CT-1] = g[L-1]), stored
+  // key-major; k~ row-major and g, for the branch replay
   {
     float *kd = rec_part<D>(ws, item, RKD);
-    const float gl = g[CT - 1];
+    float *kt = rec_part<D>(ws, item, RKF);
+    const float gl = sm.g[CT - 1];
     for (int i = tid; i < CT * D; i += 256) {
       const int key = i / CT, s = i % CT;
-      kd[i] = __expf(gl - g[s]) * kf[s][key];
+      kd[i] = __expf(gl - sm.g[s]) * sm.kf[s][key];
+      kt[i] = sm.kf[i / D][i % D];
     }
   }
-  if (tid == 0) gam[item] = eg[CT - 1];
+  if (tid < CT) glog[item * CT + tid] = sm.g[tid];
+  if (tid == 0) gam[item] = sm.eg[CT - 1];
 }
 
 // ---------------------------------------------------------------------------
@@ -274,15 +335,15 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(
 //        K runs over the keys, lane group g taking keys g D/4 .. (g+1) D/4 - 1;
 //   S (16 rows x D keys) = gamma S + delta^T Kd: wave w owns D/64 tiles of 16
 //        keys in registers, K runs over the tokens, group g taking 16g .. 16g+15.
+// delta goes to the workspace for the branch replay, also for a last partial
+// chunk (whose end state is not needed).
 // W, Kd (stored key-major) and U reach registers straight from the workspace
 // one chunk ahead; delta and S pass between waves through LDS. The D / 16 row
 // blocks of one (tree, head) take workgroup ids 8 apart, so they run on one
 // XCD and share its L2 for W and Kd.
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
 template <int D>
 __global__ __launch_bounds__(256) void gdn_chunk_scan_kernel(
-    const int32_t *__restrict__ tree_trunk_len, const float *__restrict__ ws,
+    const int32_t *__restrict__ tree_trunk_len, float *__restrict__ ws,
     const float *__restrict__ gam, float *__restrict__ ckpt, int H, int chunk, int n_chunks,
     int n_ckpt, int n_pairs) {
   constexpr int RB = 16, NB = D / RB;
@@ -295,7 +356,9 @@ __global__ __launch_bounds__(256) void gdn_chunk_scan_kernel(
   const int vb = y8 % NB, pair = x8 + 8 * (y8 / NB);
   if (pair >= n_pairs) return;
   const int h = pair % H, t = pair / H;
-  const int nfull = tree_trunk_len[t] / chunk;  // chunks whose end state is a checkpoint
+  const int T = tree_trunk_len[t];
+  const int nfull = T / chunk;                // chunks whose end state is a checkpoint
+  const int nall = (T + chunk - 1) / chunk;   // chunks whose deltas the replay may read
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
 
@@ -334,8 +397,8 @@ __global__ __launch_bounds__(256) void gdn_chunk_scan_kernel(
     _Pragma("unroll") for (int r = 0; r < 4; ++r) un[r] = U_[r * D];                       \
     gn = gam[it_];                                                                         \
   }
-  if (nfull > 0) SPEC_GDN_LOAD(0)
-  for (int ci = 0; ci < nfull; ++ci) {
+  if (nall > 0) SPEC_GDN_LOAD(0)
+  for (int ci = 0; ci < nall; ++ci) {
     float4 wc[KW / 4], kc[NT][4];
 #pragma unroll
     for (int i = 0; i < KW / 4; ++i) wc[i] = wn[i];
@@ -345,17 +408,24 @@ __global__ __launch_bounds__(256) void gdn_chunk_scan_kernel(
       for (int i = 0; i < 4; ++i) kc[j][i] = kn[j][i];
     f32x4 d0 = {un[0], un[1], un[2], un[3]}, d1 = {0.f, 0.f, 0.f, 0.f};
     const float gc = gn;
-    if (ci + 1 < nfull) SPEC_GDN_LOAD(ci + 1)
+    if (ci + 1 < nall) SPEC_GDN_LOAD(ci + 1)
     // delta = U - W S^T, two accumulation chains over the keys
 #pragma unroll
     for (int i = 0; i < KW / 4; ++i) {
       const float4 sb = ld4(&Sl[c][g * KW + 4 * i]);
-      d0 = __builtin_amdgcn_mfma_f32_16x16x4f32(-wc[i].x, sb.x, d0, 0, 0, 0);
-      d1 = __builtin_amdgcn_mfma_f32_16x16x4f32(-wc[i].y, sb.y, d1, 0, 0, 0);
-      d0 = __builtin_amdgcn_mfma_f32_16x16x4f32(-wc[i].z, sb.z, d0, 0, 0, 0);
-      d1 = __builtin_amdgcn_mfma_f32_16x16x4f32(-wc[i].w, sb.w, d1, 0, 0, 0);
+      d0 = mfma4(-wc[i].x, sb.x, d0);
+      d1 = mfma4(-wc[i].y, sb.y, d1);
+      d0 = mfma4(-wc[i].z, sb.z, d0);
+      d1 = mfma4(-wc[i].w, sb.w, d1);
     }
     const f32x4 dl = d0 + d1;  // delta[16w + 4g + r][c]
+    {
+      float *dg = rec_part<D>(ws, ((int64_t)t * n_chunks + ci) * H + h, RDL) +
+                  (16 * w + 4 * g) * D + vb * RB + c;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dg[r * D] = dl[r];
+    }
+    if (ci == nfull) break;  // a last partial chunk: no end state (uniform)
     *reinterpret_cast<float4 *>(&DlT[c][16 * w + 4 * g]) = make_float4(dl[0], dl[1], dl[2], dl[3]);
     __syncthreads();
     // S <- gamma S + delta^T Kd
@@ -366,10 +436,10 @@ __global__ __launch_bounds__(256) void gdn_chunk_scan_kernel(
       const float4 da = ld4(&DlT[c][16 * g + 4 * i]);
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        S[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(da.x, kc[j][i].x, S[j], 0, 0, 0);
-        S[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(da.y, kc[j][i].y, S[j], 0, 0, 0);
-        S[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(da.z, kc[j][i].z, S[j], 0, 0, 0);
-        S[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(da.w, kc[j][i].w, S[j], 0, 0, 0);
+        S[j] = mfma4(da.x, kc[j][i].x, S[j]);
+        S[j] = mfma4(da.y, kc[j][i].y, S[j]);
+        S[j] = mfma4(da.z, kc[j][i].z, S[j]);
+        S[j] = mfma4(da.w, kc[j][i].w, S[j]);
       }
     }
 #pragma unroll
@@ -447,17 +517,123 @@ __global__ __launch_bounds__(256) void gdn_chunk_out_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Branch replay from the trunk pass's cache: one workgroup of 256 per (branch,
+// head), pair = b * H + h. The branch's m = W - 1 tokens form an MT-row tile
+// (features along the ancestry path, A, P, the solve; Q' and O' overwrite q~
+// and v~ in LDS), then with 16x16 output tiles on the fp32 matrix cores:
+//   Y   = Q' K'^T         (MT x j), scaled by e^{G - g_r}, zero for r >= j, to LDS
+//   out = e^{G} Q' S_c^T + O' + Y Delta
+// where S_c comes straight from the checkpoint (key-major: a lane's B operand
+// is 16 consecutive value rows of one key) and k~, Delta from chunk c's cache.
+template <int D, int K, int MT>
+__global__ __launch_bounds__(256) void gdn_replay_chunk_kernel(
+    const int32_t *__restrict__ tree_off, const int32_t *__restrict__ branch_tree,
+    const int32_t *__restrict__ branch_anchor, const int32_t *__restrict__ branch_len,
+    const int32_t *__restrict__ branch_off, const __bf16 *__restrict__ xq,
+    const __bf16 *__restrict__ xk, const __bf16 *__restrict__ xv, const float *__restrict__ taps,
+    const float *__restrict__ alpha, const float *__restrict__ beta,
+    const float *__restrict__ ckpt, const float *__restrict__ ws, const float *__restrict__ glog,
+    float *__restrict__ out, int H, int chunk, int n_chunks, int n_ckpt) {
+  constexpr int MTT = MT / 16, NTT = D / 16;  // output tiles along tokens and value rows
+  constexpr int PER = MTT * NTT / 4;          // output tiles per wave
+  constexpr int KG = D / 4;                   // keys per lane group in a product over keys
+  __shared__ __attribute__((aligned(16))) ChunkLds<D, MT> sm;
+  __shared__ __attribute__((aligned(16))) float Yl[MT][CT + 4];
+  __shared__ float fr[CT];
+
+  const int b = blockIdx.x / H, h = blockIdx.x % H;
+  const int W = branch_len[b];
+  if (W < 2) return;  // the branch has no rows (workgroup-uniform, before any barrier)
+  const int m = W - 1;
+  const int t = branch_tree[b], a = branch_anchor[b], r0 = branch_off[b];
+  const int off = tree_off[t];
+  const int c = (a + 1) / chunk, j = a + 1 - c * chunk;  // checkpoint, replayed tokens
+  const int tid = threadIdx.x;
+
+  // path position p: trunk token p through the anchor, then the branch's rows
+  chunk_features<D, K, MT>(sm, [&](int p) { return p <= a ? off + p : r0 + (p - a - 1); }, a + 1, m,
+                           xq, xk, xv, taps, alpha, beta, H, h);
+  const int64_t citem = ((int64_t)t * n_chunks + c) * H + h;  // chunk c's cache (read when j > 0)
+  const float G = j > 0 ? glog[citem * CT + j - 1] : 0.f;
+  if (tid < CT) fr[tid] = tid < j ? __expf(G - glog[citem * CT + tid]) : 0.f;
+  chunk_ap<D, MT>(sm);  // its barrier also publishes fr
+  {
+    const bool isv = tid < D;
+    float *dst = isv ? &sm.vf[0][tid] : &sm.qf[0][tid - D];  // O' over v~, Q' over q~
+    chunk_solve<D, MT>(sm, [](int, float) {}, [&](int s, float val) { dst[s * (D + 4)] = val; });
+  }
+  __syncthreads();
+
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, cc = lane & 15;
+  // Y = Q' K'^T over the replayed tokens (tiles of 16 tokens x 16 replayed rows)
+  const int nrt = (j + 15) / 16;
+  for (int yt = w; yt < MTT * nrt; yt += 4) {
+    const int mt = yt % MTT, rt = yt / MTT;
+    const float *kr = rec_part<D>(ws, citem, RKF) + (16 * rt + cc) * D + g * KG;
+    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < KG / 4; ++i) {
+      const float4 qa = ld4(&sm.qf[16 * mt + cc][g * KG + 4 * i]);
+      const float4 kb = ld4(kr + 4 * i);
+      y = mfma4(qa.x, kb.x, y);
+      y = mfma4(qa.y, kb.y, y);
+      y = mfma4(qa.z, kb.z, y);
+      y = mfma4(qa.w, kb.w, y);
+    }
+    const float f = fr[16 * rt + cc];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Yl[16 * mt + 4 * g + r][16 * rt + cc] = y[r] * f;
+  }
+  // Q' S_c^T into this wave's output tiles (w, w + 4, ...)
+  const float *Sc = ckpt + (((int64_t)t * n_ckpt + c) * H + h) * (int64_t)D * D;
+  f32x4 acc[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int ot = w + 4 * p, mt = ot % MTT, nt = ot / MTT;
+    const float *sb = Sc + (int64_t)(g * KG) * D + 16 * nt + cc;  // key g KG + i, value 16 nt + cc
+    acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int i = 0; i < KG / 4; ++i) {
+      const float4 qa = ld4(&sm.qf[16 * mt + cc][g * KG + 4 * i]);
+      acc[p] = mfma4(qa.x, sb[(4 * i) * D], acc[p]);
+      acc[p] = mfma4(qa.y, sb[(4 * i + 1) * D], acc[p]);
+      acc[p] = mfma4(qa.z, sb[(4 * i + 2) * D], acc[p]);
+      acc[p] = mfma4(qa.w, sb[(4 * i + 3) * D], acc[p]);
+    }
+  }
+  __syncthreads();  // Y complete
+  const float eG = __expf(G);
+  const int nsteps = (j + 3) / 4;  // replayed rows r = 4 s + g
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int ot = w + 4 * p, mt = ot % MTT, nt = ot / MTT;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[p][r] = eG * acc[p][r] + sm.vf[16 * mt + 4 * g + r][16 * nt + cc];
+    const float *dl = rec_part<D>(ws, citem, RDL) + 16 * nt + cc;
+    for (int st = 0; st < nsteps; ++st) {
+      const int r = 4 * st + g;
+      acc[p] = mfma4(Yl[16 * mt + cc][r], dl[(int64_t)r * D], acc[p]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = 16 * mt + 4 * g + r;
+      if (tok < m) out[((int64_t)(r0 + tok) * H + h) * D + 16 * nt + cc] = acc[p][r];
+    }
+  }
+}
+
 template <int D, int K>
 hipError_t launch_chunked(const spec_tree_layout &L, int H, int chunk, int n_chunks, int n_ckpt,
                           const void *xq, const void *xk, const void *xv, const float *taps,
                           const float *alpha, const float *beta, float *ckpt, float *out,
-                          float *ws, float *gam, hipStream_t s) {
+                          float *ws, float *gam, float *glog, hipStream_t s) {
   const int64_t items = (int64_t)L.n_trees * n_chunks * H;
   const int64_t pairs = (int64_t)L.n_trees * H;
   hipLaunchKernelGGL((gdn_chunk_prep_kernel<D, K>), dim3((unsigned)items), dim3(256), 0, s,
                      L.tree_off, L.tree_trunk_len, static_cast<const __bf16 *>(xq),
                      static_cast<const __bf16 *>(xk), static_cast<const __bf16 *>(xv), taps, alpha,
-                     beta, ws, gam, H, chunk, n_chunks);
+                     beta, ws, gam, glog, H, chunk, n_chunks);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   prof_mark(s, "gdn_chunk_prep");
   hipLaunchKernelGGL((gdn_chunk_scan_kernel<D>), dim3((unsigned)((pairs + 7) / 8 * 8 * (D / 16))),
@@ -472,17 +648,46 @@ hipError_t launch_chunked(const spec_tree_layout &L, int H, int chunk, int n_chu
   return hipSuccess;
 }
 
+template <int D, int K, int MT>
+hipError_t launch_replay_chunked(const spec_tree_layout &L, int H, int chunk, int n_chunks,
+                                 int n_ckpt, const void *xq, const void *xk, const void *xv,
+                                 const float *taps, const float *alpha, const float *beta,
+                                 const float *ckpt, const float *ws, const float *glog, float *out,
+                                 hipStream_t s) {
+  const int64_t pairs = (int64_t)L.n_branches * H;
+  if (pairs == 0) return hipSuccess;
+  hipLaunchKernelGGL((gdn_replay_chunk_kernel<D, K, MT>), dim3((unsigned)pairs), dim3(256), 0, s,
+                     L.tree_off, L.branch_tree, L.branch_anchor, L.branch_len, L.branch_off,
+                     static_cast<const __bf16 *>(xq), static_cast<const __bf16 *>(xk),
+                     static_cast<const __bf16 *>(xv), taps, alpha, beta, ckpt, ws, glog, out, H,
+                     chunk, n_chunks, n_ckpt);
+  return hipGetLastError();
+}
+
+struct WorkParts {
+  int64_t items;
+  size_t rec_floats, glog_off, gam_off, total;  // float offsets; total in bytes
+};
+WorkParts work_parts(const spec_tree_layout &L, int H, int D, int chunk) {
+  WorkParts w;
+  const int64_t n_chunks = (L.max_trunk_len + chunk - 1) / chunk;
+  w.items = (int64_t)L.n_trees * n_chunks * H;
+  w.rec_floats = (size_t)w.items * NREC * CT * D;
+  w.glog_off = w.rec_floats;
+  w.gam_off = w.glog_off + (size_t)w.items * CT;
+  w.total = ((w.gam_off + (size_t)w.items) * sizeof(float) + 255) / 256 * 256;
+  return w;
+}
+
 }  // namespace
 
-// Workspace of the trunk pass; the token-at-a-time pass (chunk > 64) uses none
-// but still asks for a token 256 bytes, so that a NULL workspace always means a
-// size query.
+// Workspace of the trunk pass: per (tree, chunk, head) seven CT x D tiles, then
+// g [items][CT] and gamma [items]. The token-at-a-time pass (chunk > 64) uses
+// none but still asks for a token 256 bytes, so that a NULL workspace always
+// means a size query.
 size_t gdn_chunk_work_bytes(const spec_tree_layout &L, int H, int D, int chunk) {
   if (chunk > CT) return 256;
-  const int64_t n_chunks = (L.max_trunk_len + chunk - 1) / chunk;
-  const int64_t items = (int64_t)L.n_trees * n_chunks * H;
-  const size_t rec = (size_t)items * NREC * CT * D * sizeof(float);
-  return rec + ((size_t)items * sizeof(float) + 255) / 256 * 256;
+  return work_parts(L, H, D, chunk).total;
 }
 
 hipError_t launch_gdn_chunked(const spec_tree_layout &L, int H, int D, int K, int chunk, int n_ckpt,
@@ -490,16 +695,40 @@ hipError_t launch_gdn_chunked(const spec_tree_layout &L, int H, int D, int K, in
                               const float *alpha, const float *beta, float *ckpt, float *out,
                               void *work, hipStream_t s) {
   const int n_chunks = (L.max_trunk_len + chunk - 1) / chunk;
-  const int64_t items = (int64_t)L.n_trees * n_chunks * H;
+  const WorkParts wp = work_parts(L, H, D, chunk);
   float *ws = static_cast<float *>(work);
-  float *gam = ws + items * NREC * CT * D;
+  float *glog = ws + wp.glog_off, *gam = ws + wp.gam_off;
 #define SPEC_GDN_CHUNKED(DD, KK)                                                                  \
   if (D == DD && K == KK)                                                                         \
     return launch_chunked<DD, KK>(L, H, chunk, n_chunks, n_ckpt, xq, xk, xv, taps, alpha, beta, \
-                                  ckpt, out, ws, gam, s);
+                                  ckpt, out, ws, gam, glog, s);
   SPEC_GDN_CHUNKED(64, 1) SPEC_GDN_CHUNKED(64, 2) SPEC_GDN_CHUNKED(64, 3) SPEC_GDN_CHUNKED(64, 4)
   SPEC_GDN_CHUNKED(128, 1) SPEC_GDN_CHUNKED(128, 2) SPEC_GDN_CHUNKED(128, 3) SPEC_GDN_CHUNKED(128, 4)
 #undef SPEC_GDN_CHUNKED
+  return hipErrorInvalidValue;
+}
+
+// The branch replay from the cache of the trunk pass (chunk <= 64) that wrote ckpt.
+hipError_t launch_gdn_replay_chunked(const spec_tree_layout &L, int H, int D, int K, int chunk,
+                                     int n_ckpt, const void *xq, const void *xk, const void *xv,
+                                     const float *taps, const float *alpha, const float *beta,
+                                     const float *ckpt, const void *work, float *out,
+                                     hipStream_t s) {
+  const int n_chunks = (L.max_trunk_len + chunk - 1) / chunk;
+  const WorkParts wp = work_parts(L, H, D, chunk);
+  const float *ws = static_cast<const float *>(work);
+  const float *glog = ws + wp.glog_off;
+  const int mt = L.max_branch_len - 1 <= 16 ? 16 : L.max_branch_len - 1 <= 32 ? 32 : 64;
+#define SPEC_GDN_REPLAY(DD, KK, MM)                                                                 \
+  if (D == DD && K == KK && mt == MM)                                                               \
+    return launch_replay_chunked<DD, KK, MM>(L, H, chunk, n_chunks, n_ckpt, xq, xk, xv, taps,      \
+                                             alpha, beta, ckpt, ws, glog, out, s);
+#define SPEC_GDN_REPLAY_K(DD, MM) \
+  SPEC_GDN_REPLAY(DD, 1, MM) SPEC_GDN_REPLAY(DD, 2, MM) SPEC_GDN_REPLAY(DD, 3, MM) SPEC_GDN_REPLAY(DD, 4, MM)
+  SPEC_GDN_REPLAY_K(64, 16) SPEC_GDN_REPLAY_K(64, 32) SPEC_GDN_REPLAY_K(64, 64)
+  SPEC_GDN_REPLAY_K(128, 16) SPEC_GDN_REPLAY_K(128, 32) SPEC_GDN_REPLAY_K(128, 64)
+#undef SPEC_GDN_REPLAY_K
+#undef SPEC_GDN_REPLAY
   return hipErrorInvalidValue;
 }
 
