@@ -424,6 +424,7 @@ spec_status run_gdn(bool trunk, const spec_tree_layout *layout, int32_t n_heads,
       return fail(SPEC_ERR_INVALID_ARG, "a trunk-pass cache exists only for chunk <= 64 (got %d)", chunk);
     if (!aligned16(d_trunk_work)) return fail(SPEC_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
     if (L.max_branch_len > 65) return fail(SPEC_ERR_UNSUPPORTED, "branches longer than 65 tokens");
+    if (!L.branch_order) return fail(SPEC_ERR_INVALID_ARG, "layout device arrays are missing");
     prof_mark(s, "gdn:begin");
     const hipError_t e = launch_gdn_replay_chunked(L, n_heads, head_dim, conv_width, chunk, n_ckpt, d_xq,
                                                    d_xk, d_xv, d_taps, d_alpha, d_beta, d_ckpt,

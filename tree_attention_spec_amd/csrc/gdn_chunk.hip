@@ -99,6 +99,12 @@ __device__ __forceinline__ void chunk_features(ChunkLds<D, MT> &sm, RowOf row_of
                                       const float *__restrict__ alpha,
                                       const float *__restrict__ beta, int H, int h) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  float la = 0.f, b = 0.f;  // this lane's gates (wave 0), loaded first
+  if (wv == 0 && lane < L) {
+    const int64_t gi = (int64_t)row_of(P0 + lane) * H + h;
+    la = alpha[gi];
+    b = beta[gi];
+  }
   {
     constexpr int G = 256 / D, TPG = MT / G, NR = TPG + K - 1;
     const int d = tid % D, s0 = (tid / D) * TPG;
@@ -136,12 +142,7 @@ __device__ __forceinline__ void chunk_features(ChunkLds<D, MT> &sm, RowOf row_of
     }
   }
   if (wv == 0) {
-    float la = 0.f, b = 0.f;
-    if (lane < L) {
-      const int64_t gi = (int64_t)row_of(P0 + lane) * H + h;
-      la = __logf(alpha[gi]);
-      b = beta[gi];
-    }
+    la = lane < L ? __logf(la) : 0.f;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const float y = __shfl_up(la, o);
@@ -519,7 +520,10 @@ __global__ __launch_bounds__(256) void gdn_chunk_out_kernel(
 
 // ---------------------------------------------------------------------------
 // Branch replay from the trunk pass's cache: one workgroup of 256 per (branch,
-// head), pair = b * H + h. The branch's m = W - 1 tokens form an MT-row tile
+// head). Each XCD takes a contiguous run of pairs, head-major with the branches
+// in packed (anchor) order, so branches anchored in one chunk follow each other
+// on one XCD and read the same checkpoint through its L2. Global operands are
+// requested one phase ahead of their use. The branch's m = W - 1 tokens form an MT-row tile
 // (features along the ancestry path, A, P, the solve; Q' and O' overwrite q~
 // and v~ in LDS), then with 16x16 output tiles on the fp32 matrix cores:
 //   Y   = Q' K'^T         (MT x j), scaled by e^{G - g_r}, zero for r >= j, to LDS
@@ -528,13 +532,14 @@ __global__ __launch_bounds__(256) void gdn_chunk_out_kernel(
 // is 16 consecutive value rows of one key) and k~, Delta from chunk c's cache.
 template <int D, int K, int MT>
 __global__ __launch_bounds__(256) void gdn_replay_chunk_kernel(
-    const int32_t *__restrict__ tree_off, const int32_t *__restrict__ branch_tree,
-    const int32_t *__restrict__ branch_anchor, const int32_t *__restrict__ branch_len,
-    const int32_t *__restrict__ branch_off, const __bf16 *__restrict__ xq,
-    const __bf16 *__restrict__ xk, const __bf16 *__restrict__ xv, const float *__restrict__ taps,
-    const float *__restrict__ alpha, const float *__restrict__ beta,
-    const float *__restrict__ ckpt, const float *__restrict__ ws, const float *__restrict__ glog,
-    float *__restrict__ out, int H, int chunk, int n_chunks, int n_ckpt) {
+    const int32_t *__restrict__ tree_off, const int32_t *__restrict__ branch_order,
+    const int32_t *__restrict__ branch_tree, const int32_t *__restrict__ branch_anchor,
+    const int32_t *__restrict__ branch_len, const int32_t *__restrict__ branch_off,
+    const __bf16 *__restrict__ xq, const __bf16 *__restrict__ xk, const __bf16 *__restrict__ xv,
+    const float *__restrict__ taps, const float *__restrict__ alpha,
+    const float *__restrict__ beta, const float *__restrict__ ckpt, const float *__restrict__ ws,
+    const float *__restrict__ glog, float *__restrict__ out, int H, int B, int per_xcd, int chunk,
+    int n_chunks, int n_ckpt) {
   constexpr int MTT = MT / 16, NTT = D / 16;  // output tiles along tokens and value rows
   constexpr int PER = MTT * NTT / 4;          // output tiles per wave
   constexpr int KG = D / 4;                   // keys per lane group in a product over keys
@@ -542,7 +547,9 @@ __global__ __launch_bounds__(256) void gdn_replay_chunk_kernel(
   __shared__ __attribute__((aligned(16))) float Yl[MT][CT + 4];
   __shared__ float fr[CT];
 
-  const int b = blockIdx.x / H, h = blockIdx.x % H;
+  const int pair = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (pair >= B * H) return;
+  const int h = pair / B, b = branch_order[pair % B];
   const int W = branch_len[b];
   if (W < 2) return;  // the branch has no rows (workgroup-uniform, before any barrier)
   const int m = W - 1;
@@ -550,13 +557,14 @@ __global__ __launch_bounds__(256) void gdn_replay_chunk_kernel(
   const int off = tree_off[t];
   const int c = (a + 1) / chunk, j = a + 1 - c * chunk;  // checkpoint, replayed tokens
   const int tid = threadIdx.x;
+  const int64_t citem = ((int64_t)t * n_chunks + c) * H + h;  // chunk c's cache (read when j > 0)
+  const float G = j > 0 ? glog[citem * CT + j - 1] : 0.f;
+  const float gr = tid < j ? glog[citem * CT + tid] : 0.f;
 
   // path position p: trunk token p through the anchor, then the branch's rows
   chunk_features<D, K, MT>(sm, [&](int p) { return p <= a ? off + p : r0 + (p - a - 1); }, a + 1, m,
                            xq, xk, xv, taps, alpha, beta, H, h);
-  const int64_t citem = ((int64_t)t * n_chunks + c) * H + h;  // chunk c's cache (read when j > 0)
-  const float G = j > 0 ? glog[citem * CT + j - 1] : 0.f;
-  if (tid < CT) fr[tid] = tid < j ? __expf(G - glog[citem * CT + tid]) : 0.f;
+  if (tid < CT) fr[tid] = tid < j ? __expf(G - gr) : 0.f;
   chunk_ap<D, MT>(sm);  // its barrier also publishes fr
   {
     const bool isv = tid < D;
@@ -566,6 +574,15 @@ __global__ __launch_bounds__(256) void gdn_replay_chunk_kernel(
   __syncthreads();
 
   const int lane = tid & 63, w = tid >> 6, g = lane >> 4, cc = lane & 15;
+  const float *Sc = ckpt + (((int64_t)t * n_ckpt + c) * H + h) * (int64_t)D * D;
+  // the first output tile's column of S_c (key g KG + i, value row 16 nt + cc), in
+  // flight during Y
+  float bv0[KG];
+  {
+    const float *sb = Sc + (int64_t)(g * KG) * D + 16 * (w / MTT) + cc;
+#pragma unroll
+    for (int i = 0; i < KG; ++i) bv0[i] = sb[(int64_t)i * D];
+  }
   // Y = Q' K'^T over the replayed tokens (tiles of 16 tokens x 16 replayed rows)
   const int nrt = (j + 15) / 16;
   for (int yt = w; yt < MTT * nrt; yt += 4) {
@@ -586,7 +603,6 @@ __global__ __launch_bounds__(256) void gdn_replay_chunk_kernel(
     for (int r = 0; r < 4; ++r) Yl[16 * mt + 4 * g + r][16 * rt + cc] = y[r] * f;
   }
   // Q' S_c^T into this wave's output tiles (w, w + 4, ...)
-  const float *Sc = ckpt + (((int64_t)t * n_ckpt + c) * H + h) * (int64_t)D * D;
   f32x4 acc[PER];
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
@@ -596,11 +612,21 @@ __global__ __launch_bounds__(256) void gdn_replay_chunk_kernel(
 #pragma unroll 4
     for (int i = 0; i < KG / 4; ++i) {
       const float4 qa = ld4(&sm.qf[16 * mt + cc][g * KG + 4 * i]);
-      acc[p] = mfma4(qa.x, sb[(4 * i) * D], acc[p]);
-      acc[p] = mfma4(qa.y, sb[(4 * i + 1) * D], acc[p]);
-      acc[p] = mfma4(qa.z, sb[(4 * i + 2) * D], acc[p]);
-      acc[p] = mfma4(qa.w, sb[(4 * i + 3) * D], acc[p]);
+      float bb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bb[e] = p == 0 ? bv0[4 * i + e] : sb[(4 * i + e) * D];
+      acc[p] = mfma4(qa.x, bb[0], acc[p]);
+      acc[p] = mfma4(qa.y, bb[1], acc[p]);
+      acc[p] = mfma4(qa.z, bb[2], acc[p]);
+      acc[p] = mfma4(qa.w, bb[3], acc[p]);
     }
+  }
+  // Delta rows 4 st + g of the first output tile, in flight across the barrier
+  float dv0[16];
+  if (j > 0) {  // uniform; chunk c's cache exists
+    const float *dl = rec_part<D>(ws, citem, RDL) + g * D + 16 * (w / MTT) + cc;
+#pragma unroll
+    for (int st = 0; st < 16; ++st) dv0[st] = dl[(4 * st) * D];
   }
   __syncthreads();  // Y complete
   const float eG = __expf(G);
@@ -610,10 +636,16 @@ __global__ __launch_bounds__(256) void gdn_replay_chunk_kernel(
     const int ot = w + 4 * p, mt = ot % MTT, nt = ot / MTT;
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[p][r] = eG * acc[p][r] + sm.vf[16 * mt + 4 * g + r][16 * nt + cc];
-    const float *dl = rec_part<D>(ws, citem, RDL) + 16 * nt + cc;
-    for (int st = 0; st < nsteps; ++st) {
-      const int r = 4 * st + g;
-      acc[p] = mfma4(Yl[16 * mt + cc][r], dl[(int64_t)r * D], acc[p]);
+    if (p == 0) {
+#pragma unroll
+      for (int st = 0; st < 16; ++st)
+        if (st < nsteps) acc[p] = mfma4(Yl[16 * mt + cc][4 * st + g], dv0[st], acc[p]);
+    } else {
+      const float *dl = rec_part<D>(ws, citem, RDL) + 16 * nt + cc;
+      for (int st = 0; st < nsteps; ++st) {
+        const int r = 4 * st + g;
+        acc[p] = mfma4(Yl[16 * mt + cc][r], dl[(int64_t)r * D], acc[p]);
+      }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -656,11 +688,12 @@ hipError_t launch_replay_chunked(const spec_tree_layout &L, int H, int chunk, in
                                  hipStream_t s) {
   const int64_t pairs = (int64_t)L.n_branches * H;
   if (pairs == 0) return hipSuccess;
-  hipLaunchKernelGGL((gdn_replay_chunk_kernel<D, K, MT>), dim3((unsigned)pairs), dim3(256), 0, s,
-                     L.tree_off, L.branch_tree, L.branch_anchor, L.branch_len, L.branch_off,
-                     static_cast<const __bf16 *>(xq), static_cast<const __bf16 *>(xk),
+  const int64_t per_xcd = (pairs + 7) / 8;
+  hipLaunchKernelGGL((gdn_replay_chunk_kernel<D, K, MT>), dim3((unsigned)(per_xcd * 8)), dim3(256), 0,
+                     s, L.tree_off, L.branch_order, L.branch_tree, L.branch_anchor, L.branch_len,
+                     L.branch_off, static_cast<const __bf16 *>(xq), static_cast<const __bf16 *>(xk),
                      static_cast<const __bf16 *>(xv), taps, alpha, beta, ckpt, ws, glog, out, H,
-                     chunk, n_chunks, n_ckpt);
+                     L.n_branches, (int)per_xcd, chunk, n_chunks, n_ckpt);
   return hipGetLastError();
 }
 
