@@ -177,53 +177,42 @@ __device__ __forceinline__ void chunk_features(ChunkLds<D, MT> &sm, RowOf row_of
   __syncthreads();
 }
 
-// A_sr = e^{g_s-g_r} k_s.k_r (r < s) and P_sr = e^{g_s-g_r} q_s.k_r (r <= s):
-// lane r % MT holds k_r in 32-column pieces and each group of MT threads takes
-// MT * MT / 256 rows s, whose k_s and q_s are LDS broadcasts. Ends with a barrier.
+// A_sr = e^{g_s-g_r} k_s.k_r (r < s) and P_sr = e^{g_s-g_r} q_s.k_r (r <= s) as
+// 16 x 16 tiles on the fp32 matrix cores (v_mfma_f32_16x16x4_f32): the tiles on
+// and below the diagonal of A, then of P, dealt to the 4 waves in turn; K runs
+// over the D feature columns, lane group g taking columns g D/4 .. (g+1) D/4 - 1,
+// so each lane reads its rows of k~ (or q~) and k~ as 128-bit LDS loads. Tiles
+// above the diagonal are never read by the solve and are left alone. Ends with
+// a barrier.
 template <int D, int MT>
 __device__ __forceinline__ void chunk_ap(ChunkLds<D, MT> &sm) {
-  constexpr int RPG = MT * MT / 256;  // rows s per group
-  const int tid = threadIdx.x;
-  const int r = tid % MT, s0 = (tid / MT) * RPG;
-  float accA[RPG], accP[RPG];
+  constexpr int NT = MT / 16, TRI = NT * (NT + 1) / 2, KG = D / 4;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+  for (int tix = w; tix < 2 * TRI; tix += 4) {  // uniform per wave
+    const bool isp = tix >= TRI;
+    int k = isp ? tix - TRI : tix, si = 0;
+    while (k > si) k -= ++si;  // lower-triangle tile (si, ri = k)
+    const int ri = k;
+    const float *xs = isp ? &sm.qf[16 * si + c][g * KG] : &sm.kf[16 * si + c][g * KG];
+    const float *xr = &sm.kf[16 * ri + c][g * KG];
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < RPG; ++i) accA[i] = accP[i] = 0.f;
-#pragma unroll 1
-  for (int d0 = 0; d0 < D; d0 += 32) {
-    float kr[32];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4 x = ld4(&sm.kf[r][d0 + 4 * i]);
-      kr[4 * i] = x.x;
-      kr[4 * i + 1] = x.y;
-      kr[4 * i + 2] = x.z;
-      kr[4 * i + 3] = x.w;
+    for (int i = 0; i < KG / 4; ++i) {
+      const float4 a4 = ld4(xs + 4 * i), b4 = ld4(xr + 4 * i);
+      acc0 = mfma4(a4.x, b4.x, acc0);
+      acc1 = mfma4(a4.y, b4.y, acc1);
+      acc0 = mfma4(a4.z, b4.z, acc0);
+      acc1 = mfma4(a4.w, b4.w, acc1);
     }
+    const f32x4 acc = acc0 + acc1;  // row 16 si + 4g + e, column 16 ri + c
+    const int r = 16 * ri + c;
 #pragma unroll
-    for (int si = 0; si < RPG; ++si) {
-      const int s = s0 + si;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float4 ks = ld4(&sm.kf[s][d0 + 4 * i]);
-        const float4 qs = ld4(&sm.qf[s][d0 + 4 * i]);
-        accA[si] = fmaf(ks.x, kr[4 * i], accA[si]);
-        accA[si] = fmaf(ks.y, kr[4 * i + 1], accA[si]);
-        accA[si] = fmaf(ks.z, kr[4 * i + 2], accA[si]);
-        accA[si] = fmaf(ks.w, kr[4 * i + 3], accA[si]);
-        accP[si] = fmaf(qs.x, kr[4 * i], accP[si]);
-        accP[si] = fmaf(qs.y, kr[4 * i + 1], accP[si]);
-        accP[si] = fmaf(qs.z, kr[4 * i + 2], accP[si]);
-        accP[si] = fmaf(qs.w, kr[4 * i + 3], accP[si]);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // keeps the broadcast reads near their FMAs
+    for (int e = 0; e < 4; ++e) {
+      const int s = 16 * si + 4 * g + e;
+      const float v = __expf(sm.g[s] - sm.g[r]) * acc[e];  // kept only where r <= s, so e^.. <= 1
+      if (isp) sm.Pl[s][r] = r <= s ? v : 0.f;
+      else sm.Al[s][r] = r < s ? v : 0.f;
     }
-  }
-#pragma unroll
-  for (int si = 0; si < RPG; ++si) {
-    const int s = s0 + si;
-    const float e = __expf(sm.g[s] - sm.g[r]);  // used only where r <= s, so e <= 1
-    sm.Al[s][r] = r < s ? e * accA[si] : 0.f;
-    sm.Pl[s][r] = r <= s ? e * accP[si] : 0.f;
   }
   __syncthreads();
 }
