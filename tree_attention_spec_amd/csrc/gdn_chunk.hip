@@ -61,6 +61,19 @@ __device__ inline f32x4 mfma4(float a, float b, f32x4 c) {
 
 __device__ inline float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
+// (s_waitcnt lgkmcnt(0); vmcnt and expcnt left at their maxima), then
+// s_barrier. __syncthreads() would also wait for every global load and store
+// in flight, which would drain loads issued for a later phase. No kernel here
+// passes data between waves through global memory.
+constexpr int kWaitLgkm0 = 0xC07F;
+__device__ inline void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int D>
 __device__ inline float *rec_part(float *ws, int64_t item, int part) {
   return ws + (item * NREC + part) * (int64_t)(CT * D);
@@ -152,7 +165,7 @@ __device__ __forceinline__ void chunk_features(ChunkLds<D, MT> &sm, RowOf row_of
     sm.eg[lane] = __expf(la);
     sm.bt[lane] = b;
   }
-  __syncthreads();
+  lds_barrier();
   const float qscale = 1.f / sqrtf((float)D);
   for (int s = wv; s < MT; s += 4) {
     float sk = 0.f, sq = 0.f;
@@ -168,13 +181,13 @@ __device__ __forceinline__ void chunk_features(ChunkLds<D, MT> &sm, RowOf row_of
       sm.nq[s] = s < L ? qscale * __builtin_amdgcn_rsqf(sq) : 0.f;
     }
   }
-  __syncthreads();
+  lds_barrier();
   for (int i = tid; i < MT * D; i += 256) {
     const int s = i / D, d = i % D;
     sm.kf[s][d] *= sm.nk[s];
     sm.qf[s][d] *= sm.nq[s];
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // A_sr = e^{g_s-g_r} k_s.k_r (r < s) and P_sr = e^{g_s-g_r} q_s.k_r (r <= s) as
@@ -214,7 +227,7 @@ __device__ __forceinline__ void chunk_ap(ChunkLds<D, MT> &sm) {
       else sm.Al[s][r] = r < s ? v : 0.f;
     }
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // The triangular solve for [U | W] and P [U | W], one column per thread:
@@ -325,21 +338,27 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(
 //        K runs over the keys, lane group g taking keys g D/4 .. (g+1) D/4 - 1;
 //   S (16 rows x D keys) = gamma S + delta^T Kd: wave w owns D/64 tiles of 16
 //        keys in registers, K runs over the tokens, group g taking 16g .. 16g+15.
-// delta goes to the workspace for the branch replay, also for a last partial
-// chunk (whose end state is not needed).
-// W, Kd (stored key-major) and U reach registers straight from the workspace
-// one chunk ahead; delta and S pass between waves through LDS. The D / 16 row
-// blocks of one (tree, head) take workgroup ids 8 apart, so they run on one
-// XCD and share its L2 for W and Kd.
+// W, Kd (stored key-major) and the block's U columns are read with coalesced
+// loads one chunk ahead into registers, then written to LDS, from which the
+// matrix operands are read (a lane's operands lie in 16 rows of W or Kd, which
+// straight from memory would touch a new cache line per lane). delta and S
+// pass between waves through LDS. delta goes to the workspace for the branch
+// replay, also for a last partial chunk (whose end state is not needed). The
+// D / 16 row blocks of one (tree, head) take workgroup ids 8 apart, so they
+// run on one XCD and share its L2 for W and Kd.
 template <int D>
 __global__ __launch_bounds__(256) void gdn_chunk_scan_kernel(
     const int32_t *__restrict__ tree_trunk_len, float *__restrict__ ws,
     const float *__restrict__ gam, float *__restrict__ ckpt, int H, int chunk, int n_chunks,
     int n_ckpt, int n_pairs) {
   constexpr int RB = 16, NB = D / RB;
-  constexpr int KW = D / 4;   // keys per lane group in the delta product
-  constexpr int NT = D / 64;  // 16-key state tiles per wave
-  __shared__ __attribute__((aligned(16))) float Sl[RB][D + 4];    // S of the block
+  constexpr int KW = D / 4;              // keys per lane group in the delta product
+  constexpr int NT = D / 64;             // 16-key state tiles per wave
+  constexpr int NW4 = CT * D / 4 / 256;  // float4 pieces of a CT x D tile per thread
+  __shared__ __attribute__((aligned(16))) float Wl[CT][D + 4];   // W of the chunk
+  __shared__ __attribute__((aligned(16))) float Kl[D][CT + 4];   // Kd, key-major
+  __shared__ __attribute__((aligned(16))) float Ul[CT][RB];      // the block's U columns
+  __shared__ __attribute__((aligned(16))) float Sl[RB][D + 4];   // S of the block
   __shared__ __attribute__((aligned(16))) float DlT[RB][CT + 4];  // delta, row-major by value row
 
   const int x8 = blockIdx.x % 8, y8 = blockIdx.x / 8;
@@ -362,51 +381,47 @@ __global__ __launch_bounds__(256) void gdn_chunk_scan_kernel(
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) ck[(int64_t)(tid / 16 + 16 * i) * D + tid % 16] = 0.f;  // slot 0
 
-  // one chunk's operands for this lane:
-  //   W[16w + c][g KW ..], KdT[16 (NT w + j) + c][16 g ..], U[16w + 4g + r][vb RB + c], gamma
-  float4 wn[KW / 4], kn[NT][4];
-  float un[4], gn = 0.f;
+  // the next chunk's W, Kd and U columns, coalesced, in flight in registers
+  float4 pw[NW4], pk[NW4], pu = make_float4(0.f, 0.f, 0.f, 0.f);
+  float gn = 0.f;
 #pragma unroll
-  for (int i = 0; i < KW / 4; ++i) wn[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-  for (int j = 0; j < NT; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) kn[j][i] = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) un[r] = 0.f;
-#define SPEC_GDN_LOAD(cc)                                                                  \
-  {                                                                                        \
-    const int64_t it_ = ((int64_t)t * n_chunks + (cc)) * H + h;                            \
-    const float *W_ = rec_part<D>(ws, it_, RW) + (16 * w + c) * D + g * KW;                \
-    const float *K_ = rec_part<D>(ws, it_, RKD) + 16 * g;                                  \
-    const float *U_ = rec_part<D>(ws, it_, RU) + (16 * w + 4 * g) * D + vb * RB + c;       \
-    _Pragma("unroll") for (int i = 0; i < KW / 4; ++i) wn[i] = ld4(W_ + 4 * i);            \
-    _Pragma("unroll") for (int j = 0; j < NT; ++j)                                         \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                        \
-        kn[j][i] = ld4(K_ + (16 * (NT * w + j) + c) * CT + 4 * i);                          \
-    _Pragma("unroll") for (int r = 0; r < 4; ++r) un[r] = U_[r * D];                       \
-    gn = gam[it_];                                                                         \
+  for (int i = 0; i < NW4; ++i) pw[i] = pk[i] = pu;
+#define SPEC_GDN_LOAD(cc)                                                                       \
+  {                                                                                             \
+    const int64_t it_ = ((int64_t)t * n_chunks + (cc)) * H + h;                                 \
+    const float4 *w4_ = reinterpret_cast<const float4 *>(rec_part<D>(ws, it_, RW));             \
+    const float4 *k4_ = reinterpret_cast<const float4 *>(rec_part<D>(ws, it_, RKD));            \
+    _Pragma("unroll") for (int i = 0; i < NW4; ++i) {                                           \
+      pw[i] = w4_[tid + 256 * i];                                                               \
+      pk[i] = k4_[tid + 256 * i];                                                               \
+    }                                                                                           \
+    pu = ld4(rec_part<D>(ws, it_, RU) + (tid / 4) * D + vb * RB + (tid % 4) * 4); /* CT x RB */ \
+    gn = gam[it_];                                                                              \
   }
   if (nall > 0) SPEC_GDN_LOAD(0)
   for (int ci = 0; ci < nall; ++ci) {
-    float4 wc[KW / 4], kc[NT][4];
 #pragma unroll
-    for (int i = 0; i < KW / 4; ++i) wc[i] = wn[i];
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) kc[j][i] = kn[j][i];
-    f32x4 d0 = {un[0], un[1], un[2], un[3]}, d1 = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NW4; ++i) {
+      const int e = (tid + 256 * i) * 4;
+      *reinterpret_cast<float4 *>(&Wl[e / D][e % D]) = pw[i];
+      *reinterpret_cast<float4 *>(&Kl[e / CT][e % CT]) = pk[i];
+    }
+    *reinterpret_cast<float4 *>(&Ul[tid / 4][(tid % 4) * 4]) = pu;
     const float gc = gn;
+    lds_barrier();
     if (ci + 1 < nall) SPEC_GDN_LOAD(ci + 1)
     // delta = U - W S^T, two accumulation chains over the keys
+    f32x4 d0, d1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) d0[r] = Ul[16 * w + 4 * g + r][c];
 #pragma unroll
     for (int i = 0; i < KW / 4; ++i) {
       const float4 sb = ld4(&Sl[c][g * KW + 4 * i]);
-      d0 = mfma4(-wc[i].x, sb.x, d0);
-      d1 = mfma4(-wc[i].y, sb.y, d1);
-      d0 = mfma4(-wc[i].z, sb.z, d0);
-      d1 = mfma4(-wc[i].w, sb.w, d1);
+      const float4 wa = ld4(&Wl[16 * w + c][g * KW + 4 * i]);
+      d0 = mfma4(-wa.x, sb.x, d0);
+      d1 = mfma4(-wa.y, sb.y, d1);
+      d0 = mfma4(-wa.z, sb.z, d0);
+      d1 = mfma4(-wa.w, sb.w, d1);
     }
     const f32x4 dl = d0 + d1;  // delta[16w + 4g + r][c]
     {
@@ -417,7 +432,7 @@ __global__ __launch_bounds__(256) void gdn_chunk_scan_kernel(
     }
     if (ci == nfull) break;  // a last partial chunk: no end state (uniform)
     *reinterpret_cast<float4 *>(&DlT[c][16 * w + 4 * g]) = make_float4(dl[0], dl[1], dl[2], dl[3]);
-    __syncthreads();
+    lds_barrier();
     // S <- gamma S + delta^T Kd
 #pragma unroll
     for (int j = 0; j < NT; ++j) S[j] *= gc;
@@ -426,17 +441,18 @@ __global__ __launch_bounds__(256) void gdn_chunk_scan_kernel(
       const float4 da = ld4(&DlT[c][16 * g + 4 * i]);
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        S[j] = mfma4(da.x, kc[j][i].x, S[j]);
-        S[j] = mfma4(da.y, kc[j][i].y, S[j]);
-        S[j] = mfma4(da.z, kc[j][i].z, S[j]);
-        S[j] = mfma4(da.w, kc[j][i].w, S[j]);
+        const float4 kb = ld4(&Kl[16 * (NT * w + j) + c][16 * g + 4 * i]);
+        S[j] = mfma4(da.x, kb.x, S[j]);
+        S[j] = mfma4(da.y, kb.y, S[j]);
+        S[j] = mfma4(da.z, kb.z, S[j]);
+        S[j] = mfma4(da.w, kb.w, S[j]);
       }
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) Sl[4 * g + r][16 * (NT * w + j) + c] = S[j][r];
-    __syncthreads();
+    lds_barrier();
     // checkpoint ci + 1, 16 consecutive value rows per key
     float *slot = ck + (int64_t)(ci + 1) * slot_stride;
 #pragma unroll
@@ -479,7 +495,7 @@ __global__ __launch_bounds__(256) void gdn_chunk_out_kernel(
   float acc[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) acc[i] = op[(sg + G * i) * D + v];
-  __syncthreads();
+  lds_barrier();
   const float *sc = ckpt + (((int64_t)t * n_ckpt + c) * H + h) * (int64_t)D * D + v;
 #pragma unroll 1
   for (int k0 = 0; k0 < D; k0 += 32) {
@@ -560,7 +576,7 @@ __global__ __launch_bounds__(256) void gdn_replay_chunk_kernel(
     float *dst = isv ? &sm.vf[0][tid] : &sm.qf[0][tid - D];  // O' over v~, Q' over q~
     chunk_solve<D, MT>(sm, [](int, float) {}, [&](int s, float val) { dst[s * (D + 4)] = val; });
   }
-  __syncthreads();
+  lds_barrier();
 
   const int lane = tid & 63, w = tid >> 6, g = lane >> 4, cc = lane & 15;
   const float *Sc = ckpt + (((int64_t)t * n_ckpt + c) * H + h) * (int64_t)D * D;
@@ -617,7 +633,7 @@ __global__ __launch_bounds__(256) void gdn_replay_chunk_kernel(
 #pragma unroll
     for (int st = 0; st < 16; ++st) dv0[st] = dl[(4 * st) * D];
   }
-  __syncthreads();  // Y complete
+  lds_barrier();  // Y complete
   const float eG = __expf(G);
   const int nsteps = (j + 3) / 4;  // replayed rows r = 4 s + g
 #pragma unroll
