@@ -252,31 +252,37 @@ __device__ __forceinline__ void chunk_solve(ChunkLds<D, MT> &sm, EpiX epi_x, Epi
   for (int s = 0; s < MT; ++s) x[s] = 0.f;
 #pragma unroll
   for (int s = 0; s < MT; ++s) {
-    float acc = rhs[s * (D + 4)] * (isv ? 1.f : sm.eg[s]);
+    // short tiles: two accumulation chains (even and odd groups of four), so a
+    // row's sum waits on half as many dependent FMAs (the 64-row tile keeps one:
+    // it has enough independent work and schedules better that way)
+    float acc = rhs[s * (D + 4)] * (isv ? 1.f : sm.eg[s]), acc2 = 0.f;
 #pragma unroll
     for (int r0 = 0; r0 < s; r0 += 4) {  // A_sr = 0 and x_r = 0 for r >= s
       const float4 a = ld4(&sm.Al[s][r0]);
-      acc = fmaf(-a.x, x[r0], acc);
-      acc = fmaf(-a.y, x[r0 + 1], acc);
-      acc = fmaf(-a.z, x[r0 + 2], acc);
-      acc = fmaf(-a.w, x[r0 + 3], acc);
+      float &ac = (MT < 64 && (r0 & 4)) ? acc2 : acc;
+      ac = fmaf(-a.x, x[r0], ac);
+      ac = fmaf(-a.y, x[r0 + 1], ac);
+      ac = fmaf(-a.z, x[r0 + 2], ac);
+      ac = fmaf(-a.w, x[r0 + 3], ac);
     }
-    x[s] = sm.bt[s] * acc;
+    x[s] = sm.bt[s] * (acc + acc2);
     if (s % 8 == 7) __builtin_amdgcn_sched_barrier(0);  // bounds how far reads are hoisted
   }
 #pragma unroll
   for (int s = 0; s < MT; ++s) epi_x(s, x[s]);
 #pragma unroll
   for (int s = 0; s < MT; ++s) {
-    float acc = 0.f;
+    float acc = 0.f, acc2 = 0.f;
 #pragma unroll
     for (int r0 = 0; r0 <= s; r0 += 4) {  // P_sr = 0 for r > s
       const float4 p = ld4(&sm.Pl[s][r0]);
-      acc = fmaf(p.x, x[r0], acc);
-      acc = fmaf(p.y, x[r0 + 1], acc);
-      acc = fmaf(p.z, x[r0 + 2], acc);
-      acc = fmaf(p.w, x[r0 + 3], acc);
+      float &ac = (MT < 64 && (r0 & 4)) ? acc2 : acc;
+      ac = fmaf(p.x, x[r0], ac);
+      ac = fmaf(p.y, x[r0 + 1], ac);
+      ac = fmaf(p.z, x[r0 + 2], ac);
+      ac = fmaf(p.w, x[r0 + 3], ac);
     }
+    acc += acc2;
     const float qv = qcol[s * (D + 4)];
     epi_y(s, isv ? acc : sm.eg[s] * qv - acc);
     if (s % 8 == 7) __builtin_amdgcn_sched_barrier(0);
@@ -536,7 +542,7 @@ __global__ __launch_bounds__(256) void gdn_chunk_out_kernel(
 // where S_c comes straight from the checkpoint (key-major: a lane's B operand
 // is 16 consecutive value rows of one key) and k~, Delta from chunk c's cache.
 template <int D, int K, int MT>
-__global__ __launch_bounds__(256) void gdn_replay_chunk_kernel(
+__global__ __launch_bounds__(256, MT == 16 ? 3 : 1) void gdn_replay_chunk_kernel(
     const int32_t *__restrict__ tree_off, const int32_t *__restrict__ branch_order,
     const int32_t *__restrict__ branch_tree, const int32_t *__restrict__ branch_anchor,
     const int32_t *__restrict__ branch_len, const int32_t *__restrict__ branch_off,
@@ -645,12 +651,14 @@ __global__ __launch_bounds__(256) void gdn_replay_chunk_kernel(
 #pragma unroll
       for (int st = 0; st < 16; ++st)
         if (st < nsteps) acc[p] = mfma4(Yl[16 * mt + cc][4 * st + g], dv0[st], acc[p]);
-    } else {
-      const float *dl = rec_part<D>(ws, citem, RDL) + 16 * nt + cc;
-      for (int st = 0; st < nsteps; ++st) {
-        const int r = 4 * st + g;
-        acc[p] = mfma4(Yl[16 * mt + cc][r], dl[(int64_t)r * D], acc[p]);
-      }
+    } else if (j > 0) {  // uniform; the tile's 16 Delta loads issued together
+      const float *dl = rec_part<D>(ws, citem, RDL) + g * D + 16 * nt + cc;
+      float dv[16];
+#pragma unroll
+      for (int st = 0; st < 16; ++st) dv[st] = dl[(4 * st) * D];
+#pragma unroll
+      for (int st = 0; st < 16; ++st)
+        if (st < nsteps) acc[p] = mfma4(Yl[16 * mt + cc][4 * st + g], dv[st], acc[p]);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
