@@ -147,44 +147,50 @@ def _trunk_compare(s, H, D, K, C, seed, heads=None):
         tas.spec_gdn_replay_fwd(tree, *x, ckpt=ck_g, chunk=C, out=out_c, trunk_work=work)
         outs.append(out_c)
     torch.cuda.synchronize()
-    ck = np.swapaxes(ck_g.cpu().numpy().astype(np.float64), -1, -2)            # value-major, as the oracle
-    trunk_got = trunk_out.cpu().numpy().astype(np.float64)
-
     hs = list(range(H)) if heads is None else list(heads)
+    tr = lay["row_branch"] < 0
+    T = np.asarray(s["trunk_len"])
+    # whole-tensor checks on the device: branch rows untouched by the trunk pass, slots a
+    # tree never reaches untouched, slot 0 the zero state, the replays leave trunk rows
+    trg = torch.from_numpy(tr).cuda()
+    assert bool((trunk_out[~trg] == 7.0).all())
+    for ti in range(lay["n_trees"]):
+        reach = int(T[ti]) // C + 1
+        assert bool((ck_g[ti, 0] == 0.0).all()) and bool((ck_g[ti, reach:] == 5.0).all())
+    for o in outs:
+        assert torch.equal(o[trg], trunk_out[trg])
+    hsg = torch.tensor(hs, device="cuda")
+    ck = np.swapaxes(ck_g.index_select(2, hsg).cpu().numpy().astype(np.float64), -1, -2)  # value-major
+    trunk_got = trunk_out.index_select(1, hsg).cpu().numpy().astype(np.float64)
+
     sub = lambda a: np.ascontiguousarray(a[:, hs])
     t = inp["taps"].astype(np.float64)[:, hs]
     q, k, v = gdn_features_ref(lay, sub(widen(inp["xq"])), sub(widen(inp["xk"])), sub(widen(inp["xv"])),
                                t[0], t[1], t[2])
     al, be = sub(inp["alpha"].astype(np.float64)), sub(inp["beta"].astype(np.float64))
     ck_ref, o_ref = gdn_trunk_ref(lay, q, k, v, al, be, C)
-    tr = lay["row_branch"] < 0
-    T = np.asarray(s["trunk_len"])
-    # trunk outputs; branch rows untouched by the trunk pass
+    # trunk outputs
     scale = np.abs(o_ref[tr]).max()
-    err = np.abs(trunk_got[:, hs][tr] - o_ref[tr]).max()
+    err = np.abs(trunk_got[tr] - o_ref[tr]).max()
     say("  trunk outputs: max abs err %.3e (max |o| %.3e)" % (err, scale))
     assert err <= GDN_RTOL * scale
-    assert np.all(trunk_got[~tr] == 7.0)
-    # checkpoints every slot a tree reaches; the others untouched
+    # checkpoints: every slot a tree reaches
     for ti in range(lay["n_trees"]):
         reach = int(T[ti]) // C + 1
         cs = np.abs(ck_ref[ti, :reach]).max() if reach > 1 else 1.0
-        cerr = np.abs(ck[ti, :reach][:, hs] - ck_ref[ti, :reach]).max()
+        cerr = np.abs(ck[ti, :reach] - ck_ref[ti, :reach]).max()
         say("  tree %d: %d checkpoints, max abs err %.3e (max |S| %.3e)" % (ti, reach, cerr, cs))
         assert cerr <= GDN_RTOL * cs
-        assert np.all(ck[ti, 0] == 0.0)
-        assert np.all(ck[ti, reach:] == 5.0)
     # both replays from the GPU's checkpoints against the oracle's chained path
     br = lay["row_branch"] >= 0
-    want = gdn_replay_ref(lay, q, k, v, al, be, ck_ref, C) if br.any() else None
-    for name, o in zip(("token-at-a-time", "cached"), outs):
-        got = o.cpu().numpy().astype(np.float64)
-        if br.any():
+    if br.any():
+        want = gdn_replay_ref(lay, q, k, v, al, be, ck_ref, C)
+        for name, o in zip(("token-at-a-time", "cached"), outs):
+            got = o.index_select(1, hsg).cpu().numpy().astype(np.float64)
             bs = np.abs(want[br]).max()
-            berr = np.abs(got[:, hs][br] - want[br]).max()
+            berr = np.abs(got[br] - want[br]).max()
             say("  %s replay: max abs err %.3e (max |o| %.3e)" % (name, berr, bs))
             assert berr <= 2 * GDN_RTOL * bs
-        assert np.array_equal(got[tr], trunk_got[tr])                           # the replay leaves trunk rows
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
@@ -266,3 +272,14 @@ def test_gdn_trunk_workload_sampled_heads():
     cfg = CONFIGS["gqa8b"]
     say("gdn trunk pass + replay: 8B-like tree full size, heads 0, 17, 31")
     _trunk_compare(gen_structure(cfg), 32, 128, 4, 64, seed=cfg.seed, heads=[0, 17, 31])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["long", "batched", "stress"])
+def test_gdn_other_workloads_sampled_heads(name):
+    """The other workloads' trees at full size (a 16,384-token trunk; 8 trees of 2,048;
+    a 32,768-token trunk with widths 1..16 and 64 heads), trunk pass and both replays on
+    the GPU for all heads, two heads against the oracle."""
+    cfg = CONFIGS[name]
+    say("gdn trunk pass + replay: %s tree full size, %d heads, heads 1 and last" % (name, cfg.hq))
+    _trunk_compare(gen_structure(cfg), cfg.hq, 128, 4, 64, seed=cfg.seed, heads=[1, cfg.hq - 1])
