@@ -237,7 +237,7 @@ __device__ __forceinline__ void chunk_ap(ChunkLds<D, MT> &sm) {
 // or Q'[s][j] = e^{g_s} q_s[j] - (P W)[s][j]. Each thread touches only its own column of vf
 // (U threads) or of kf and qf (W threads), so epi may overwrite that column of
 // vf or qf. Threads 2D and up return at once.
-template <int D, int MT, class EpiX, class EpiY>
+template <int D, int MT, bool WITH_Y = true, class EpiX, class EpiY>
 __device__ __forceinline__ void chunk_solve(ChunkLds<D, MT> &sm, EpiX epi_x, EpiY epi_y) {
   const int j = threadIdx.x;
   if (j >= 2 * D) return;
@@ -270,6 +270,12 @@ __device__ __forceinline__ void chunk_solve(ChunkLds<D, MT> &sm, EpiX epi_x, Epi
   }
 #pragma unroll
   for (int s = 0; s < MT; ++s) epi_x(s, x[s]);
+  if (!WITH_Y) {  // x back into this thread's own right-hand-side column, for chunk_px_mfma
+    float *xc = const_cast<float *>(rhs);
+#pragma unroll
+    for (int s = 0; s < MT; ++s) xc[s * (D + 4)] = x[s];
+    return;
+  }
 #pragma unroll
   for (int s = 0; s < MT; ++s) {
     float acc = 0.f, acc2 = 0.f;
@@ -286,6 +292,41 @@ __device__ __forceinline__ void chunk_solve(ChunkLds<D, MT> &sm, EpiX epi_x, Epi
     const float qv = qcol[s * (D + 4)];
     epi_y(s, isv ? acc : sm.eg[s] * qv - acc);
     if (s % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// P [U | W] on the fp32 matrix cores, for the 64-row tile after chunk_solve<...,
+// false> has put [U | W] into the right-hand-side columns (U over v~, W over k~).
+// Output tiles of 16 rows x 16 columns, 16 per wave (wave w: columns 64w ..
+// 64w + 63, all in U or all in W); only the K blocks at or below the tile's rows
+// (P is lower-triangular). epi(s, col, isv, val) receives O'[s][col] or
+// Q'[s][col] = e^{g_s} q_s[col] - (P W)[s][col]. Starts with a barrier.
+template <int D, class Epi>
+__device__ __forceinline__ void chunk_px_mfma(ChunkLds<D, CT> &sm, Epi epi) {
+  lds_barrier();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+  constexpr int NTW = 2 * D / 16 / 4;  // 16-column tiles per wave
+#pragma unroll 1
+  for (int q = 0; q < NTW; ++q) {
+    const int col0 = 16 * (NTW * w + q);  // first of the tile's 2D columns
+    const bool isv = col0 < D;
+    const int cb = isv ? col0 : col0 - D;
+    const float *X = isv ? &sm.vf[0][cb + c] : &sm.kf[0][cb + c];
+#pragma unroll
+    for (int mt = 0; mt < CT / 16; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 4 * (mt + 1); ++st) {  // K rows r = 4 st + g <= 16 mt + 15
+        const int r = 4 * st + g;
+        acc = mfma4(sm.Pl[16 * mt + c][r], X[r * (D + 4)], acc);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int srow = 16 * mt + 4 * g + e;
+        const float y = acc[e];
+        epi(srow, cb + c, isv, isv ? y : sm.eg[srow] * sm.qf[srow][cb + c] - y);
+      }
+    }
   }
 }
 
@@ -313,15 +354,9 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(
   chunk_features<D, K, CT>(sm, [&](int p) { return off + p; }, p0, L, xq, xk, xv, taps, alpha,
                            beta, H, h);
   chunk_ap<D, CT>(sm);
-  {
-    const bool isv = tid < D;
-    const int col = isv ? tid : tid - D;
-    float *dx = rec_part<D>(ws, item, isv ? RU : RW) + col;  // U or W
-    float *dv = rec_part<D>(ws, item, isv ? RO : RQ) + col;  // O' or Q'
-    chunk_solve<D, CT>(sm, [&](int s, float x) { dx[s * D] = x; }, [&](int s, float val) { dv[s * D] = val; });
-  }
   // Kd_s = e^{g_{L-1} - g_s} k_s (g is flat past L, so g[CT-1] = g[L-1]), stored
-  // key-major; k~ row-major and g, for the branch replay
+  // key-major; k~ row-major and g, for the branch replay. Before the solve, which
+  // puts W over k~; the barrier keeps every read of k~ ahead of that.
   {
     float *kd = rec_part<D>(ws, item, RKD);
     float *kt = rec_part<D>(ws, item, RKF);
@@ -333,6 +368,17 @@ __global__ __launch_bounds__(256) void gdn_chunk_prep_kernel(
     }
   }
   if (tid < CT) glog[item * CT + tid] = sm.g[tid];
+  lds_barrier();
+  {
+    const bool isv = tid < D;
+    const int col = isv ? tid : tid - D;
+    float *dx = rec_part<D>(ws, item, isv ? RU : RW) + col;  // U or W
+    chunk_solve<D, CT, false>(sm, [&](int s, float x) { dx[s * D] = x; }, [](int, float) {});
+  }
+  {
+    float *ro = rec_part<D>(ws, item, RO), *rq = rec_part<D>(ws, item, RQ);
+    chunk_px_mfma<D>(sm, [&](int s, int col, bool isv, float val) { (isv ? ro : rq)[s * D + col] = val; });
+  }
   if (tid == 0) gam[item] = sm.eg[CT - 1];
 }
 
