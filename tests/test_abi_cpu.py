@@ -221,3 +221,23 @@ def test_gdn_trunk_argument_checks(tas):
     assert call(32, 128, 4, 64, nbytes=1000) == 3   # SPEC_ERR_WORKSPACE: too small
     assert n.value == query(32, 128, 64)[1]
     assert call(32, 128, 4, 64, work=ctypes.c_void_p(0x1004)) == 1
+
+
+def test_gdn_replay_cache_argument_checks(tas):
+    """spec_gdn_replay_fwd with a trunk-pass cache: rejected for chunk > 64 (no cache exists
+    there) and for a misaligned cache, before any launch."""
+    from tree_attention_spec_amd import _lib
+    lib = tas.library()
+    L = _query_layout(tas)
+    P = ctypes.c_void_p(0x1000)
+    fake = ctypes.cast(ctypes.c_void_p(0x1000), _lib._i32p)
+    for f in ("tree_off", "branch_tree", "branch_anchor", "branch_len", "branch_off", "branch_order"):
+        setattr(L, f, fake)
+
+    def call(C, cache):
+        return lib.spec_gdn_replay_fwd(ctypes.byref(L), 32, 128, 4, C, P, P, P, P, P, P, P, cache, P, None)
+
+    assert call(128, P) == 1
+    assert "chunk <= 64" in lib.spec_last_error().decode()
+    assert call(64, ctypes.c_void_p(0x1004)) == 1
+    assert "aligned" in lib.spec_last_error().decode()
