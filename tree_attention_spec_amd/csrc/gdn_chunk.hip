@@ -24,7 +24,8 @@
 //   scan (tree, head, 16 value rows): S <- gamma S + (U - W S^T)^T Kd over the
 //        full chunks in order on the fp32 matrix cores, storing each end state
 //        as the next checkpoint.
-//   out  (tree, chunk, head): o = Q' S_c^T + O' from checkpoint c.
+//   out  (tree, chunk, head): o = Q' S_c^T + O' from checkpoint c, on the
+//        fp32 matrix cores.
 // A chunk tile always has 64 rows; rows past the chunk's tokens are zero.
 // Intermediates live in a caller-provided workspace, which also keeps, per
 // chunk, the deltas, the normalised keys and g for the branch replay below.
@@ -517,24 +518,28 @@ __global__ __launch_bounds__(256) void gdn_chunk_scan_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// out: one workgroup of 256 per (tree, chunk, head): o = Q' S_c^T + O'.
+// out: one workgroup of 256 per (tree, chunk, head): o = Q' S_c^T + O' on the
+// fp32 matrix cores, as 16 x 16 output tiles (tokens x value rows); wave w takes
+// the value-row tiles D/64 w .. and all four token tiles of each, so a lane's
+// column of S_c (16 consecutive value rows of one key per load, from the
+// key-major checkpoint) is loaded once and used four times. Q' comes through LDS.
 template <int D>
 __global__ __launch_bounds__(256) void gdn_chunk_out_kernel(
     const int32_t *__restrict__ tree_off, const int32_t *__restrict__ tree_trunk_len,
     const float *__restrict__ ws, const float *__restrict__ ckpt, float *__restrict__ out, int H,
     int chunk, int n_chunks, int n_ckpt) {
-  constexpr int LD = D + 4, G = 256 / D, RPT = CT / G;
+  constexpr int LD = D + 4, KG = D / 4, NTW = D / 64;  // value-row tiles per wave
   __shared__ __attribute__((aligned(16))) float Ql[CT][LD];
   const int64_t item = blockIdx.x;
   const int h = (int)(item % H);
-  const int c = (int)((item / H) % n_chunks);
+  const int ch = (int)((item / H) % n_chunks);
   const int t = (int)(item / ((int64_t)H * n_chunks));
   const int T = tree_trunk_len[t];
-  const int p0 = c * chunk;
+  const int p0 = ch * chunk;
   if (p0 >= T) return;
   const int L = min(chunk, T - p0);
   const int off = tree_off[t];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, cc = lane & 15;
   {
     const float4 *q4 = reinterpret_cast<const float4 *>(rec_part<D>(ws, item, RQ));
     for (int i = tid; i < CT * D / 4; i += 256) {
@@ -542,36 +547,35 @@ __global__ __launch_bounds__(256) void gdn_chunk_out_kernel(
       *reinterpret_cast<float4 *>(&Ql[e / D][e % D]) = q4[i];
     }
   }
-  const int v = tid % D, sg = tid / D;  // sg is uniform across a wave
   const float *op = rec_part<D>(ws, item, RO);
-  float acc[RPT];
-#pragma unroll
-  for (int i = 0; i < RPT; ++i) acc[i] = op[(sg + G * i) * D + v];
+  const float *Sc = ckpt + (((int64_t)t * n_ckpt + ch) * H + h) * (int64_t)D * D;
   lds_barrier();
-  const float *sc = ckpt + (((int64_t)t * n_ckpt + c) * H + h) * (int64_t)D * D + v;
 #pragma unroll 1
-  for (int k0 = 0; k0 < D; k0 += 32) {
-    float sr[32];
+  for (int q = 0; q < NTW; ++q) {
+    const int nt = NTW * w + q;
+    float bv[KG];  // S_c[16 nt + cc][g KG + i]: key-major, so 16 lanes read 16 consecutive floats
 #pragma unroll
-    for (int kk = 0; kk < 32; ++kk) sr[kk] = sc[(int64_t)(k0 + kk) * D];
+    for (int i = 0; i < KG; ++i) bv[i] = Sc[(int64_t)(g * KG + i) * D + 16 * nt + cc];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int s = sg + G * i;
+    for (int mt = 0; mt < CT / 16; ++mt) {
+      if (16 * mt >= L) break;  // uniform
+      f32x4 acc;
 #pragma unroll
-      for (int kk = 0; kk < 32; kk += 4) {
-        const float4 q4 = ld4(&Ql[s][k0 + kk]);
-        acc[i] = fmaf(q4.x, sr[kk], acc[i]);
-        acc[i] = fmaf(q4.y, sr[kk + 1], acc[i]);
-        acc[i] = fmaf(q4.z, sr[kk + 2], acc[i]);
-        acc[i] = fmaf(q4.w, sr[kk + 3], acc[i]);
+      for (int e = 0; e < 4; ++e) acc[e] = op[(16 * mt + 4 * g + e) * D + 16 * nt + cc];
+#pragma unroll
+      for (int i = 0; i < KG / 4; ++i) {
+        const float4 qa = ld4(&Ql[16 * mt + cc][g * KG + 4 * i]);
+        acc = mfma4(qa.x, bv[4 * i], acc);
+        acc = mfma4(qa.y, bv[4 * i + 1], acc);
+        acc = mfma4(qa.z, bv[4 * i + 2], acc);
+        acc = mfma4(qa.w, bv[4 * i + 3], acc);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int s = sg + G * i;
-    if (s < L) out[((int64_t)(off + p0 + s) * H + h) * D + v] = acc[i];
+      for (int e = 0; e < 4; ++e) {
+        const int s = 16 * mt + 4 * g + e;
+        if (s < L) out[((int64_t)(off + p0 + s) * H + h) * D + 16 * nt + cc] = acc[e];
+      }
+    }
   }
 }
 
