@@ -520,9 +520,10 @@ __global__ __launch_bounds__(256) void gdn_chunk_scan_kernel(
 // ---------------------------------------------------------------------------
 // out: one workgroup of 256 per (tree, chunk, head): o = Q' S_c^T + O' on the
 // fp32 matrix cores, as 16 x 16 output tiles (tokens x value rows); wave w takes
-// the value-row tiles D/64 w .. and all four token tiles of each, so a lane's
-// column of S_c (16 consecutive value rows of one key per load, from the
-// key-major checkpoint) is loaded once and used four times. Q' comes through LDS.
+// the D/64 adjacent value-row tiles from D/64 w on and all four token tiles of
+// each, so a lane's columns of S_c (16 consecutive value rows of one key per
+// load, from the key-major checkpoint) are loaded once and used four times. Q'
+// comes through LDS.
 template <int D>
 __global__ __launch_bounds__(256) void gdn_chunk_out_kernel(
     const int32_t *__restrict__ tree_off, const int32_t *__restrict__ tree_trunk_len,
@@ -550,32 +551,40 @@ __global__ __launch_bounds__(256) void gdn_chunk_out_kernel(
   const float *op = rec_part<D>(ws, item, RO);
   const float *Sc = ckpt + (((int64_t)t * n_ckpt + ch) * H + h) * (int64_t)D * D;
   lds_barrier();
-#pragma unroll 1
-  for (int q = 0; q < NTW; ++q) {
-    const int nt = NTW * w + q;
-    float bv[KG];  // S_c[16 nt + cc][g KG + i]: key-major, so 16 lanes read 16 consecutive floats
+  // the wave's NTW adjacent value-row tiles together, so that the loads of S_c and O'
+  // for them cover whole cache lines at once: S_c[16 nt + cc][g KG + i] (key-major, 16
+  // lanes read 16 consecutive floats per tile)
+  float bv[NTW][KG];
 #pragma unroll
-    for (int i = 0; i < KG; ++i) bv[i] = Sc[(int64_t)(g * KG + i) * D + 16 * nt + cc];
+  for (int q = 0; q < NTW; ++q)
 #pragma unroll
-    for (int mt = 0; mt < CT / 16; ++mt) {
-      if (16 * mt >= L) break;  // uniform
-      f32x4 acc;
+    for (int i = 0; i < KG; ++i) bv[q][i] = Sc[(int64_t)(g * KG + i) * D + 16 * (NTW * w + q) + cc];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = op[(16 * mt + 4 * g + e) * D + 16 * nt + cc];
+  for (int mt = 0; mt < CT / 16; ++mt) {
+    if (16 * mt >= L) break;  // uniform
+    f32x4 acc[NTW];
 #pragma unroll
-      for (int i = 0; i < KG / 4; ++i) {
-        const float4 qa = ld4(&Ql[16 * mt + cc][g * KG + 4 * i]);
-        acc = mfma4(qa.x, bv[4 * i], acc);
-        acc = mfma4(qa.y, bv[4 * i + 1], acc);
-        acc = mfma4(qa.z, bv[4 * i + 2], acc);
-        acc = mfma4(qa.w, bv[4 * i + 3], acc);
+    for (int q = 0; q < NTW; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[q][e] = op[(16 * mt + 4 * g + e) * D + 16 * (NTW * w + q) + cc];
+#pragma unroll
+    for (int i = 0; i < KG / 4; ++i) {
+      const float4 qa = ld4(&Ql[16 * mt + cc][g * KG + 4 * i]);
+#pragma unroll
+      for (int q = 0; q < NTW; ++q) {
+        acc[q] = mfma4(qa.x, bv[q][4 * i], acc[q]);
+        acc[q] = mfma4(qa.y, bv[q][4 * i + 1], acc[q]);
+        acc[q] = mfma4(qa.z, bv[q][4 * i + 2], acc[q]);
+        acc[q] = mfma4(qa.w, bv[q][4 * i + 3], acc[q]);
       }
+    }
+#pragma unroll
+    for (int q = 0; q < NTW; ++q)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int s = 16 * mt + 4 * g + e;
-        if (s < L) out[((int64_t)(off + p0 + s) * H + h) * D + 16 * nt + cc] = acc[e];
+        if (s < L) out[((int64_t)(off + p0 + s) * H + h) * D + 16 * (NTW * w + q) + cc] = acc[q][e];
       }
-    }
   }
 }
 
