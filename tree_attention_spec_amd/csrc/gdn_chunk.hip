@@ -649,7 +649,7 @@ __global__ __launch_bounds__(256, MT == 16 ? 3 : 1) void gdn_replay_chunk_kernel
   // flight during Y
   float bv0[KG];
   {
-    const float *sb = Sc + (int64_t)(g * KG) * D + 16 * (w / MTT) + cc;
+    const float *sb = Sc + (int64_t)(g * KG) * D + 16 * ((PER * w) / MTT) + cc;
 #pragma unroll
     for (int i = 0; i < KG; ++i) bv0[i] = sb[(int64_t)i * D];
   }
@@ -672,11 +672,12 @@ __global__ __launch_bounds__(256, MT == 16 ? 3 : 1) void gdn_replay_chunk_kernel
 #pragma unroll
     for (int r = 0; r < 4; ++r) Yl[16 * mt + 4 * g + r][16 * rt + cc] = y[r] * f;
   }
-  // Q' S_c^T into this wave's output tiles (w, w + 4, ...)
+  // Q' S_c^T into this wave's output tiles PER w .. PER w + PER - 1 (adjacent value
+  // rows, so a wave's loads of S_c and Delta use whole cache lines between them)
   f32x4 acc[PER];
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
-    const int ot = w + 4 * p, mt = ot % MTT, nt = ot / MTT;
+    const int ot = PER * w + p, mt = ot % MTT, nt = ot / MTT;
     const float *sb = Sc + (int64_t)(g * KG) * D + 16 * nt + cc;  // key g KG + i, value 16 nt + cc
     acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
@@ -694,7 +695,7 @@ __global__ __launch_bounds__(256, MT == 16 ? 3 : 1) void gdn_replay_chunk_kernel
   // Delta rows 4 st + g of the first output tile, in flight across the barrier
   float dv0[16];
   if (j > 0) {  // uniform; chunk c's cache exists
-    const float *dl = rec_part<D>(ws, citem, RDL) + g * D + 16 * (w / MTT) + cc;
+    const float *dl = rec_part<D>(ws, citem, RDL) + g * D + 16 * ((PER * w) / MTT) + cc;
 #pragma unroll
     for (int st = 0; st < 16; ++st) dv0[st] = dl[(4 * st) * D];
   }
@@ -703,7 +704,7 @@ __global__ __launch_bounds__(256, MT == 16 ? 3 : 1) void gdn_replay_chunk_kernel
   const int nsteps = (j + 3) / 4;  // replayed rows r = 4 s + g
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
-    const int ot = w + 4 * p, mt = ot % MTT, nt = ot / MTT;
+    const int ot = PER * w + p, mt = ot % MTT, nt = ot / MTT;
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[p][r] = eG * acc[p][r] + sm.vf[16 * mt + 4 * g + r][16 * nt + cc];
     if (p == 0) {
