@@ -21,9 +21,10 @@
 // chunks at once; only S_end chains the chunks. Three kernels:
 //   prep (tree, chunk, head): features of the chunk's tokens (convolution along
 //        the trunk, SiLU, L2 norms), A and P, the triangular solve, Q', O', Kd.
-//   scan (tree, head, 16 value rows): S <- gamma S + (U - W S^T)^T Kd over the
-//        full chunks in order on the fp32 matrix cores, storing each end state
-//        as the next checkpoint.
+//   scan (tree, head, 16 value rows): delta = U - W S^T and S <- gamma S +
+//        delta^T Kd over the chunks in order on the fp32 matrix cores, storing
+//        each full chunk's end state as the next checkpoint (and every chunk's
+//        delta, a last partial one included, for the replay).
 //   out  (tree, chunk, head): o = Q' S_c^T + O' from checkpoint c, on the
 //        fp32 matrix cores.
 // A chunk tile always has 64 rows; rows past the chunk's tokens are zero.
@@ -35,7 +36,8 @@
 // after it through a, then takes its own tokens). With c = floor((a+1)/C) and
 // j = a + 1 - cC replayed tokens of chunk c, the state after the anchor is
 //   S_a = e^{G} S_c + sum_{r<j} e^{G - g_r} delta_r k_r^T,   G = g_{j-1},
-// where delta_r are chunk c's own deltas (they depend only on tokens before r).
+// where delta_r are chunk c's own deltas (delta_r depends only on S_c and the
+// chunk's tokens up to r, so the first j of them are the replayed tokens' updates).
 // The branch's m = W - 1 tokens are one more chunk that starts from S_a: with
 // its Q', O' from the same in-chunk algebra, its outputs are
 //   o = Q' S_a^T + O' = e^{G} Q' S_c^T + (Q' K'^T) Delta + O',  K'_r = e^{G - g_r} k_r,
@@ -235,9 +237,11 @@ __device__ __forceinline__ void chunk_ap(ChunkLds<D, MT> &sm) {
 // thread j < D takes column j of U, thread D + j column j of W (rows of A and
 // P are LDS broadcasts). For each row s, epi_x(s, x) receives the thread's
 // entry x of U or W, then epi_y(s, val) receives val = O'[s][j] = (P U)[s][j]
-// or Q'[s][j] = e^{g_s} q_s[j] - (P W)[s][j]. Each thread touches only its own column of vf
-// (U threads) or of kf and qf (W threads), so epi may overwrite that column of
-// vf or qf. Threads 2D and up return at once.
+// or Q'[s][j] = e^{g_s} q_s[j] - (P W)[s][j]. Each thread touches only its own
+// column of vf (U threads) or of kf and qf (W threads), so epi may overwrite that
+// column of vf or qf. With WITH_Y false the P product is left out and the
+// thread's column of [U | W] is written back over its right-hand-side column
+// (for chunk_px_mfma). Threads 2D and up return at once.
 template <int D, int MT, bool WITH_Y = true, class EpiX, class EpiY>
 __device__ __forceinline__ void chunk_solve(ChunkLds<D, MT> &sm, EpiX epi_x, EpiY epi_y) {
   const int j = threadIdx.x;
