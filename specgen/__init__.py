@@ -2,7 +2,8 @@
 
 This package is the only code shared by the CPU oracle and the HIP path. It
 draws tree structures, Q/K/V tensors, logit rows and GDN replay inputs from
-counter-addressed NumPy PCG64 streams and rounds them to bfloat16 where a
+counter-addressed NumPy PCG64 streams (hidden states
+and output heads too) and rounds them to bfloat16 where a
 workload asks for it.
 It holds none of the method's arithmetic (no packing, attention or loss).
 """
@@ -12,6 +13,8 @@ from .gen import (  # noqa: F401
     f32_to_bf16_bits,
     gen_gdn,
     gen_gdn_states,
+    gen_head,
+    gen_head_draft_rows,
     gen_logits,
     gen_logit_rows,
     gen_qkv,

@@ -2,8 +2,9 @@
 
 Every array is drawn from NumPy's PCG64 seeded by
 ``SeedSequence(seed, spawn_key=(stream, chunk))``: the stream names the
-tensor (0 structure, 1 Q, 2 K, 3 V, 4 draft logits, 5 teacher logits) and the
-chunk is a fixed block of rows. Any chunk can therefore be regenerated alone
+tensor (0 structure, 1 Q, 2 K, 3 V, 4 draft logits, 5 teacher logits, 6-11
+GDN inputs, 12-14 hidden states, output head and draft logits of the head
+workloads) and the chunk is a fixed block of rows. Any chunk can therefore be regenerated alone
 (the oracle uses this to rebuild sampled logit rows), and the bytes do not
 depend on how many threads fill the chunks.
 
@@ -24,6 +25,8 @@ LOGIT_CHUNK_ROWS = 8
 
 _S_STRUCT, _S_Q, _S_K, _S_V, _S_DRAFT, _S_TEACHER = range(6)
 _S_GDN_Q, _S_GDN_K, _S_GDN_V, _S_GDN_TAPS, _S_GDN_GATES, _S_GDN_STATE = range(6, 12)
+_S_HIDDEN, _S_HEAD, _S_HEAD_DRAFT = range(12, 15)
+HEAD_CHUNK_ROWS = 1024
 
 
 def _workers() -> int:
@@ -222,3 +225,46 @@ def gen_gdn_states(seed: int, n_states: int, heads: int, head_dim: int, std: flo
     with ThreadPoolExecutor(_workers()) as ex:
         list(ex.map(fill, range(n_states)))
     return st
+
+
+def _fill_scaled_bf16(out_rows: np.ndarray, seed: int, stream: int, chunk: int, std: float):
+    x = _rng(seed, stream, chunk).standard_normal(out_rows.shape, dtype=np.float32)
+    out_rows[...] = f32_to_bf16_bits(np.float32(std) * x)
+
+
+def _chunked_bf16(shape, chunk_rows: int, seed: int, stream: int, std: float) -> np.ndarray:
+    arr = np.empty(shape, dtype=np.uint16)
+    jobs = [(arr[r0:r0 + chunk_rows], c) for c, r0 in enumerate(range(0, shape[0], chunk_rows))]
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(lambda j: _fill_scaled_bf16(j[0], seed, stream, j[1], std), jobs))
+    return arr
+
+
+def gen_head(seed: int, n_rows: int, d_model: int, vocab: int, n_steps: int, logit_std: float = 3.0):
+    """Inputs of E2E-TV scored from hidden states through an output head.
+
+    Returns a dict of uint16 bfloat16 bit patterns:
+      hidden  [N, d_model] N(0,1): final hidden states of every packed row;
+      head    [V, d_model] N(0, (logit_std / sqrt(d_model))^2): the output head,
+              so that a teacher logit has standard deviation about logit_std;
+      draft   [R, V] N(0, logit_std^2): draft logits, one row per supervised step.
+    """
+    return {
+        "hidden": _chunked_bf16((n_rows, d_model), HEAD_CHUNK_ROWS, seed, _S_HIDDEN, 1.0),
+        "head": _chunked_bf16((vocab, d_model), HEAD_CHUNK_ROWS, seed, _S_HEAD,
+                              logit_std / np.sqrt(d_model)),
+        "draft": _chunked_bf16((n_steps, vocab), LOGIT_CHUNK_ROWS, seed, _S_HEAD_DRAFT, logit_std),
+    }
+
+
+def gen_head_draft_rows(seed: int, n_steps: int, vocab: int, rows, logit_std: float = 3.0):
+    """Regenerate only the given rows of gen_head's draft logits (bf16 bit patterns [k, V])."""
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.empty((len(rows), vocab), dtype=np.uint16)
+    for c in np.unique(rows // LOGIT_CHUNK_ROWS):
+        n = min(LOGIT_CHUNK_ROWS, n_steps - c * LOGIT_CHUNK_ROWS)
+        blk = np.empty((n, vocab), dtype=np.uint16)
+        _fill_scaled_bf16(blk, seed, _S_HEAD_DRAFT, int(c), logit_std)
+        sel = rows // LOGIT_CHUNK_ROWS == c
+        out[sel] = blk[rows[sel] - c * LOGIT_CHUNK_ROWS]
+    return out
