@@ -10,6 +10,7 @@ recorded by the library on the stream it launches on, inside the timed steps.
 
     python bench.py [--steps K] [--warmup W] [--config gqa8b] [--no-cpu-baseline]
     python bench.py --gdn [--config gqa8b]   # GDN scoring: trunk pass + indexed replay
+    python bench.py --head [--config gqa8b]  # E2E-TV through the output head
 
 Prints one JSON line. Only one GPU is supported (--gpus must be 1).
 """
@@ -84,6 +85,10 @@ MARK_KERNELS = {
     "e2etv_stats": (["e2etv_team_clear", "e2etv_stats_team_kernel", "e2etv_stats_kernel"], ("e2etv.hip",)),
     "e2etv_scan": (["e2etv_scan_kernel"], ("e2etv.hip",)),
     "e2etv_grad": (["e2etv_grad_kernel"], ("e2etv.hip",)),
+    "e2etv_head_lse": (["e2etv_head_lse_kernel"], ("e2etv_head.hip",)),
+    "e2etv_head_merge": (["e2etv_head_merge_kernel"], ("e2etv_head.hip",)),
+    "e2etv_head_tv": (["e2etv_head_tv_kernel"], ("e2etv_head.hip",)),
+    "e2etv_head_sum": (["e2etv_head_sum_kernel"], ("e2etv_head.hip",)),
     "gdn_trunk": (["gdn_trunk_kernel"], ("gdn.hip", "gdn_util.h")),
     "gdn_chunk_prep": (["gdn_chunk_prep_kernel"], ("gdn_chunk.hip", "gdn_util.h")),
     "gdn_chunk_scan": (["gdn_chunk_scan_kernel"], ("gdn_chunk.hip", "gdn_util.h")),
@@ -394,6 +399,112 @@ def gdn_bench(args, cfg, s, dev):
     }
 
 
+def head_bench(args, cfg, s, dev):
+    """E2E-TV scored from hidden states through an output head (readout, head product and
+    E2E-TV fused; teacher logits never stored): the workload's supervised steps, hidden size
+    cfg.hq * cfg.head_dim, vocabulary cfg.vocab, bf16 draft logits, gradient written."""
+    import numpy as np
+    import torch
+    import tree_attention_spec_amd as tas
+    from specgen import gen_head
+
+    tree = tas.spec_tree_pack(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"])
+    N, R, V, d = tree.n_rows, tree.n_steps, cfg.vocab, cfg.hq * cfg.head_dim
+    log("E2E-TV through the head: R=%d steps, N=%d rows, d_model=%d, V=%d; generating inputs"
+        % (R, N, d, V))
+    inp = gen_head(cfg.seed, N, d, V, R)
+    x = {k: torch.from_numpy(inp[k].view(np.int16)).to(dev).view(torch.bfloat16)
+         for k in ("draft", "hidden", "head")}
+    alpha = torch.empty(R, dtype=torch.float32, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    grad = torch.empty((R, V), dtype=torch.float32, device=dev)
+    work = torch.empty(tas.e2etv_head_work_bytes(tree, V, d), dtype=torch.uint8, device=dev)
+
+    def call():
+        tas.spec_e2etv_head_fwd_bwd(tree, x["draft"], x["hidden"], x["head"], alpha_out=alpha,
+                                    loss_out=loss, grad_out=grad, work=work)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    timers = [tas.KernelTimer(capacity=12) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        with timers[i]:
+            call()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    per = {}
+    for tm in timers:
+        for n, dd in tm.durations():
+            per.setdefault(n, []).append(dd)
+    kms = {n: sum(v) / len(v) for n, v in per.items()}
+    for k in kms:
+        log("%s %.4f ms" % (k, kms[k]))
+    gemm = 2.0 * R * d * V           # one pass of the head product
+    dom = max(("e2etv_head_lse", "e2etv_head_tv"), key=kms.get)
+    tf = gemm / (kms[dom] * 1e-3) / 1e12
+    kern = {k: {"ms": kms[k], "traffic": measured_traffic(k, source_hash(*MARK_KERNELS[k][1]), args.config)}
+            for k in kms if k in MARK_KERNELS}
+    for k in ("e2etv_head_lse", "e2etv_head_tv"):
+        kern[k]["tflops"] = gemm / (kms[k] * 1e-3) / 1e12
+        kern[k]["frac"] = kern[k]["tflops"] / PEAK_BF16_TFLOPS
+    return {
+        "metric": "E2E-TV rows/s from hidden states and output head (fwd + grad)",
+        "value": R / (ms_per_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded inputs)",
+        "config": {"workload": cfg.name + " tree, E2E-TV through the output head", "steps": R,
+                   "n_rows": N, "d_model": d, "vocab": V, "draft_dtype": "bf16",
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
+                     "algorithmic_flop_per_launch": gemm,
+                     "traffic": measured_traffic(dom, source_hash(*MARK_KERNELS[dom][1]), args.config)},
+        "kernels": kern,
+        **({} if args.no_cpu_baseline else {"cpu_baseline": head_cpu_baseline(s, inp, R)}),
+    }
+
+
+def head_cpu_baseline(s, inp, R, n_sample=32):
+    """The head-path oracle on a bounded sample: the first n_sample steps' teacher logits
+    (float64 product over the whole head, in vocabulary blocks) and their E2E-TV statistics,
+    scaled to all steps."""
+    import numpy as np
+    from oracle import e2etv_row_stats_ref, head_logits_ref, pack_ref
+    from specgen import bf16_bits_to_f32
+
+    log("timing the head oracle on %d steps" % n_sample)
+    lay = pack_ref(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"])
+    wid = lambda a: bf16_bits_to_f32(a).astype(np.float64)
+    rows = np.arange(n_sample)
+    V = inp["head"].shape[0]
+    t0 = time.perf_counter()
+    hidden = wid(inp["hidden"])
+    y = np.empty((n_sample, V))
+    for v0 in range(0, V, 16384):
+        y[:, v0:v0 + 16384] = head_logits_ref(lay, hidden, wid(inp["head"][v0:v0 + 16384]), steps=rows)
+    e2etv_row_stats_ref(wid(inp["draft"][:n_sample]), y)
+    total = (time.perf_counter() - t0) * R / n_sample
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    return {"value": R / total, "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "sample": "the first %d of %d steps: float64 NumPy head product over the whole vocabulary "
+                      "(BLAS threads) and the E2E-TV row statistics, scaled to all steps" % (n_sample, R),
+            "seconds_full_estimate": total, "host_cpus": len(os.sched_getaffinity(0))}
+
+
 def gdn_cpu_baseline(s, inp, C, n_rows, per_thread=2):
     """The GDN oracle on a bounded sample: features of every packed row, the whole
     trunk pass (heads split over the host threads), then the replay of per_thread
@@ -449,6 +560,8 @@ def main():
     ap.add_argument("--gdn", action="store_true",
                     help="time GDN scoring of the workload's tree (spec_gdn_trunk_fwd, then spec_gdn_replay_fwd) "
                          "instead of the attention + E2E-TV step, and print its own JSON line")
+    ap.add_argument("--head", action="store_true",
+                    help="E2E-TV from hidden states through the output head (fused readout, product, E2E-TV)")
     ap.add_argument("--gdn-token-replay", action="store_true",
                     help="with --gdn: replay a token at a time instead of from the trunk pass's cache")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -494,6 +607,9 @@ def main():
     s = gen_structure(cfg)
     if args.gdn:
         print(json.dumps(gdn_bench(args, cfg, s, dev)), flush=True)
+        return
+    if args.head:
+        print(json.dumps(head_bench(args, cfg, s, dev)), flush=True)
         return
     layout, mem_bytes = tas.spec_tree_pack_query(s["trunk_len"], s["n_branches"], s["anchors"],
                                                  s["branch_len"])

@@ -6,6 +6,8 @@
  *   spec_tree_attn_fwd  tree-masked GQA attention, RoPE at semantic positions,
  *                       optional predecessor-row readout
  *   spec_e2etv_fwd_bwd  E2E-TV overlap, prefix-product loss and its gradient
+ *   spec_e2etv_head_fwd_bwd  the same with the teacher logits formed through an
+ *                       output head from hidden states (never stored)
  *                       with respect to the draft logits
  *
  * Sources, cited by page title and section:
@@ -43,7 +45,7 @@
 extern "C" {
 #endif
 
-#define SPEC_TREE_ABI_VERSION 4
+#define SPEC_TREE_ABI_VERSION 5
 #define SPEC_MAX_BRANCH_LEN 64 /* largest supported branch width W_b */
 
 typedef enum spec_status {
@@ -230,6 +232,46 @@ spec_status spec_e2etv_fwd_bwd(const spec_tree_layout *layout, int64_t vocab,
                                const void *d_teacher, float inv_norm, float *d_alpha,
                                float *d_loss, float *d_grad, void *d_work, size_t *work_bytes,
                                spec_stream stream);
+
+/*
+ * spec_e2etv_head_fwd_bwd -- E2E-TV with the teacher logits read through an
+ * output head: the predecessor readout, the head product and E2E-TV fused, so
+ * the teacher logits never reach memory.
+ *
+ * Defines: [SpecOPD notes page, "Inputs and code mapping"] (prediction logits
+ * are formed from hidden states and a head the caller supplies; E2E-TV takes
+ * logits aligned by history) and [SpecOPD paper page, Figure 3] (step (b,i)
+ * is read from its predecessor's row, the anchor row for i = 1):
+ *   y[s, v] = sum_k hidden[step_pred_row[s], k] * head[v, k]
+ * then alpha, L and the gradient exactly as spec_e2etv_fwd_bwd with teacher
+ * logits y. The products run on bf16 MFMA with float32 sums.
+ *
+ * Arguments:
+ *   layout        from spec_tree_pack (uses n_steps, n_branches,
+ *                 max_branch_len, step_off, step_pred_row).
+ *   vocab         V >= 8, a multiple of 8.
+ *   d_model       hidden size, a positive multiple of 64.
+ *   draft_dtype   SPEC_BF16 or SPEC_F32: the dtype of d_draft.
+ *   d_draft       [R, V] draft logits; NaN or -inf mean inactive support.
+ *   d_hidden      [N, d_model] bf16 final hidden states of every packed row
+ *                 (N = layout n_rows); only steps' predecessor rows are read.
+ *   d_head        [V, d_model] bf16 output head (row v gives logit v).
+ *   inv_norm      <= 0 selects 1/R; otherwise used as given.
+ *   d_alpha       [R] float32 out; d_loss: [1] float32 out.
+ *   d_grad        optional [R, V] float32 out, dL/d draft logits (NULL: forward only).
+ *   d_work        workspace of *work_bytes bytes, or NULL for a size query.
+ * All device buffers 16-byte aligned. Calls that share a workspace must not
+ * overlap in time. Data preconditions (not checked; violations give NaN):
+ * hidden and head finite, at least one active draft entry per row.
+ * Errors: SPEC_ERR_INVALID_ARG, SPEC_ERR_UNSUPPORTED (vocab or d_model not a
+ * multiple of 8 or 64, branches longer than 64 steps, draft dtype),
+ * SPEC_ERR_WORKSPACE, SPEC_ERR_HIP.
+ */
+spec_status spec_e2etv_head_fwd_bwd(const spec_tree_layout *layout, int64_t vocab,
+                                    int32_t d_model, spec_dtype draft_dtype, const void *d_draft,
+                                    const void *d_hidden, const void *d_head, float inv_norm,
+                                    float *d_alpha, float *d_loss, float *d_grad, void *d_work,
+                                    size_t *work_bytes, spec_stream stream);
 
 /*
  * spec_gdn_replay_fwd -- indexed GDN state replay: the linear-attention

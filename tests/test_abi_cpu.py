@@ -153,6 +153,28 @@ def test_e2etv_size_query_and_checks(tas):
                                   ctypes.c_void_p(0x1000), ctypes.byref(big), None) == 1
 
 
+def test_e2etv_head_size_query_and_checks(tas):
+    """spec_e2etv_head_fwd_bwd: size query and argument checks, no GPU touched."""
+    lib = tas.library()
+    L = _query_layout(tas)
+    size = ctypes.c_size_t(0)
+    call = lambda V, d, dt, w=0.0, work=None, sz=size: lib.spec_e2etv_head_fwd_bwd(
+        ctypes.byref(L), V, d, dt, None, None, None, w, None, None, None, work, ctypes.byref(sz), None)
+    assert call(151936, 4096, 1) == 0
+    R = L.n_steps
+    # four [R] arrays, [R][V/64] float4 partials, R float64 sums and the bitmask
+    assert size.value >= 4 * 4 * R + 16 * R * (151936 // 64) + 8 * R + R * 151936 // 8
+    assert call(0, 4096, 1) == 1                  # empty vocabulary
+    assert call(151936, 0, 1) == 1                # no hidden dimensions
+    assert call(151932, 4096, 1) == 2             # vocab not a multiple of 8
+    assert call(151936, 4000, 1) == 2             # d_model not a multiple of 64
+    assert call(151936, 4096, 3) == 2             # unsupported draft dtype
+    assert call(151936, 4096, 1, float("inf")) == 1
+    big = ctypes.c_size_t(1 << 40)
+    # a workspace with a layout that has no device arrays is refused before any launch
+    assert call(151936, 4096, 1, work=ctypes.c_void_p(0x1000), sz=big) == 1
+
+
 def test_gdn_argument_checks(tas):
     """spec_gdn_replay_fwd rejects bad arguments before any launch (no GPU is touched)."""
     from tree_attention_spec_amd import _lib

@@ -20,6 +20,7 @@ from ._lib import (LAYOUT_ARRAYS, SPEC_BF16, SPEC_F32, SPEC_MAX_BRANCH_LEN, Spec
                    spec_tree_layout)
 
 __all__ = ["spec_tree_pack", "spec_tree_pack_query", "spec_tree_attn_fwd", "spec_e2etv_fwd_bwd",
+           "spec_e2etv_head_fwd_bwd", "e2etv_head_work_bytes",
            "spec_gdn_trunk_fwd", "spec_gdn_replay_fwd", "gdn_checkpoint_slots", "gdn_trunk_work_bytes", "PackedTree", "SpecError", "library",
            "KernelTimer"]
 
@@ -208,6 +209,56 @@ def spec_e2etv_fwd_bwd(tree: PackedTree, draft: torch.Tensor, teacher: torch.Ten
                                            float(inv_norm), ptr(alpha_out), ptr(loss_out),
                                            ptr(grad_out), ptr(work), ctypes.byref(nbytes),
                                            ctypes.c_void_p(_stream(dev))))
+    return alpha_out, loss_out, grad_out
+
+
+def e2etv_head_work_bytes(tree, vocab, d_model, draft_dtype=torch.bfloat16) -> int:
+    lib = library()
+    nbytes = ctypes.c_size_t(0)
+    dt = SPEC_BF16 if draft_dtype == torch.bfloat16 else SPEC_F32
+    _lib.check(lib, lib.spec_e2etv_head_fwd_bwd(ctypes.byref(tree.layout), vocab, d_model, dt, None,
+                                                None, None, 0.0, None, None, None, None,
+                                                ctypes.byref(nbytes), None))
+    return nbytes.value
+
+
+def spec_e2etv_head_fwd_bwd(tree: PackedTree, draft: torch.Tensor, hidden: torch.Tensor,
+                            head: torch.Tensor, inv_norm: float = 0.0, grad: bool = True,
+                            alpha_out=None, loss_out=None, grad_out=None, work: torch.Tensor = None):
+    """E2E-TV with teacher logits hidden[step_pred_row] @ head^T formed on the device and never
+    stored. draft [R, V] (bf16 or fp32), hidden [N, d] bf16, head [V, d] bf16.
+    Returns (alpha [R] fp32, loss [1] fp32, grad [R, V] fp32 or None)."""
+    R, V = draft.shape
+    if R != tree.n_steps or head.dim() != 2 or head.shape[0] != V:
+        raise ValueError("draft must be [n_steps, vocab] and head [vocab, d_model]")
+    d = head.shape[1]
+    if hidden.shape != (tree.n_rows, d):
+        raise ValueError("hidden must be [n_rows, d_model]")
+    if hidden.dtype != torch.bfloat16 or head.dtype != torch.bfloat16:
+        raise ValueError("hidden and head must be bfloat16")
+    if not (draft.is_contiguous() and hidden.is_contiguous() and head.is_contiguous()):
+        raise ValueError("draft, hidden and head must be contiguous")
+    dt = _dtype_code(draft)
+    dev = draft.device
+    if alpha_out is None:
+        alpha_out = torch.empty(R, dtype=torch.float32, device=dev)
+    if loss_out is None:
+        loss_out = torch.empty(1, dtype=torch.float32, device=dev)
+    if grad and grad_out is None:
+        grad_out = torch.empty((R, V), dtype=torch.float32, device=dev)
+    if not grad:
+        grad_out = None
+    if work is None:
+        work = torch.empty(max(e2etv_head_work_bytes(tree, V, d, draft.dtype), 256),
+                           dtype=torch.uint8, device=dev)
+    lib = library()
+    nbytes = ctypes.c_size_t(work.numel())
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    _lib.check(lib, lib.spec_e2etv_head_fwd_bwd(ctypes.byref(tree.layout), V, d, dt, ptr(draft),
+                                                ptr(hidden), ptr(head), float(inv_norm),
+                                                ptr(alpha_out), ptr(loss_out), ptr(grad_out),
+                                                ptr(work), ctypes.byref(nbytes),
+                                                ctypes.c_void_p(_stream(dev))))
     return alpha_out, loss_out, grad_out
 
 

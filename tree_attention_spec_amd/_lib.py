@@ -85,7 +85,8 @@ LAYOUT_ARRAYS = {
     "attn_items": lambda L: L.n_attn_items * 8,
 }
 
-EXPORTS = ["spec_tree_pack", "spec_tree_attn_fwd", "spec_e2etv_fwd_bwd", "spec_gdn_trunk_fwd",
+EXPORTS = ["spec_tree_pack", "spec_tree_attn_fwd", "spec_e2etv_fwd_bwd", "spec_e2etv_head_fwd_bwd",
+           "spec_gdn_trunk_fwd",
            "spec_gdn_replay_fwd", "spec_status_string", "spec_last_error", "spec_abi_version",
            "spec_profile_attach"]
 
@@ -109,6 +110,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_e2etv_fwd_bwd.argtypes = [c.POINTER(spec_tree_layout), c.c_int64, c.c_int, c.c_void_p,
                                        c.c_void_p, c.c_float, c.c_void_p, c.c_void_p, c.c_void_p,
                                        c.c_void_p, c.POINTER(c.c_size_t), c.c_void_p]
+    lib.spec_e2etv_head_fwd_bwd.restype = c.c_int
+    lib.spec_e2etv_head_fwd_bwd.argtypes = [c.POINTER(spec_tree_layout), c.c_int64, c.c_int32,
+                                            c.c_int, c.c_void_p, c.c_void_p, c.c_void_p, c.c_float,
+                                            c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
+                                            c.POINTER(c.c_size_t), c.c_void_p]
     lib.spec_gdn_trunk_fwd.restype = c.c_int
     lib.spec_gdn_trunk_fwd.argtypes = [c.POINTER(spec_tree_layout), c.c_int32, c.c_int32, c.c_int32,
                                        c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,

@@ -242,3 +242,51 @@ extern "C" spec_status spec_e2etv_fwd_bwd(const spec_tree_layout *layout, int64_
                             e2etv_carve(d_work, layout->n_steps, vocab), s));
   return SPEC_OK;
 }
+
+extern "C" spec_status spec_e2etv_head_fwd_bwd(const spec_tree_layout *layout, int64_t vocab,
+                                               int32_t d_model, spec_dtype dtype,
+                                               const void *d_draft, const void *d_hidden,
+                                               const void *d_head, float inv_norm, float *d_alpha,
+                                               float *d_loss, float *d_grad, void *d_work,
+                                               size_t *work_bytes, spec_stream stream) {
+  clear_error();
+  if (!work_bytes) return fail(SPEC_ERR_INVALID_ARG, "work_bytes must be non-NULL");
+  if (!layout) return fail(SPEC_ERR_INVALID_ARG, "layout must be non-NULL");
+  if (layout->n_steps < 1 || layout->n_branches < 1)
+    return fail(SPEC_ERR_INVALID_ARG, "the layout has no supervised steps");
+  if (d_work && (!layout->step_off || !layout->step_pred_row))
+    return fail(SPEC_ERR_INVALID_ARG, "layout device arrays are missing (pack with a buffer first)");
+  if (vocab < 1 || vocab > (int64_t)INT32_MAX)
+    return fail(SPEC_ERR_INVALID_ARG, "vocab %lld out of range", (long long)vocab);
+  if (d_model < 1) return fail(SPEC_ERR_INVALID_ARG, "d_model %d out of range", (int)d_model);
+  if (vocab % 8 != 0 || d_model % 64 != 0)
+    return fail(SPEC_ERR_UNSUPPORTED, "vocab (%lld) must be a multiple of 8 and d_model (%d) of 64",
+                (long long)vocab, (int)d_model);
+  if (layout->max_branch_len > 64)
+    return fail(SPEC_ERR_UNSUPPORTED, "branches of %d steps (at most 64)", (int)layout->max_branch_len);
+  if (dtype != SPEC_BF16 && dtype != SPEC_F32)
+    return fail(SPEC_ERR_UNSUPPORTED, "draft dtype %d not supported", (int)dtype);
+  if (!std::isfinite(inv_norm)) return fail(SPEC_ERR_INVALID_ARG, "inv_norm must be finite");
+  const size_t need = e2etv_head_work_bytes(layout->n_steps, vocab);
+  if (!d_work) {
+    *work_bytes = need;
+    return SPEC_OK;
+  }
+  if (*work_bytes < need) {
+    size_t have = *work_bytes;
+    *work_bytes = need;
+    return fail(SPEC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", have, need);
+  }
+  if (!d_draft || !d_hidden || !d_head || !d_alpha || !d_loss)
+    return fail(SPEC_ERR_INVALID_ARG,
+                "d_draft, d_hidden, d_head, d_alpha and d_loss must be non-NULL");
+  if (!aligned16(d_draft) || !aligned16(d_hidden) || !aligned16(d_head) || !aligned16(d_work) ||
+      (d_grad && !aligned16(d_grad)))
+    return fail(SPEC_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  const float w = inv_norm > 0.f ? inv_norm : (float)(1.0 / (double)layout->n_steps);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  prof_mark(s, "e2etv_head:begin");
+  SPEC_HIP_TRY(launch_e2etv_head(*layout, vocab, d_model, dtype, d_draft, d_hidden, d_head, w,
+                                 d_alpha, d_loss, d_grad, d_work, s));
+  return SPEC_OK;
+}

@@ -88,5 +88,19 @@ E2etvWork e2etv_carve(void *d_work, int64_t n_steps, int64_t vocab);
 hipError_t launch_e2etv(const spec_tree_layout &L, int64_t vocab, spec_dtype dtype,
                         const void *draft, const void *teacher, float inv_norm, float *alpha,
                         float *loss, float *grad, const E2etvWork &w, hipStream_t stream);
+// The scan (prefix products, dL/d alpha, L) and gradient stages alone, for a
+// path with its own statistics kernels: w.part holds [R][team] (alpha, S)
+// partials summed in member order, w.lse_q2 the draft log-sum-exps, w.bits the
+// {q < p} bitmask, and w.status[1] (the scan's ticket) is zero. vocab % 8 == 0.
+hipError_t launch_e2etv_tail(const spec_tree_layout &L, int64_t vocab, spec_dtype dtype,
+                             const void *draft, float inv_norm, int team, float *alpha,
+                             float *loss, float *grad, const E2etvWork &w, hipStream_t stream);
+
+// E2E-TV with the teacher logits formed from hidden states and an output head.
+size_t e2etv_head_work_bytes(int64_t n_steps, int64_t vocab);
+hipError_t launch_e2etv_head(const spec_tree_layout &L, int64_t vocab, int32_t d_model,
+                             spec_dtype draft_dtype, const void *draft, const void *hidden,
+                             const void *head, float inv_norm, float *alpha, float *loss,
+                             float *grad, void *work, hipStream_t stream);
 
 }  // namespace spec

@@ -1314,4 +1314,35 @@ hipError_t launch_e2etv(const spec_tree_layout &L, int64_t V, spec_dtype dtype, 
              : launch_typed<float, false>(L, V, draft, teacher, w, alpha, loss, grad, ws, s);
 }
 
+hipError_t launch_e2etv_tail(const spec_tree_layout &L, int64_t V, spec_dtype dtype, const void *draft,
+                             float w, int team, float *alpha, float *loss, float *grad,
+                             const E2etvWork &ws, hipStream_t s) {
+  hipLaunchKernelGGL(e2etv_scan_kernel, dim3((unsigned)((L.n_branches + kScanWaves - 1) / kScanWaves)),
+                     dim3(kScanWaves * 64), 0, s, L.step_off, L.n_branches, ws.part, team,
+                     (const unsigned *)nullptr, w, alpha, ws.S, ws.coef, ws.branch_sum,
+                     ws.status + 1, loss);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !grad) return e;
+  prof_mark(s, "e2etv_scan");
+  const int64_t R = L.n_steps;
+  const int64_t per_block = (int64_t)kGradThreads * 8 * kGradVecs;
+  const int64_t chunks = (V + per_block - 1) / per_block;
+  if (chunks * R > INT32_MAX || V % 8 != 0) return hipErrorInvalidValue;
+  // the vector gradient path reads the draft row and the bitmask only
+  if (dtype == SPEC_BF16) {
+    const __bf16 *z = static_cast<const __bf16 *>(draft);
+    hipLaunchKernelGGL((e2etv_grad_kernel<__bf16, true>), dim3((unsigned)(chunks * R)),
+                       dim3(kGradThreads), 0, s, z, z, V, ws.lse_q2, ws.lse_p2, ws.S, ws.coef, grad,
+                       ws.bits, ws.bits_row, (int32_t)chunks);
+  } else {
+    const float *z = static_cast<const float *>(draft);
+    hipLaunchKernelGGL((e2etv_grad_kernel<float, true>), dim3((unsigned)(chunks * R)),
+                       dim3(kGradThreads), 0, s, z, z, V, ws.lse_q2, ws.lse_p2, ws.S, ws.coef, grad,
+                       ws.bits, ws.bits_row, (int32_t)chunks);
+  }
+  e = hipGetLastError();
+  prof_mark(s, "e2etv_grad");
+  return e;
+}
+
 }  // namespace spec
