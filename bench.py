@@ -8,9 +8,13 @@ already resident in device memory when the timed region starts. The headline
 is supervised rows per second; per-kernel durations come from HIP events
 recorded by the library on the stream it launches on, inside the timed steps.
 
-    python bench.py [--steps K] [--warmup W] [--config gqa8b] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--config stress] [--no-cpu-baseline]
     python bench.py --gdn [--config gqa8b]   # GDN scoring: trunk pass + indexed replay
     python bench.py --head [--config gqa8b]  # E2E-TV through the output head
+
+The default workload is the stress tree (trunk 32768, 2048 branches of 1..16
+steps, 64 query / 8 KV heads, vocabulary 151936): the largest of the five
+workloads, all of which fit one GPU.
 
 Prints one JSON line. Only one GPU is supported (--gpus must be 1).
 """
@@ -214,7 +218,7 @@ def ablation(cfg, s, tree, qt, kt, vt, out, steps, warmup):
     }
 
 
-def cpu_baseline(cfg, s, q, k, v, z_rows_fn, N, R, n_attn=24, n_e2e=6):
+def cpu_baseline(cfg, s, q, k, v, z_rows_fn, N, R, n_attn=None, n_e2e=6):
     """Time the oracle on a bounded random sample and scale it to the full step.
 
     The sample is spread over one thread per host CPU (at most 16): NumPy releases
@@ -232,6 +236,10 @@ def cpu_baseline(cfg, s, q, k, v, z_rows_fn, N, R, n_attn=24, n_e2e=6):
         return bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
 
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    if n_attn is None:
+        # a row's oracle cost grows with the keys it sees: fewer rows on long trunks keep
+        # the sample near 10-30 s of host time
+        n_attn = max(4, min(24, int(24 * 4096 / max(int(max(s["trunk_len"])), 1))))
     rng = np.random.default_rng(123)
     t0 = time.perf_counter()
     lay = pack_ref(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"])
@@ -552,7 +560,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="gqa8b")
+    ap.add_argument("--config", default=None,
+                    help="workload (default: stress for the scoring step, gqa8b for --gdn and --head)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ablation", action="store_true",
                     help="also time every branch scored as its own causal sequence (uncached independent "
@@ -571,6 +580,8 @@ def main():
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB"),
                     help="write profiles/traffic.json from four rocprofv3 --pmc databases and exit")
     args = ap.parse_args()
+    if args.config is None:
+        args.config = "gqa8b" if (args.gdn or args.head) else "stress"
     if args.summarize_pmc:
         print(json.dumps(summarize_pmc(args.summarize_pmc), indent=1))
         return

@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 from _util import ATTN_ATOL, ATTN_ATOL_F32, Case, from_device, sample_rows, say, to_device, widen
-from oracle import readout_ref, tree_attn_ref
+from oracle import brute_force_branch_ref, readout_ref, tree_attn_ref
 from specgen import CONFIGS, small_config
 
 pytestmark = pytest.mark.gpu
@@ -187,13 +187,14 @@ def test_attn_workload_sampled(name):
     assert torch.isfinite(out.float()).all()
 
 
-def test_attn_independent_layout_matches_shared():
-    """Every branch packed as its own tree (trunk through its anchor, then the branch) —
-    the uncached independent scoring the paper page's Figure 13 compares against — gives
-    the shared-prefix layout's branch and anchor rows (same tokens, same positions)."""
+def test_attn_independent_layout_matches_oracle():
+    """Every branch packed as its own tree (trunk through its anchor, then the branch): the
+    uncached independent scoring the paper page's Figure 13 compares against. Every row of
+    that layout equals the oracle's per-branch causal brute force, and its branch and anchor
+    rows equal the shared-prefix layout's (same tokens, same positions)."""
     import torch
     import tree_attention_spec_amd as tas
-    say("attn: independent per-branch layout vs shared prefix")
+    say("attn: independent per-branch layout vs the oracle's brute force and the shared prefix")
     case = Case(small_config("batched", n_trees=2, trunk=200, branches=9, width=8, hq=8, hkv=2,
                              head_dim=128))
     q, k, v = case.qkv()
@@ -211,10 +212,20 @@ def test_attn_independent_layout_matches_shared():
     out_i, _ = tas.spec_tree_attn_fwd(tree_i, to_device(q[idx]), to_device(k[idx]), to_device(v[idx]),
                                       rope_base=case.cfg.rope_base)
     torch.cuda.synchronize()
+    oi = from_device(out_i)
     toff_i = from_device(tree_i.arrays()["tree_off"]).astype(np.int64)
+    qd, kd, vd = widen(q), widen(k), widen(v)
+    worst = 0.0
+    for b in range(len(a)):
+        rows_ref, o_ref = brute_force_branch_ref(lay, qd, kd, vd, b, case.cfg.rope_base)
+        assert len(rows_ref) == a[b] + w[b]
+        got = oi[toff_i[b]:toff_i[b] + a[b] + w[b]]
+        worst = max(worst, float(np.abs(got - o_ref).max()))
     rows_s = np.concatenate([np.concatenate([[trunk0[b] + a[b]], lay["branch_off"][b] + np.arange(w[b] - 1)])
                              for b in range(len(a))])
     rows_i = np.concatenate([toff_i[b] + a[b] + np.arange(w[b]) for b in range(len(a))])
-    diff = np.abs(from_device(out)[rows_s] - from_device(out_i)[rows_i]).max()
-    say("  max abs diff %.3e over %d rows" % (diff, len(rows_s)))
+    diff = np.abs(from_device(out)[rows_s] - oi[rows_i]).max()
+    say("  independent layout vs brute force: max abs err %.3e over %d rows; vs shared layout %.3e"
+        % (worst, tree_i.n_rows, diff))
+    assert worst <= ATTN_ATOL
     assert diff <= ATTN_ATOL

@@ -145,38 +145,80 @@ def test_e2etv_forward_only_and_determinism():
     assert torch.equal(a1, a3) and torch.equal(l1, l3)
 
 
+def _oracle_stats_all(z, y, chunk=32):
+    """Oracle alpha and S of every row, row chunks spread over the host's threads
+    (NumPy releases the interpreter lock inside its array operations)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    R = z.shape[0]
+    alpha, S = np.empty(R), np.empty(R)
+
+    def run(r0):
+        a, s_, _, _, _, _ = e2etv_row_stats_ref(widen(z[r0:r0 + chunk]), widen(y[r0:r0 + chunk]))
+        alpha[r0:r0 + chunk], S[r0:r0 + chunk] = a, s_
+
+    with ThreadPoolExecutor(max(1, min(16, len(os.sched_getaffinity(0))))) as ex:
+        list(ex.map(run, range(0, R, chunk)))
+    return alpha, S
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("name", ["gqa8b", "long", "batched", "stress"])
-def test_e2etv_workload_sampled(name):
-    """Full-size workloads; sampled rows for alpha and the gradient, L from all alphas."""
+def test_e2etv_workload_full(name):
+    """Full-size workloads in the benchmarked launch: every step's alpha against the oracle,
+    the oracle's own L (from its alphas) against the GPU's, and sampled gradient rows with
+    the oracle's coefficients."""
     import torch
-    say("e2etv parity: %s full size, sampled rows" % name)
+    say("e2etv parity: %s full size, every alpha" % name)
     case = Case(CONFIGS[name])
     tree = _pack(case.s)
     z, y = case.logits()
     zt, yt = to_device(z), to_device(y)
-    case.drop_logits()
-    del z, y
     a, l, g = _run(tree, zt, yt)
     del zt, yt
     R = case.R
-    rng = np.random.default_rng(1)
-    rows = np.unique(np.concatenate([[0, R - 1], rng.choice(R, size=10, replace=False)]))
-    zs, ys = gen_logit_rows(case.cfg, R, rows)
-    alpha, S, _, _, q, p = e2etv_row_stats_ref(zs.astype(np.float64), ys.astype(np.float64))
     ga = from_device(a)
-    arel = np.max(np.abs(ga[rows] - alpha) / alpha)
-    # L and c from the GPU's alphas (checked on the sampled rows above)
-    L = e2etv_loss_ref(ga, case.lay["step_off"])
-    c = e2etv_coef_ref(ga, case.lay["step_off"])[rows]
-    gref = e2etv_grad_ref(q, p, S, c)
+    alpha, _ = _oracle_stats_all(z, y)
+    case.drop_logits()
+    del z, y
+    arel = np.max(np.abs(ga - alpha) / alpha)
+    L = e2etv_loss_ref(alpha, case.lay["step_off"])
+    c_all = e2etv_coef_ref(alpha, case.lay["step_off"])
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, R - 1], rng.choice(R, size=30, replace=False)]))
+    zs, ys = gen_logit_rows(case.cfg, R, rows)
+    _, S, _, _, q, p = e2etv_row_stats_ref(zs.astype(np.float64), ys.astype(np.float64))
+    gref = e2etv_grad_ref(q, p, S, c_all[rows])
     gg = from_device(g[torch.from_numpy(rows).cuda()])
     gw, nt = check_grad_rows(gg, gref, q, p)
-    say("  alpha rel %.2e, L %.7f vs %.7f, grad rel %.2e (%d near-ties)" % (arel, l.item(), L, gw, nt))
+    say("  %d alphas: max rel %.2e; L %.7f vs oracle %.7f; %d grad rows rel %.2e (%d near-ties)"
+        % (R, arel, l.item(), L, len(rows), gw, nt))
     assert arel <= ALPHA_RTOL
     assert abs(l.item() - L) <= max(LOSS_RTOL * abs(L), LOSS_ATOL)
     assert gw <= 1e-4
     assert torch.isfinite(g).all()
+
+
+@pytest.mark.parametrize("recipe", ["stress", "gqa8b"])
+def test_e2etv_fused_pipeline_depth(recipe):
+    """Enough steps (R >= 256 over the fused kernel's 25 teams at vocabulary 151936) that
+    every team runs its pipeline at full depth for many rows, with branches that cross from
+    the last team to the first: every alpha, the oracle's own L and every gradient row
+    against the oracle."""
+    import tree_attention_spec_amd as tas
+    say("e2etv parity: fused pipeline depth, %s recipe" % recipe)
+    if recipe == "stress":
+        cfg = small_config("stress", trunk=3000, branches=72, width=16, vocab=151936)
+    else:
+        cfg = small_config("gqa8b", trunk=2000, branches=40, width=16, vocab=151936)
+    case = Case(cfg)
+    assert case.R >= 256, case.R
+    z, y = case.logits()
+    tm = tas.KernelTimer(capacity=16)
+    with tm:
+        _full_compare(case, z, y)
+    names = [n for n, _ in tm.durations()]
+    assert "e2etv_fused" in names, names
 
 
 def test_e2etv_long_branches_multipass():

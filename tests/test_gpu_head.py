@@ -111,13 +111,23 @@ def test_head_matches_supplied_logit_path():
     assert np.max(np.abs(from_device(a) - from_device(a2)) / from_device(a2)) <= 2 * ALPHA_RTOL
 
 
+def test_head_many_step_tiles():
+    """R >= 256 steps (three 128-step tiles) at vocabulary 151936: every alpha, the oracle's
+    own L and every gradient row against the oracle."""
+    say("e2etv head parity: R >= 256 steps, vocabulary 151936")
+    case = Case(small_config("gqa8b", trunk=2000, branches=20, width=16, vocab=151936))
+    assert case.R >= 256
+    _compare(case, 128, 151936)
+
+
 @pytest.mark.slow
-def test_head_gqa8b_sampled():
-    """Full size (4096 steps, vocabulary 151936, hidden 4096): sampled rows against the oracle,
-    L from all of the GPU's alphas."""
+def test_head_gqa8b_full():
+    """Full size (4096 steps, vocabulary 151936, hidden 4096): every step's alpha against the
+    oracle (head product in float64, row blocks), the oracle's own L, and sampled gradient
+    rows with the oracle's coefficients."""
     import torch
     import tree_attention_spec_amd as tas
-    say("e2etv head parity: gqa8b full size, sampled rows")
+    say("e2etv head parity: gqa8b full size, every alpha")
     cfg = CONFIGS["gqa8b"]
     case = Case(cfg)
     d, V = cfg.hq * cfg.head_dim, cfg.vocab
@@ -127,22 +137,26 @@ def test_head_gqa8b_sampled():
                                           to_device(inp["head"]))
     torch.cuda.synchronize()
     R = case.R
-    rng = np.random.default_rng(1)
-    rows = np.unique(np.concatenate([[0, R - 1, 127, 128], rng.choice(R, size=8, replace=False)]))
     hidden = widen(inp["hidden"])
-    y = np.zeros((len(rows), V))
-    for v0 in range(0, V, 16384):
-        y[:, v0:v0 + 16384] = head_logits_ref(case.lay, hidden, widen(inp["head"][v0:v0 + 16384]),
-                                              steps=rows)
-    z = widen(gen_head_draft_rows(0, R, V, rows))
-    alpha, S, _, _, q, p = e2etv_row_stats_ref(z, y)
+    head = widen(inp["head"])
+    alpha = np.empty(R)
+    for r0 in range(0, R, 256):
+        steps = np.arange(r0, min(R, r0 + 256))
+        y = head_logits_ref(case.lay, hidden, head, steps=steps)
+        alpha[steps] = e2etv_row_stats_ref(widen(inp["draft"][steps]), y)[0]
     ga = from_device(a)
-    arel = np.max(np.abs(ga[rows] - alpha) / alpha)
-    L = e2etv_loss_ref(ga, case.lay["step_off"])
-    c = e2etv_coef_ref(ga, case.lay["step_off"])[rows]
+    arel = np.max(np.abs(ga - alpha) / alpha)
+    L = e2etv_loss_ref(alpha, case.lay["step_off"])
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, R - 1, 127, 128], rng.choice(R, size=12, replace=False)]))
+    y = head_logits_ref(case.lay, hidden, head, steps=rows)
+    z = widen(gen_head_draft_rows(0, R, V, rows))
+    _, S, _, _, q, p = e2etv_row_stats_ref(z, y)
+    c = e2etv_coef_ref(alpha, case.lay["step_off"])[rows]
     gref = e2etv_grad_ref(q, p, S, c)
     gw, nt = check_grad_rows(from_device(g[torch.from_numpy(rows).cuda()]), gref, q, p)
-    say("  alpha rel %.2e, L %.7f vs %.7f, grad rel %.2e (%d near-ties)" % (arel, l.item(), L, gw, nt))
+    say("  %d alphas: max rel %.2e; L %.7f vs oracle %.7f; %d grad rows rel %.2e (%d near-ties)"
+        % (R, arel, l.item(), L, len(rows), gw, nt))
     assert arel <= ALPHA_RTOL
     assert abs(l.item() - L) <= max(LOSS_RTOL * abs(L), LOSS_ATOL)
     assert gw <= 1e-4
