@@ -6,9 +6,14 @@
  *   spec_tree_attn_fwd  tree-masked GQA attention, RoPE at semantic positions,
  *                       optional predecessor-row readout
  *   spec_e2etv_fwd_bwd  E2E-TV overlap, prefix-product loss and its gradient
- *   spec_e2etv_head_fwd_bwd  the same with the teacher logits formed through an
- *                       output head from hidden states (never stored)
  *                       with respect to the draft logits
+ * Beside them:
+ *   spec_e2etv_fwd_bwd_noalloc  the same E2E-TV call with a library-owned
+ *                       workspace, for callers that cannot allocate
+ *   spec_e2etv_head_fwd_bwd  E2E-TV with the teacher logits formed through an
+ *                       output head from hidden states (never stored)
+ *   spec_gdn_trunk_fwd, spec_gdn_replay_fwd  GDN scoring for linear-attention
+ *                       targets: shared trunk pass, indexed state replay
  *
  * Sources, cited by page title and section:
  *   [SpecOPD paper page]  "SpecOPD: Branch-Parallel On-Policy Distillation for
@@ -20,7 +25,9 @@
  * Conventions shared by every call
  *   - All pointers named d_* are device pointers; h_* are host pointers.
  *   - The caller allocates and owns every buffer. The library never allocates
- *     or frees device memory; scratch memory comes from a caller workspace.
+ *     or frees device memory; scratch memory comes from a caller workspace
+ *     (spec_e2etv_fwd_bwd_noalloc alone uses a fixed device array the loaded
+ *     library holds per GPU instead).
  *     Passing d_mem / d_work == NULL is a size query: the call validates what
  *     it can, writes the byte count and returns SPEC_OK without touching the
  *     GPU (no HIP call at all).
@@ -33,7 +40,8 @@
  *     is launched and spec_last_error() describes the problem (thread-local).
  *   - Tensors are dense and row-major. Device buffers must be 16-byte aligned.
  *   - The library holds no state between calls; calls on different streams
- *     may run concurrently as long as their buffers are disjoint.
+ *     may run concurrently as long as their buffers are disjoint (calls of
+ *     spec_e2etv_fwd_bwd_noalloc on one GPU share its array and must not).
  */
 #ifndef SPEC_TREE_H
 #define SPEC_TREE_H
@@ -45,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SPEC_TREE_ABI_VERSION 5
+#define SPEC_TREE_ABI_VERSION 6
 #define SPEC_MAX_BRANCH_LEN 64 /* largest supported branch width W_b */
 
 typedef enum spec_status {
@@ -232,6 +240,36 @@ spec_status spec_e2etv_fwd_bwd(const spec_tree_layout *layout, int64_t vocab,
                                const void *d_teacher, float inv_norm, float *d_alpha,
                                float *d_loss, float *d_grad, void *d_work, size_t *work_bytes,
                                spec_stream stream);
+
+/*
+ * spec_e2etv_fwd_bwd_noalloc -- spec_e2etv_fwd_bwd without a caller workspace.
+ *
+ * For callers that cannot allocate device memory or hand over a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. Same arguments, results and kernels as spec_e2etv_fwd_bwd (minus
+ * d_work / work_bytes); the workspace is a library-owned device array of
+ * SPEC_NOALLOC_SCRATCH_BYTES per GPU, held from the library's first use on
+ * that GPU until the process ends. The call itself allocates nothing and
+ * calls no allocating routine. The kernels clear what must start at zero, so
+ * the array may hold anything from an earlier call.
+ *
+ * Limit: the E2E-TV workspace of (R steps, vocabulary V) must fit the array:
+ * 4*4R + 16*8R*2 + 8R bytes plus 256 (about 280 B per step: R up to ~119k) on
+ * the fused path (bf16 logits, V a multiple of 8, branches of at most 64
+ * steps), plus R * ceil(V/8) bitmask bytes on every other path. Larger
+ * requests return SPEC_ERR_UNSUPPORTED with nothing launched.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (other streams, other threads) race and must be serialised by the
+ * caller.
+ * Errors: as spec_e2etv_fwd_bwd, plus SPEC_ERR_UNSUPPORTED for the limit
+ * above and SPEC_ERR_HIP if the array's device address cannot be looked up.
+ */
+#define SPEC_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+spec_status spec_e2etv_fwd_bwd_noalloc(const spec_tree_layout *layout, int64_t vocab,
+                                       spec_dtype logit_dtype, const void *d_draft,
+                                       const void *d_teacher, float inv_norm, float *d_alpha,
+                                       float *d_loss, float *d_grad, spec_stream stream);
 
 /*
  * spec_e2etv_head_fwd_bwd -- E2E-TV with the teacher logits read through an

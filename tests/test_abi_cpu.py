@@ -153,6 +153,29 @@ def test_e2etv_size_query_and_checks(tas):
                                   ctypes.c_void_p(0x1000), ctypes.byref(big), None) == 1
 
 
+def test_e2etv_noalloc_checks(tas):
+    """spec_e2etv_fwd_bwd_noalloc: argument checks and the scratch limit, refused before
+    any HIP call."""
+    lib = tas.library()
+    L = _query_layout(tas)
+    fake = ctypes.c_void_p(0x1000)
+    call = lambda V, dt, out=fake: lib.spec_e2etv_fwd_bwd_noalloc(
+        ctypes.byref(L), V, dt, fake, fake, 0.0, out, out, None, None)
+    assert call(151936, 1) == 1                   # the layout has no device arrays
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    L.step_off = ctypes.cast(fake, i32p)          # never read on the host
+    L.step_branch = ctypes.cast(fake, i32p)
+    assert call(151936, 3) == 2                   # unsupported dtype
+    assert call(0, 1) == 1                        # empty vocabulary
+    assert call(151936, 1, out=None) == 1         # alpha and loss outputs are required
+    # float32 logits keep the {q < p} bitmask, R * V / 8 bytes: past the array for this R
+    m = re.search(r"#define SPEC_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    cap = int(m.group(1)) << int(m.group(2))
+    V = 8 * (cap // L.n_steps + 8)
+    assert call(V, 0) == 2
+    assert "scratch" in lib.spec_last_error().decode()
+
+
 def test_e2etv_head_size_query_and_checks(tas):
     """spec_e2etv_head_fwd_bwd: size query and argument checks, no GPU touched."""
     lib = tas.library()

@@ -212,6 +212,27 @@ def spec_e2etv_fwd_bwd(tree: PackedTree, draft: torch.Tensor, teacher: torch.Ten
     return alpha_out, loss_out, grad_out
 
 
+def spec_e2etv_fwd_bwd_noalloc(tree: PackedTree, draft: torch.Tensor, teacher: torch.Tensor,
+                               inv_norm: float = 0.0, alpha_out=None, loss_out=None, grad_out=None):
+    """spec_e2etv_fwd_bwd with the library's own per-GPU workspace: the call allocates
+    nothing itself, so every output tensor must be passed in (grad_out may be None for a
+    forward-only call). Returns (alpha_out, loss_out, grad_out)."""
+    R, V = draft.shape
+    if teacher.shape != (R, V) or R != tree.n_steps:
+        raise ValueError("draft/teacher must be [n_steps, vocab]")
+    if not (draft.is_contiguous() and teacher.is_contiguous()) or draft.dtype != teacher.dtype:
+        raise ValueError("draft and teacher must be contiguous and share a dtype")
+    if alpha_out is None or loss_out is None:
+        raise ValueError("the no-allocation call needs alpha_out and loss_out")
+    lib = library()
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    _lib.check(lib, lib.spec_e2etv_fwd_bwd_noalloc(ctypes.byref(tree.layout), V, _dtype_code(draft),
+                                                   ptr(draft), ptr(teacher), float(inv_norm),
+                                                   ptr(alpha_out), ptr(loss_out), ptr(grad_out),
+                                                   ctypes.c_void_p(_stream(draft.device))))
+    return alpha_out, loss_out, grad_out
+
+
 def e2etv_head_work_bytes(tree, vocab, d_model, draft_dtype=torch.bfloat16) -> int:
     lib = library()
     nbytes = ctypes.c_size_t(0)

@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "common.h"
 
@@ -100,6 +101,8 @@ E2etvOffsets e2etv_offsets(int64_t R, int64_t V) {
 }  // namespace
 
 size_t e2etv_work_bytes(int64_t R, int64_t V) { return e2etv_offsets(R, V).total; }
+
+size_t e2etv_work_bytes_fused(int64_t R) { return e2etv_offsets(R, 8).bits; }
 
 E2etvWork e2etv_carve(void *d_work, int64_t R, int64_t V) {
   char *p = static_cast<char *>(d_work);
@@ -203,6 +206,34 @@ extern "C" spec_status spec_tree_attn_fwd(const spec_tree_layout *layout, int32_
   return SPEC_OK;
 }
 
+namespace {
+// Checks of spec_e2etv_fwd_bwd that need no buffer: the layout, vocabulary, dtype
+// and normaliser.
+spec_status check_e2etv_shape(const spec_tree_layout *layout, int64_t vocab, spec_dtype dtype,
+                              float inv_norm, bool need_device) {
+  if (!layout) return fail(SPEC_ERR_INVALID_ARG, "layout must be non-NULL");
+  if (layout->n_steps < 1 || layout->n_branches < 1)
+    return fail(SPEC_ERR_INVALID_ARG, "the layout has no supervised steps");
+  if (need_device && (!layout->step_off || !layout->step_branch))
+    return fail(SPEC_ERR_INVALID_ARG, "layout device arrays are missing (pack with a buffer first)");
+  if (vocab < 1 || vocab > (int64_t)INT32_MAX)
+    return fail(SPEC_ERR_INVALID_ARG, "vocab %lld out of range", (long long)vocab);
+  if (dtype != SPEC_BF16 && dtype != SPEC_F32)
+    return fail(SPEC_ERR_UNSUPPORTED, "logit dtype %d not supported", (int)dtype);
+  if (!std::isfinite(inv_norm)) return fail(SPEC_ERR_INVALID_ARG, "inv_norm must be finite");
+  return SPEC_OK;
+}
+
+spec_status check_e2etv_buffers(const void *d_draft, const void *d_teacher, const float *d_alpha,
+                                const float *d_loss, const float *d_grad) {
+  if (!d_draft || !d_teacher || !d_alpha || !d_loss)
+    return fail(SPEC_ERR_INVALID_ARG, "d_draft, d_teacher, d_alpha and d_loss must be non-NULL");
+  if (!aligned16(d_draft) || !aligned16(d_teacher) || (d_grad && !aligned16(d_grad)))
+    return fail(SPEC_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  return SPEC_OK;
+}
+}  // namespace
+
 extern "C" spec_status spec_e2etv_fwd_bwd(const spec_tree_layout *layout, int64_t vocab,
                                           spec_dtype dtype, const void *d_draft,
                                           const void *d_teacher, float inv_norm, float *d_alpha,
@@ -210,16 +241,8 @@ extern "C" spec_status spec_e2etv_fwd_bwd(const spec_tree_layout *layout, int64_
                                           size_t *work_bytes, spec_stream stream) {
   clear_error();
   if (!work_bytes) return fail(SPEC_ERR_INVALID_ARG, "work_bytes must be non-NULL");
-  if (!layout) return fail(SPEC_ERR_INVALID_ARG, "layout must be non-NULL");
-  if (layout->n_steps < 1 || layout->n_branches < 1)
-    return fail(SPEC_ERR_INVALID_ARG, "the layout has no supervised steps");
-  if (d_work && !layout->step_off)
-    return fail(SPEC_ERR_INVALID_ARG, "layout device arrays are missing (pack with a buffer first)");
-  if (vocab < 1 || vocab > (int64_t)INT32_MAX)
-    return fail(SPEC_ERR_INVALID_ARG, "vocab %lld out of range", (long long)vocab);
-  if (dtype != SPEC_BF16 && dtype != SPEC_F32)
-    return fail(SPEC_ERR_UNSUPPORTED, "logit dtype %d not supported", (int)dtype);
-  if (!std::isfinite(inv_norm)) return fail(SPEC_ERR_INVALID_ARG, "inv_norm must be finite");
+  spec_status st = check_e2etv_shape(layout, vocab, dtype, inv_norm, d_work != nullptr);
+  if (st != SPEC_OK) return st;
   const size_t need = e2etv_work_bytes(layout->n_steps, vocab);
   if (!d_work) {
     *work_bytes = need;
@@ -230,16 +253,81 @@ extern "C" spec_status spec_e2etv_fwd_bwd(const spec_tree_layout *layout, int64_
     *work_bytes = need;
     return fail(SPEC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", have, need);
   }
-  if (!d_draft || !d_teacher || !d_alpha || !d_loss)
-    return fail(SPEC_ERR_INVALID_ARG, "d_draft, d_teacher, d_alpha and d_loss must be non-NULL");
-  if (!aligned16(d_draft) || !aligned16(d_teacher) || !aligned16(d_work) ||
-      (d_grad && !aligned16(d_grad)))
-    return fail(SPEC_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  st = check_e2etv_buffers(d_draft, d_teacher, d_alpha, d_loss, d_grad);
+  if (st != SPEC_OK) return st;
+  if (!aligned16(d_work)) return fail(SPEC_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
   const float w = inv_norm > 0.f ? inv_norm : (float)(1.0 / (double)layout->n_steps);
   hipStream_t s = static_cast<hipStream_t>(stream);
   prof_mark(s, "e2etv:begin");
   SPEC_HIP_TRY(launch_e2etv(*layout, vocab, dtype, d_draft, d_teacher, w, d_alpha, d_loss, d_grad,
                             e2etv_carve(d_work, layout->n_steps, vocab), s));
+  return SPEC_OK;
+}
+
+// ---------------------------------------------------------------- no-allocation E2E-TV
+// The workspace of spec_e2etv_fwd_bwd_noalloc: one array per device, held by the
+// loaded code object until the process ends. Its device address is looked up once
+// per device (hipGetSymbolAddress, with that device current) and only that address
+// is handed to kernels: in host code `scratch` names a host-side stand-in.
+static __device__ __align__(256) unsigned char scratch[SPEC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {};
+
+spec_status scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SPEC_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || !aligned16(p)) return fail(SPEC_ERR_HIP, "scratch has no usable device address");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return SPEC_OK;
+}
+}  // namespace
+
+extern "C" spec_status spec_e2etv_fwd_bwd_noalloc(const spec_tree_layout *layout, int64_t vocab,
+                                                  spec_dtype dtype, const void *d_draft,
+                                                  const void *d_teacher, float inv_norm,
+                                                  float *d_alpha, float *d_loss, float *d_grad,
+                                                  spec_stream stream) {
+  clear_error();
+  spec_status st = check_e2etv_shape(layout, vocab, dtype, inv_norm, true);
+  if (st != SPEC_OK) return st;
+  st = check_e2etv_buffers(d_draft, d_teacher, d_alpha, d_loss, d_grad);
+  if (st != SPEC_OK) return st;
+  const int64_t R = layout->n_steps;
+  const size_t cap = SPEC_NOALLOC_SCRATCH_BYTES;
+  const size_t need = e2etv_work_bytes(R, vocab);
+  bool with_bits = need <= cap;
+  if (!with_bits) {
+    // the fused pipeline needs no bitmask; every other path does
+    bool fused = false;
+    if (dtype == SPEC_BF16 && vocab % 8 == 0 && e2etv_work_bytes_fused(R) <= cap)
+      SPEC_HIP_TRY(e2etv_takes_fused_path(*layout, vocab, dtype, &fused));
+    if (!fused)
+      return fail(SPEC_ERR_UNSUPPORTED,
+                  "%lld steps x vocabulary %lld need %zu bytes of scratch; the no-allocation entry "
+                  "point holds %zu (use spec_e2etv_fwd_bwd with a workspace)",
+                  (long long)R, (long long)vocab, fused ? e2etv_work_bytes_fused(R) : need, cap);
+  }
+  void *base = nullptr;
+  st = scratch_address(&base);
+  if (st != SPEC_OK) return st;
+  E2etvWork ws = e2etv_carve(base, R, vocab);
+  if (!with_bits) ws.bits = nullptr;
+  const float w = inv_norm > 0.f ? inv_norm : (float)(1.0 / (double)R);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  prof_mark(s, "e2etv:begin");
+  SPEC_HIP_TRY(launch_e2etv(*layout, vocab, dtype, d_draft, d_teacher, w, d_alpha, d_loss, d_grad, ws, s));
   return SPEC_OK;
 }
 

@@ -84,7 +84,12 @@ struct E2etvWork {
   int64_t bits_row;
 };
 size_t e2etv_work_bytes(int64_t n_steps, int64_t vocab);
+// Bytes of the workspace before the {q < p} bitmask: all the fused path uses.
+size_t e2etv_work_bytes_fused(int64_t n_steps);
 E2etvWork e2etv_carve(void *d_work, int64_t n_steps, int64_t vocab);
+// Whether launch_e2etv runs the fused pipeline (which never touches w.bits) for
+// this layout, vocabulary and dtype on the current device.
+hipError_t e2etv_takes_fused_path(const spec_tree_layout &L, int64_t vocab, spec_dtype dtype, bool *fused);
 hipError_t launch_e2etv(const spec_tree_layout &L, int64_t vocab, spec_dtype dtype,
                         const void *draft, const void *teacher, float inv_norm, float *alpha,
                         float *loss, float *grad, const E2etvWork &w, hipStream_t stream);

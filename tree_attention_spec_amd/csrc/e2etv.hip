@@ -1131,8 +1131,9 @@ TeamDevice team_device(int dev) {
   if (dev < 0 || dev >= 64) return TeamDevice{};
   TeamDevice &d = cache[dev];
   if (!d.init) {
-    hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
-    hipDeviceGetAttribute(&d.coop, hipDeviceAttributeCooperativeLaunch, dev);
+    // a failed query leaves cus / coop at 0, which turns the team paths off
+    if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) d.cus = 0;
+    if (hipDeviceGetAttribute(&d.coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) d.coop = 0;
     d.occ[1] = team_occupancy<1>();
     d.occ[2] = team_occupancy<2>();
     d.occ[3] = team_occupancy<3>();
@@ -1191,15 +1192,22 @@ hipError_t launch_team_stats(int64_t R, int64_t V, const void *draft, const void
 
 // Fused statistics and gradient if the rows fit a team and every branch spans
 // at most two pipeline steps; *done = false (nothing launched) otherwise.
-hipError_t launch_fused(const spec_tree_layout &L, int64_t V, const void *draft, const void *teacher,
-                        float w, float *alpha, float *loss, float *grad, const E2etvWork &ws,
-                        hipStream_t s, bool *done) {
-  *done = false;
+// Shape of a fused launch: team size T, vectors per lane and team count.
+struct FusePlan {
+  int64_t T = 0, n_teams = 0;
+  int vpl = 0;
+};
+
+// Whether bf16 rows of V (a multiple of 8) entries fit the fused pipeline on the
+// current device: a row slice per member in registers, every branch within two
+// pipeline steps (W_b - 1 <= team count) and the team's rows' branch extents in LDS.
+hipError_t fuse_plan(const spec_tree_layout &L, int64_t V, FusePlan *p, bool *ok) {
+  *ok = false;
   const int64_t R = L.n_steps;
   const int64_t V8 = V / 8;
   const int64_t per_member = (int64_t)kTeamData * kFuseMaxVpl;
   const int64_t T = (V8 + per_member - 1) / per_member;
-  if (T < 1 || T > kTeamMax || V8 * 32 > INT32_MAX || L.max_branch_len > 64) return hipSuccess;
+  if (V % 8 != 0 || T < 1 || T > kTeamMax || V8 * 32 > INT32_MAX || L.max_branch_len > 64) return hipSuccess;
   const int vpl = (int)(((V8 + T - 1) / T + kTeamData - 1) / kTeamData);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -1209,6 +1217,25 @@ hipError_t launch_fused(const spec_tree_layout &L, int64_t V, const void *draft,
   const int64_t n_teams = std::min<int64_t>((int64_t)d.fuse_occ[vpl] * d.cus / T, R);
   if (n_teams < 1 || (int64_t)L.max_branch_len - 1 > n_teams || (R + n_teams - 1) / n_teams > kFuseRowCap)
     return hipSuccess;
+  p->T = T;
+  p->n_teams = n_teams;
+  p->vpl = vpl;
+  *ok = true;
+  return hipSuccess;
+}
+
+hipError_t launch_fused(const spec_tree_layout &L, int64_t V, const void *draft, const void *teacher,
+                        float w, float *alpha, float *loss, float *grad, const E2etvWork &ws,
+                        hipStream_t s, bool *done) {
+  *done = false;
+  const int64_t R = L.n_steps;
+  const int64_t V8 = V / 8;
+  FusePlan plan;
+  bool ok = false;
+  hipError_t e = fuse_plan(L, V, &plan, &ok);
+  if (e != hipSuccess || !ok) return e;
+  const int64_t T = plan.T, n_teams = plan.n_teams;
+  const int vpl = plan.vpl;
   const int64_t n_slots = R * T;
   hipLaunchKernelGGL(e2etv_fuse_clear, dim3((unsigned)std::min<int64_t>(1024, (n_slots + 255) / 256)), dim3(256),
                      0, s, ws.xchg, reinterpret_cast<unsigned long long *>(ws.part), n_slots, ws.status);
@@ -1265,6 +1292,9 @@ hipError_t launch_typed(const spec_tree_layout &L, int64_t V, const void *draft,
     e = launch_fused(L, V, draft, teacher, w, alpha, loss, grad, ws, s, &fused);
     if (e != hipSuccess || fused) return e;
   }
+  // every other path keeps the {q < p} bitmask; a workspace carved without it
+  // (the fused path's share only) cannot take them
+  if (!ws.bits) return hipErrorInvalidValue;
   if (std::is_same<T, __bf16>::value && VEC) {
     e = launch_team_stats(R, V, draft, teacher, ws, s, &team);
     if (e != hipSuccess) return e;
@@ -1302,6 +1332,13 @@ hipError_t launch_typed(const spec_tree_layout &L, int64_t V, const void *draft,
 }
 
 }  // namespace
+
+hipError_t e2etv_takes_fused_path(const spec_tree_layout &L, int64_t V, spec_dtype dtype, bool *fused) {
+  *fused = false;
+  if (dtype != SPEC_BF16 || V % 8 != 0) return hipSuccess;
+  FusePlan plan;
+  return fuse_plan(L, V, &plan, fused);
+}
 
 hipError_t launch_e2etv(const spec_tree_layout &L, int64_t V, spec_dtype dtype, const void *draft,
                         const void *teacher, float w, float *alpha, float *loss, float *grad,
