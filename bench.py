@@ -555,6 +555,83 @@ def gdn_cpu_baseline(s, inp, C, n_rows, per_thread=2):
             "seconds_full_estimate": total, "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def ceilings(args):
+    """Achievable rates on this GPU for the two roofline bounds, from the probe library
+    (tree_attention_spec_amd/libspec_probe.so): HBM streams of the shapes the E2E-TV
+    kernel moves (read-only, write-only, and two bf16 reads to one float32 write per
+    element) with and without non-temporal loads and stores, and chains of bf16 MFMAs."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "tree_attention_spec_amd", "libspec_probe.so")
+    if not os.path.exists(path):
+        raise ImportError("libspec_probe.so is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    c = ctypes
+    lib.spec_probe_read.argtypes = [c.c_void_p, c.c_int64, c.c_void_p, c.c_int, c.c_int, c.c_void_p]
+    lib.spec_probe_write.argtypes = [c.c_void_p, c.c_int64, c.c_int, c.c_int, c.c_void_p]
+    lib.spec_probe_mixed.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_int64, c.c_int, c.c_int, c.c_int,
+                                     c.c_int, c.c_void_p]
+    lib.spec_probe_mfma.argtypes = [c.c_void_p, c.c_int, c.c_int, c.c_void_p]
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = torch.cuda.current_stream(dev)
+    sp = c.c_void_p(stream.cuda_stream)
+
+    def timed(fn, reps=10):
+        for _ in range(2):
+            assert fn() == 0
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
+            assert fn() == 0
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))[reps // 2]
+
+    n = 1 << 30                          # elements of the mixed stream
+    a = torch.randn(n, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, device=dev).to(torch.bfloat16)
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    sink = torch.zeros(16, dtype=torch.int32, device=dev)
+    P = lambda t: c.c_void_p(t.data_ptr())
+    res = {"device": torch.cuda.get_device_name(dev), "compute_units": cus, "streams": {}, "mfma": {}}
+    grids = [0, 8 * cus, 32 * cus]
+    for nt in (0, 1):
+        for g in grids:
+            ms = timed(lambda: lib.spec_probe_read(P(out), 4 * n, P(sink), nt, g, sp))
+            res["streams"]["read nt=%d grid=%d" % (nt, g)] = {"bytes": 4 * n, "ms": ms, "GB/s": 4 * n / ms / 1e6}
+            ms = timed(lambda: lib.spec_probe_write(P(out), 4 * n, nt, g, sp))
+            res["streams"]["write nt=%d grid=%d" % (nt, g)] = {"bytes": 4 * n, "ms": ms, "GB/s": 4 * n / ms / 1e6}
+    for ntl in (0, 1):
+        for nts in (0, 1):
+            for un in (1, 4):
+                for g in grids:
+                    ms = timed(lambda: lib.spec_probe_mixed(P(a), P(b), P(out), n, ntl, nts, un, g, sp))
+                    res["streams"]["mixed bf16+bf16->f32 ntload=%d ntstore=%d unroll=%d grid=%d"
+                                   % (ntl, nts, un, g)] = {"bytes": 8 * n, "ms": ms, "GB/s": 8 * n / ms / 1e6}
+    # correctness of the mixed probe on a few elements (it writes a - b)
+    torch.cuda.synchronize()
+    idx = torch.randint(0, n, (64,), device=dev)
+    assert torch.equal(out[idx], a[idx].float() - b[idx].float())
+    del a, b, out
+    iters = 2048
+    for waves_per_simd in (2, 4, 8):
+        blocks = cus * waves_per_simd          # 4 waves per workgroup, one per SIMD
+        flop = float(blocks) * 4 * 4 * iters * 32 * 32 * 16 * 2
+        ms = timed(lambda: lib.spec_probe_mfma(P(sink), blocks, iters, sp), reps=5)
+        res["mfma"]["bf16 32x32x16, %d waves/SIMD" % waves_per_simd] = {"flop": flop, "ms": ms,
+                                                                        "TFLOP/s": flop / ms / 1e9}
+    best = lambda d, key, pre: max((v[key], k) for k, v in d.items() if k.startswith(pre))
+    res["summary"] = {
+        "read_GBs": best(res["streams"], "GB/s", "read"),
+        "write_GBs": best(res["streams"], "GB/s", "write"),
+        "mixed_GBs": best(res["streams"], "GB/s", "mixed"),
+        "mfma_bf16_TFLOPs": best(res["mfma"], "TFLOP/s", "bf16"),
+        "datasheet": {"hbm_GBs": PEAK_HBM_GBS, "bf16_TFLOPs": PEAK_BF16_TFLOPS},
+    }
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -573,6 +650,8 @@ def main():
                     help="E2E-TV from hidden states through the output head (fused readout, product, E2E-TV)")
     ap.add_argument("--gdn-token-replay", action="store_true",
                     help="with --gdn: replay a token at a time instead of from the trunk pass's cache")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure achievable HBM stream and bf16 MFMA rates with the probe library and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM counters) and exit")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DB",
@@ -596,6 +675,10 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.ceilings:
+        print(json.dumps(ceilings(args)), flush=True)
+        return
 
     if args.copy_calibration:
         n = 1 << 30

@@ -18,6 +18,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libspec_tree.so")
+# ceiling probes for the roofline figures: a library of its own, loaded only by the
+# benchmark's ceiling mode
+PROBE_SOURCE = "probe.hip"
+PROBE_LIB = os.path.join(PKG, "libspec_probe.so")
 ARCH = "gfx950"
 
 SOURCES = ["abi.hip", "pack.hip", "rope.hip", "attn.hip", "e2etv.hip", "e2etv_head.hip", "gdn.hip", "gdn_chunk.hip"]
@@ -55,14 +59,19 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         out = _run([cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
         return obj, out
 
-    with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        results = list(ex.map(compile_one, SOURCES))
+    with ThreadPoolExecutor(min(len(SOURCES) + 1, os.cpu_count() or 1)) as ex:
+        results = list(ex.map(compile_one, SOURCES + [PROBE_SOURCE]))
     for _, out in results:
         if verbose and out.strip():
             print(out)
+    objs = [o for o, _ in results]
+    probe_obj = objs.pop()
     tmp = LIB + ".tmp"
-    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *[o for o, _ in results], "-o", tmp])
+    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", probe_obj, "-o", tmp])
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 
