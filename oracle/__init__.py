@@ -3,7 +3,8 @@
 A plain, slow, obviously correct NumPy float64 statement of what the path
 computes: the proposal-tree pack, tree-masked GQA attention with RoPE at
 semantic positions, predecessor-row readout, the E2E-TV surrogate with its
-gradient (also with teacher logits formed through an output head), and indexed GDN state replay for linear-attention targets. It shares no code with the HIP library and imports nothing from it;
+gradient (also with teacher logits formed through an output head), indexed GDN state replay for
+linear-attention targets, and sparse attention with branch-consistent indexer groups. It shares no code with the HIP library and imports nothing from it;
 the only shared module is ``specgen`` (seeded inputs, no method arithmetic).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
@@ -38,6 +39,15 @@ from .e2etv_ref import (  # noqa: F401
     e2etv_row_stats_ref,
 )
 from .head_ref import e2etv_head_ref, head_logits_ref  # noqa: F401
+from .qsa_ref import (  # noqa: F401
+    qsa_attn_ref,
+    qsa_brute_force_branch_ref,
+    qsa_causal_ref,
+    qsa_group_keys,
+    qsa_history_ref,
+    qsa_pick,
+    qsa_row_structure,
+)
 from .gdn_ref import (  # noqa: F401
     ancestors_ref,
     conv_ancestry_ref,
