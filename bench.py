@@ -11,6 +11,7 @@ recorded by the library on the stream it launches on, inside the timed steps.
     python bench.py [--steps K] [--warmup W] [--config stress] [--no-cpu-baseline]
     python bench.py --gdn [--config gqa8b]   # GDN scoring: trunk pass + indexed replay
     python bench.py --head [--config gqa8b]  # E2E-TV through the output head
+    python bench.py --qsa [--config gqa8b]   # sparse attention with branch-consistent indexer groups
 
 The default workload is the stress tree (trunk 32768, 2048 branches of 1..16
 steps, 64 query / 8 KV heads, vocabulary 151936): the largest of the five
@@ -99,6 +100,9 @@ MARK_KERNELS = {
     "gdn_chunk_out": (["gdn_chunk_out_kernel"], ("gdn_chunk.hip", "gdn_util.h")),
     "gdn_replay": (["gdn_replay_kernel"], ("gdn.hip", "gdn_util.h")),
     "gdn_replay_chunk": (["gdn_replay_chunk_kernel"], ("gdn_chunk.hip", "gdn_util.h")),
+    "qsa_keys": (["qsa_keys_kernel"], ("qsa.hip",)),
+    "qsa_select": (["qsa_select_kernel"], ("qsa.hip",)),
+    "qsa_attn": (["qsa_attn_kernel"], ("qsa.hip", "rope.hip")),
 }
 
 
@@ -482,6 +486,136 @@ def head_bench(args, cfg, s, dev):
     }
 
 
+QSA_GROUP, QSA_TOP_K, QSA_INDEX_DIM = 64, 16, 64
+
+
+def qsa_keys_read(s, G, top_k):
+    """Keys every packed row attends to under sparse attention: the picked groups' G keys
+    each (min(n_c, top_k) groups) plus the causal tail, summed over rows."""
+    import numpy as np
+    tot = 0
+    for t_len in s["trunk_len"]:
+        tot += _qsa_keys_at(np.arange(int(t_len), dtype=np.int64), G, top_k)
+    a = np.asarray(s["anchors"], np.int64)
+    w = np.asarray(s["branch_len"], np.int64)
+    for ab, wb in zip(a, w):
+        pos = ab + np.arange(1, wb, dtype=np.int64)
+        tot += _qsa_keys_at(pos, G, top_k)
+    return int(tot)
+
+
+def _qsa_keys_at(pos, G, top_k):
+    import numpy as np
+    n_c = (pos + 1) // G
+    return int(np.sum(np.minimum(n_c, top_k) * G + (pos + 1 - n_c * G)))
+
+
+def qsa_bench(args, cfg, s, dev):
+    """Sparse attention with branch-consistent indexer groups over the workload's tree:
+    group keys, top-k picks and attention over the picked groups plus the causal tail
+    (G = 64, top_k = 16, index dim 64, N(0,1) indexer inputs), with the readout."""
+    import numpy as np
+    import torch
+    import tree_attention_spec_amd as tas
+    from specgen import gen_qkv, gen_qsa_index
+
+    G, K, DI = QSA_GROUP, QSA_TOP_K, QSA_INDEX_DIM
+    tree = tas.spec_tree_pack(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"])
+    N = tree.n_rows
+    log("sparse attention: N=%d rows, %d/%d heads, G=%d, top_k=%d, index dim %d; generating inputs"
+        % (N, cfg.hq, cfg.hkv, G, K, DI))
+    q, k, v = gen_qkv(cfg, N)
+    idx = gen_qsa_index(cfg.seed, N, cfg.hkv, DI)
+    dvt = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    qt, kt, vt, qit, kit = dvt(q), dvt(k), dvt(v), dvt(idx["qi"]), dvt(idx["ki"])
+    out = torch.empty_like(qt)
+    sel = torch.empty((N, cfg.hkv, K), dtype=torch.int32, device=dev)
+    ro = torch.empty((tree.n_steps, cfg.hq, cfg.head_dim), dtype=qt.dtype, device=dev)
+    work = torch.empty(tas.qsa_work_bytes(tree, cfg.hq, cfg.hkv, cfg.head_dim, DI, G, K), dtype=torch.uint8,
+                       device=dev)
+
+    def call():
+        tas.spec_qsa_attn_fwd(tree, qt, kt, vt, qit, kit, G, K, rope_base=cfg.rope_base, out=out, selected=sel,
+                              readout_out=ro, work=work)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    timers = [tas.KernelTimer(capacity=12) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        with timers[i]:
+            call()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    per = {}
+    for tm in timers:
+        for n, d in tm.durations():
+            per.setdefault(n, []).append(d)
+    kms = {n: sum(x) / len(x) for n, x in per.items()}
+    for kname in kms:
+        log("%s %.4f ms" % (kname, kms[kname]))
+    keys = qsa_keys_read(s, G, K)
+    flop = 4.0 * cfg.head_dim * cfg.hq * keys
+    gathered = float(keys) * cfg.hkv * cfg.head_dim * 2 * 2          # K and V bytes the rows read
+    t_attn = kms.get("qsa_attn", float("nan"))
+    tf = flop / (t_attn * 1e-3) / 1e12
+    res = {
+        "metric": "sparse-attention rows/s (group keys + top-k picks + attention over picked groups and tail)",
+        "value": N / (ms_per_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded inputs)",
+        "config": {"workload": cfg.name + " tree, sparse attention with branch-consistent indexer groups",
+                   "n_rows": N, "heads_q": cfg.hq, "heads_kv": cfg.hkv, "head_dim": cfg.head_dim,
+                   "group_size": G, "top_k": K, "index_dim": DI, "attended_keys": keys,
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": "qsa_attn", "bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS, "algorithmic_flop_per_launch": flop,
+                     "gathered_kv_bytes_per_launch": gathered,
+                     "gathered_GBs": gathered / (t_attn * 1e-3) / 1e9,
+                     "traffic": measured_traffic("qsa_attn", source_hash(*MARK_KERNELS["qsa_attn"][1]),
+                                                 args.config)},
+        "kernel_ms": kms,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = qsa_cpu_baseline(cfg, s, q, k, v, idx, G, K, N)
+    return res
+
+
+def qsa_cpu_baseline(cfg, s, q, k, v, idx, G, K, N, per_thread=2):
+    """The sparse-attention oracle on a bounded sample: per_thread random packed rows per
+    host thread (history walk, group keys, picks, attention), scaled to all rows."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle import pack_ref
+    from oracle.qsa_ref import qsa_attn_ref
+    from specgen import bf16_bits_to_f32
+
+    log("timing the sparse-attention oracle on a bounded sample")
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    lay = pack_ref(s["trunk_len"], s["n_branches"], s["anchors"], s["branch_len"])
+    wid = lambda a: bf16_bits_to_f32(a).astype(np.float64)
+    qd, kd, vd, qid, kid = wid(q), wid(k), wid(v), wid(idx["qi"]), wid(idx["ki"])
+    rows = np.random.default_rng(321).choice(N, size=min(N, per_thread * workers), replace=False)
+    with ThreadPoolExecutor(workers) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(lambda part: qsa_attn_ref(lay, qd, kd, vd, qid, kid, G, K, cfg.rope_base, rows=part),
+                    np.array_split(rows, workers)))
+        total = (N / len(rows)) * (time.perf_counter() - t0)
+    return {"value": N / total, "unit": "rows/s", "cores": workers, "kind": "oracle",
+            "sample": "%d random packed rows of %d, float64 NumPy over %d threads (each row's history, group "
+                      "keys, top-k picks and attention), scaled to all rows" % (len(rows), N, workers),
+            "seconds_full_estimate": total, "host_cpus": len(os.sched_getaffinity(0))}
+
+
 def head_cpu_baseline(s, inp, R, n_sample=32):
     """The head-path oracle on a bounded sample: the first n_sample steps' teacher logits
     (float64 product over the whole head, in vocabulary blocks) and their E2E-TV statistics,
@@ -648,6 +782,9 @@ def main():
                          "instead of the attention + E2E-TV step, and print its own JSON line")
     ap.add_argument("--head", action="store_true",
                     help="E2E-TV from hidden states through the output head (fused readout, product, E2E-TV)")
+    ap.add_argument("--qsa", action="store_true",
+                    help="sparse attention with branch-consistent indexer groups (spec_qsa_attn_fwd) over the "
+                         "workload's tree, with its own JSON line")
     ap.add_argument("--gdn-token-replay", action="store_true",
                     help="with --gdn: replay a token at a time instead of from the trunk pass's cache")
     ap.add_argument("--ceilings", action="store_true",
@@ -660,7 +797,7 @@ def main():
                     help="write profiles/traffic.json from four rocprofv3 --pmc databases and exit")
     args = ap.parse_args()
     if args.config is None:
-        args.config = "gqa8b" if (args.gdn or args.head) else "stress"
+        args.config = "gqa8b" if (args.gdn or args.head or args.qsa) else "stress"
     if args.summarize_pmc:
         print(json.dumps(summarize_pmc(args.summarize_pmc), indent=1))
         return
@@ -704,6 +841,9 @@ def main():
         return
     if args.head:
         print(json.dumps(head_bench(args, cfg, s, dev)), flush=True)
+        return
+    if args.qsa:
+        print(json.dumps(qsa_bench(args, cfg, s, dev)), flush=True)
         return
     layout, mem_bytes = tas.spec_tree_pack_query(s["trunk_len"], s["n_branches"], s["anchors"],
                                                  s["branch_len"])

@@ -14,6 +14,7 @@
  *                       output head from hidden states (never stored)
  *   spec_gdn_trunk_fwd, spec_gdn_replay_fwd  GDN scoring for linear-attention
  *                       targets: shared trunk pass, indexed state replay
+ *   spec_qsa_attn_fwd   sparse attention with branch-consistent indexer groups
  *
  * Sources, cited by page title and section:
  *   [SpecOPD paper page]  "SpecOPD: Branch-Parallel On-Policy Distillation for
@@ -53,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SPEC_TREE_ABI_VERSION 6
+#define SPEC_TREE_ABI_VERSION 7
 #define SPEC_MAX_BRANCH_LEN 64 /* largest supported branch width W_b */
 
 typedef enum spec_status {
@@ -195,6 +196,59 @@ spec_status spec_tree_attn_fwd(const spec_tree_layout *layout, int32_t n_heads_q
                                float rope_base, float softmax_scale, void *d_out,
                                void *d_readout, void *d_work, size_t *work_bytes,
                                spec_stream stream);
+
+/*
+ * spec_qsa_attn_fwd -- sparse attention with branch-consistent indexer groups.
+ *
+ * Defines: [SpecOPD paper page, Figure 4] (branch-parallel scoring with sparse
+ * attention): keys are grouped group_size tokens at a time and each complete
+ * group carries an indexer group key; rows reuse the complete groups of the
+ * shared trunk; a group holding tokens of the row's own branch is keyed from
+ * that branch's history (a branch-specific key, rebuilt per branch); the row's
+ * incomplete group is its causal tail; the row's indexer query picks complete
+ * groups by top-k and attention reads the picked groups' keys plus the tail,
+ * which bypasses top-k.
+ *
+ * For packed row r at semantic position t (history: trunk positions through the
+ * anchor, then the branch's own tokens) and KV head g:
+ *   complete groups j < n_c = floor((t + 1) / G); tail = positions n_c*G .. t;
+ *   key_j  = mean over the group's positions p of ki[row(p), g];
+ *   score_j = <qi[r, g], key_j>; picked = the top_k best (ties: lower j; all if
+ *   n_c <= top_k);
+ *   O[r, h] for the query heads h of g = softmax attention (as spec_tree_attn_fwd:
+ *   rotate-half RoPE at semantic positions, scale) over the keys of the picked
+ *   groups and of the tail.
+ * Readings the pages leave open: the mean as the group key, one indexer query
+ * and key per token and KV head (the pick is shared by the KV head's query
+ * heads), the group a row completes counted as complete.
+ *
+ * Arguments:
+ *   layout        from spec_tree_pack (device arrays resident).
+ *   n_heads_q, n_heads_kv  Hq % Hkv == 0, Hq / Hkv <= 16.
+ *   head_dim      128 (bf16 inputs).
+ *   index_dim     DI, a multiple of 8 in [8, 256].
+ *   group_size    G >= 1; at most 1024 complete groups per row ((max_pos+1)/G).
+ *   top_k         1..64.
+ *   d_q [N,Hq,128], d_k / d_v [N,Hkv,128] bf16, pre-RoPE; d_qi / d_ki [N,Hkv,DI]
+ *                 bf16 indexer queries and keys (used as given).
+ *   rope_base, softmax_scale  as spec_tree_attn_fwd.
+ *   d_out         [N,Hq,128] bf16.
+ *   d_selected    optional [N,Hkv,top_k] int32 out: the picked groups in
+ *                 ascending order, -1 padded (NULL: kept in the workspace).
+ *   d_readout     optional [R,Hq,128]: readout[s] = O[step_pred_row[s]].
+ *   d_work        workspace of *work_bytes bytes, or NULL for a size query.
+ * Scores are summed in float32 in index order; where two groups' float32 scores
+ * tie, the lower index wins.
+ * Errors: SPEC_ERR_INVALID_ARG, SPEC_ERR_UNSUPPORTED (head_dim, group of query
+ * heads, index_dim, group count, sizes past 32-bit offsets), SPEC_ERR_WORKSPACE,
+ * SPEC_ERR_HIP.
+ */
+spec_status spec_qsa_attn_fwd(const spec_tree_layout *layout, int32_t n_heads_q, int32_t n_heads_kv,
+                              int32_t head_dim, int32_t index_dim, int32_t group_size, int32_t top_k,
+                              const void *d_q, const void *d_k, const void *d_v, const void *d_qi,
+                              const void *d_ki, float rope_base, float softmax_scale, void *d_out,
+                              int32_t *d_selected, void *d_readout, void *d_work, size_t *work_bytes,
+                              spec_stream stream);
 
 /*
  * spec_e2etv_fwd_bwd -- E2E-TV surrogate, loss and gradient w.r.t. the draft.

@@ -1,7 +1,8 @@
 """Seeded synthetic inputs for the branch-parallel scoring path.
 
 This package is the only code shared by the CPU oracle and the HIP path. It
-draws tree structures, Q/K/V tensors, logit rows and GDN replay inputs from
+draws tree structures, Q/K/V tensors, logit rows, GDN replay inputs and the
+indexer queries and keys of sparse attention from
 counter-addressed NumPy PCG64 streams (hidden states
 and output heads too) and rounds them to bfloat16 where a
 workload asks for it.
@@ -18,5 +19,6 @@ from .gen import (  # noqa: F401
     gen_logits,
     gen_logit_rows,
     gen_qkv,
+    gen_qsa_index,
     gen_structure,
 )

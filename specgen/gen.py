@@ -26,6 +26,7 @@ LOGIT_CHUNK_ROWS = 8
 _S_STRUCT, _S_Q, _S_K, _S_V, _S_DRAFT, _S_TEACHER = range(6)
 _S_GDN_Q, _S_GDN_K, _S_GDN_V, _S_GDN_TAPS, _S_GDN_GATES, _S_GDN_STATE = range(6, 12)
 _S_HIDDEN, _S_HEAD, _S_HEAD_DRAFT = range(12, 15)
+_S_QSA_QI, _S_QSA_KI = range(15, 17)
 HEAD_CHUNK_ROWS = 1024
 
 
@@ -267,4 +268,30 @@ def gen_head_draft_rows(seed: int, n_steps: int, vocab: int, rows, logit_std: fl
         _fill_scaled_bf16(blk, seed, _S_HEAD_DRAFT, int(c), logit_std)
         sel = rows // LOGIT_CHUNK_ROWS == c
         out[sel] = blk[rows[sel] - c * LOGIT_CHUNK_ROWS]
+    return out
+
+
+def _fill_grid_bf16(out_rows: np.ndarray, seed: int, stream: int, chunk: int, levels: int):
+    x = _rng(seed, stream, chunk).integers(-levels, levels + 1, size=out_rows.shape)
+    out_rows[...] = f32_to_bf16_bits((x / np.float32(levels)).astype(np.float32))
+
+
+def gen_qsa_index(seed: int, n_rows: int, n_heads_kv: int, index_dim: int, grid: int = 0):
+    """Indexer queries and keys of sparse attention: [N, Hkv, DI] each, bf16 bit patterns.
+
+    grid = 0: N(0,1) draws. grid = m > 0: values k/m for integers k in [-m, m]
+    (exactly representable in bf16), so that with a power-of-two group size every
+    group mean and every score is exact in float32 as well as in float64.
+    """
+    out = {}
+    for name, stream in (("qi", _S_QSA_QI), ("ki", _S_QSA_KI)):
+        arr = np.empty((n_rows, n_heads_kv, index_dim), dtype=np.uint16)
+        jobs = [(arr[r0:r0 + QKV_CHUNK_ROWS], c) for c, r0 in enumerate(range(0, n_rows, QKV_CHUNK_ROWS))]
+        if grid:
+            fill = lambda j: _fill_grid_bf16(j[0], seed, stream, j[1], grid)
+        else:
+            fill = lambda j: _fill_scaled_bf16(j[0], seed, stream, j[1], 1.0)
+        with ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(fill, jobs))
+        out[name] = arr
     return out

@@ -176,6 +176,30 @@ def test_e2etv_noalloc_checks(tas):
     assert "scratch" in lib.spec_last_error().decode()
 
 
+def test_qsa_size_query_and_checks(tas):
+    """spec_qsa_attn_fwd: size query and argument checks, no GPU touched."""
+    lib = tas.library()
+    L = _query_layout(tas)
+    size = ctypes.c_size_t(0)
+    call = lambda hq=32, hkv=8, D=128, di=64, G=64, k=16, base=10000.0, work=None, sz=size: lib.spec_qsa_attn_fwd(
+        ctypes.byref(L), hq, hkv, D, di, G, k, None, None, None, None, None, base, 0.0, None, None, None, work,
+        ctypes.byref(sz), None)
+    assert call() == 0
+    # K / V^T tiles, the group keys and the picks
+    assert size.value >= 2 * L.n_rows * 8 * 128 * 2 + L.n_rows * 8 * 16 * 4
+    assert call(D=64) == 2                 # head dim other than 128
+    assert call(hq=64, hkv=2) == 2         # 32 query heads per KV head
+    assert call(hq=32, hkv=7) == 1         # Hq % Hkv != 0
+    assert call(di=12) == 2                # index dim not a multiple of 8
+    assert call(k=0) == 1 and call(k=65) == 1
+    assert call(G=0) == 1
+    assert call(G=2) == 2                  # more than 1024 complete groups per row
+    assert call(base=-1.0) == 1
+    big = ctypes.c_size_t(1 << 40)
+    # a workspace with a layout that has no device arrays is refused before any launch
+    assert call(work=ctypes.c_void_p(0x1000), sz=big) == 1
+
+
 def test_e2etv_head_size_query_and_checks(tas):
     """spec_e2etv_head_fwd_bwd: size query and argument checks, no GPU touched."""
     lib = tas.library()

@@ -20,7 +20,8 @@ from ._lib import (LAYOUT_ARRAYS, SPEC_BF16, SPEC_F32, SPEC_MAX_BRANCH_LEN, Spec
                    spec_tree_layout)
 
 __all__ = ["spec_tree_pack", "spec_tree_pack_query", "spec_tree_attn_fwd", "spec_e2etv_fwd_bwd",
-           "spec_e2etv_head_fwd_bwd", "e2etv_head_work_bytes",
+           "spec_e2etv_head_fwd_bwd", "e2etv_head_work_bytes", "spec_qsa_attn_fwd", "qsa_work_bytes",
+           "spec_e2etv_fwd_bwd_noalloc",
            "spec_gdn_trunk_fwd", "spec_gdn_replay_fwd", "gdn_checkpoint_slots", "gdn_trunk_work_bytes", "PackedTree", "SpecError", "library",
            "KernelTimer"]
 
@@ -169,6 +170,57 @@ def spec_tree_attn_fwd(tree: PackedTree, q: torch.Tensor, k: torch.Tensor, v: to
     st, _ = _attn_call(tree, hq, hkv, D, dt, q, k, v, rope_base, softmax_scale, out, readout_out, work)
     _lib.check(library(), st)
     return out, readout_out
+
+
+def _qsa_call(tree, hq, hkv, D, di, G, top_k, q, k, v, qi, ki, rope_base, scale, out, sel, readout, work):
+    lib = library()
+    nbytes = ctypes.c_size_t(work.numel() if work is not None else 0)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    dev = q.device if q is not None else None
+    return lib.spec_qsa_attn_fwd(ctypes.byref(tree.layout), hq, hkv, D, di, G, top_k, ptr(q), ptr(k), ptr(v),
+                                 ptr(qi), ptr(ki), float(rope_base), float(scale), ptr(out), ptr(sel),
+                                 ptr(readout), ptr(work), ctypes.byref(nbytes),
+                                 ctypes.c_void_p(_stream(dev)) if dev is not None else None), nbytes.value
+
+
+def qsa_work_bytes(tree, n_heads_q, n_heads_kv, head_dim, index_dim, group_size, top_k) -> int:
+    st, n = _qsa_call(tree, n_heads_q, n_heads_kv, head_dim, index_dim, group_size, top_k, None, None, None,
+                      None, None, 10000.0, 0.0, None, None, None, None)
+    _lib.check(library(), st)
+    return n
+
+
+def spec_qsa_attn_fwd(tree: PackedTree, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                      qi: torch.Tensor, ki: torch.Tensor, group_size: int, top_k: int,
+                      rope_base: float = 10000.0, softmax_scale: float = 0.0, out=None, selected=None,
+                      readout: bool = True, readout_out=None, work=None):
+    """Sparse attention with branch-consistent indexer groups over a packed tree.
+
+    q [N, Hq, 128], k / v [N, Hkv, 128], qi / ki [N, Hkv, DI], all bf16. Returns
+    (out [N, Hq, 128] bf16, selected [N, Hkv, top_k] int32 ascending group indices
+    with -1 padding, readout [R, Hq, 128] bf16 or None)."""
+    N, hq, D = q.shape
+    hkv, di = ki.shape[1], ki.shape[2]
+    if N != tree.n_rows or k.shape != (N, hkv, D) or v.shape != (N, hkv, D) or qi.shape != (N, hkv, di):
+        raise ValueError("q [N,Hq,D], k/v [N,Hkv,D], qi/ki [N,Hkv,DI] with N = tree.n_rows")
+    for t in (q, k, v, qi, ki):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("sparse attention inputs must be contiguous bf16")
+    if out is None:
+        out = torch.empty_like(q)
+    if selected is None:
+        selected = torch.empty((N, hkv, top_k), dtype=torch.int32, device=q.device)
+    if readout and readout_out is None and tree.n_steps > 0:
+        readout_out = torch.empty((tree.n_steps, hq, D), dtype=q.dtype, device=q.device)
+    if not readout:
+        readout_out = None
+    if work is None:
+        work = torch.empty(max(qsa_work_bytes(tree, hq, hkv, D, di, group_size, top_k), 256), dtype=torch.uint8,
+                           device=q.device)
+    st, _ = _qsa_call(tree, hq, hkv, D, di, group_size, top_k, q, k, v, qi, ki, rope_base, softmax_scale, out,
+                      selected, readout_out, work)
+    _lib.check(library(), st)
+    return out, selected, readout_out
 
 
 def e2etv_work_bytes(tree, vocab, dtype) -> int:

@@ -24,7 +24,8 @@ PROBE_SOURCE = "probe.hip"
 PROBE_LIB = os.path.join(PKG, "libspec_probe.so")
 ARCH = "gfx950"
 
-SOURCES = ["abi.hip", "pack.hip", "rope.hip", "attn.hip", "e2etv.hip", "e2etv_head.hip", "gdn.hip", "gdn_chunk.hip"]
+SOURCES = ["abi.hip", "pack.hip", "rope.hip", "attn.hip", "qsa.hip", "e2etv.hip", "e2etv_head.hip", "gdn.hip",
+           "gdn_chunk.hip"]
 
 # Packed fp32 VALU ops are disabled for device code; hipcc's host pass warns
 # that it does not know the feature, which is harmless.

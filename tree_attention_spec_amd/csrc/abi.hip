@@ -264,6 +264,74 @@ extern "C" spec_status spec_e2etv_fwd_bwd(const spec_tree_layout *layout, int64_
   return SPEC_OK;
 }
 
+extern "C" spec_status spec_qsa_attn_fwd(const spec_tree_layout *layout, int32_t hq, int32_t hkv, int32_t D,
+                                         int32_t index_dim, int32_t group_size, int32_t top_k,
+                                         const void *d_q, const void *d_k, const void *d_v, const void *d_qi,
+                                         const void *d_ki, float rope_base, float softmax_scale, void *d_out,
+                                         int32_t *d_selected, void *d_readout, void *d_work,
+                                         size_t *work_bytes, spec_stream stream) {
+  clear_error();
+  if (!work_bytes) return fail(SPEC_ERR_INVALID_ARG, "work_bytes must be non-NULL");
+  spec_status st = check_layout(layout, d_work != nullptr);
+  if (st != SPEC_OK) return st;
+  if (d_work && (!layout->row_tree || !layout->row_branch || !layout->row_anchor || !layout->branch_tree ||
+                 !layout->branch_anchor || !layout->branch_len || !layout->branch_off || !layout->tree_trunk_len))
+    return fail(SPEC_ERR_INVALID_ARG, "layout device arrays are missing (pack with a buffer first)");
+  if (hq < 1 || hkv < 1 || hq % hkv != 0)
+    return fail(SPEC_ERR_INVALID_ARG, "need Hq >= 1, Hkv >= 1 and Hq %% Hkv == 0 (got %d, %d)", hq, hkv);
+  if (D != 128) return fail(SPEC_ERR_UNSUPPORTED, "head_dim %d: the sparse path takes 128", D);
+  if (hq / hkv > 16) return fail(SPEC_ERR_UNSUPPORTED, "GQA group %d larger than 16", hq / hkv);
+  if (index_dim < 8 || index_dim > 256 || index_dim % 8 != 0)
+    return fail(SPEC_ERR_UNSUPPORTED, "index_dim %d: a multiple of 8 in [8, 256]", index_dim);
+  if (group_size < 1 || top_k < 1 || top_k > 64)
+    return fail(SPEC_ERR_INVALID_ARG, "need group_size >= 1 and 1 <= top_k <= 64 (got %d, %d)", group_size,
+                top_k);
+  if (((int64_t)layout->max_pos + 1) / group_size > 1024)
+    return fail(SPEC_ERR_UNSUPPORTED, "%lld complete groups per row (at most 1024)",
+                (long long)(((int64_t)layout->max_pos + 1) / group_size));
+  if (!(rope_base > 0.f) || !std::isfinite(rope_base))
+    return fail(SPEC_ERR_INVALID_ARG, "rope_base must be a positive finite number");
+  const int64_t n_tiles = (layout->n_rows + kKeyTile - 1) / kKeyTile;
+  if (n_tiles * kKeyTile * D * 2 >= ((int64_t)1 << 31) || (int64_t)layout->n_rows * hq * D >= ((int64_t)1 << 31))
+    return fail(SPEC_ERR_UNSUPPORTED, "tensor too large for 32-bit offsets");
+  const AttnWork w = attn_work(*layout, hkv, D, SPEC_BF16);
+  const size_t off_keys = w.total;
+  const size_t off_sel = off_keys + align_up(qsa_keys_floats(*layout, hkv, index_dim, group_size) * 4, 256);
+  const size_t total = off_sel + align_up((size_t)layout->n_rows * hkv * top_k * 4, 256);
+  if (!d_work) {
+    *work_bytes = total;
+    return SPEC_OK;
+  }
+  if (*work_bytes < total) {
+    size_t have = *work_bytes;
+    *work_bytes = total;
+    return fail(SPEC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", have, total);
+  }
+  if (!d_q || !d_k || !d_v || !d_qi || !d_ki || !d_out)
+    return fail(SPEC_ERR_INVALID_ARG, "d_q, d_k, d_v, d_qi, d_ki and d_out must be non-NULL");
+  if (!aligned16(d_q) || !aligned16(d_k) || !aligned16(d_v) || !aligned16(d_qi) || !aligned16(d_ki) ||
+      !aligned16(d_out) || !aligned16(d_work) || (d_readout && !aligned16(d_readout)) ||
+      (d_selected && !aligned16(d_selected)))
+    return fail(SPEC_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)D);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *wb = static_cast<char *>(d_work);
+  float2 *tab = reinterpret_cast<float2 *>(wb + w.off_tab);
+  prof_mark(s, "qsa:begin");
+  SPEC_HIP_TRY(launch_rope_table(tab, layout->max_pos + 1, D / 2, (double)rope_base, s));
+  prof_mark(s, "rope_table");
+  SPEC_HIP_TRY(launch_kv_tiles(d_k, d_v, wb + w.off_k, wb + w.off_v, tab, layout->row_pos, layout->n_rows, hkv, s));
+  prof_mark(s, "kv_tiles");
+  int32_t *sel = d_selected ? d_selected : reinterpret_cast<int32_t *>(wb + off_sel);
+  SPEC_HIP_TRY(launch_qsa(*layout, hq, hkv, index_dim, group_size, top_k, d_q, d_qi, d_ki, wb + w.off_k,
+                          wb + w.off_v, tab, scale, reinterpret_cast<float *>(wb + off_keys), sel, d_out, s));
+  if (d_readout && layout->n_steps > 0) {
+    SPEC_HIP_TRY(launch_readout(layout->step_pred_row, layout->n_steps, (int64_t)hq * D * 2, d_out, d_readout, s));
+    prof_mark(s, "readout");
+  }
+  return SPEC_OK;
+}
+
 // ---------------------------------------------------------------- no-allocation E2E-TV
 // The workspace of spec_e2etv_fwd_bwd_noalloc: one array per device, held by the
 // loaded code object until the process ends. Its device address is looked up once

@@ -101,6 +101,15 @@ hipError_t launch_e2etv_tail(const spec_tree_layout &L, int64_t vocab, spec_dtyp
                              const void *draft, float inv_norm, int team, float *alpha,
                              float *loss, float *grad, const E2etvWork &w, hipStream_t stream);
 
+// Sparse attention with branch-consistent indexer groups (head dim 128, bf16):
+// group keys, top-k picks and attention over the picked groups plus the causal
+// tail, reading the K / V^T tiles of launch_kv_tiles.
+size_t qsa_keys_floats(const spec_tree_layout &L, int32_t hkv, int32_t index_dim, int32_t group_size);
+hipError_t launch_qsa(const spec_tree_layout &L, int32_t hq, int32_t hkv, int32_t index_dim,
+                      int32_t group_size, int32_t top_k, const void *q, const void *qi, const void *ki,
+                      const void *kt, const void *vt, const float2 *tab, float scale, float *keys,
+                      int32_t *sel, void *out, hipStream_t stream);
+
 // E2E-TV with the teacher logits formed from hidden states and an output head.
 size_t e2etv_head_work_bytes(int64_t n_steps, int64_t vocab);
 hipError_t launch_e2etv_head(const spec_tree_layout &L, int64_t vocab, int32_t d_model,
