@@ -285,8 +285,8 @@ spec_status spec_qsa_attn_fwd(const spec_tree_layout *layout, int32_t n_heads_q,
  * For bf16 logits with V a multiple of 8 the work runs as one cooperative
  * kernel whose workgroups wait on each other through bounded polls; if a poll
  * ever times out (it cannot while the kernel is resident on the device as a
- * whole) alpha and the loss come back NaN. Calls that share a workspace must
- * not overlap in time.
+ * whole) alpha and the loss come back NaN and spec_e2etv_status reports it.
+ * Calls that share a workspace must not overlap in time.
  * Errors: SPEC_ERR_INVALID_ARG, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP.
  */
 spec_status spec_e2etv_fwd_bwd(const spec_tree_layout *layout, int64_t vocab,
@@ -294,6 +294,19 @@ spec_status spec_e2etv_fwd_bwd(const spec_tree_layout *layout, int64_t vocab,
                                const void *d_teacher, float inv_norm, float *d_alpha,
                                float *d_loss, float *d_grad, void *d_work, size_t *work_bytes,
                                spec_stream stream);
+
+/*
+ * spec_e2etv_status -- the status word of the last E2E-TV call on a workspace.
+ *
+ * Waits for `stream` (the stream of that call) and copies the call's status
+ * word to *h_status: 0 when every bounded wait of its team kernels was met,
+ * nonzero when one timed out (alpha and the loss of that call are then NaN).
+ * layout and vocab must be those of the call; d_work its workspace, or NULL
+ * for the array of spec_e2etv_fwd_bwd_noalloc on the current device.
+ * Errors: SPEC_ERR_INVALID_ARG, SPEC_ERR_HIP.
+ */
+spec_status spec_e2etv_status(const spec_tree_layout *layout, int64_t vocab, const void *d_work,
+                              uint32_t *h_status, spec_stream stream);
 
 /*
  * spec_e2etv_fwd_bwd_noalloc -- spec_e2etv_fwd_bwd without a caller workspace.
@@ -369,14 +382,13 @@ spec_status spec_e2etv_head_fwd_bwd(const spec_tree_layout *layout, int64_t voca
  * spec_gdn_replay_fwd -- indexed GDN state replay: the linear-attention
  * (GDN) outputs of every branch row.
  *
- * Defines: [SpecOPD paper page, Figure 5] (branch-parallel scoring with linear
- * attention): a shared trunk pass keeps an FP32 GDN state at every
- * chunk-token boundary; a branch starts from the checkpoint at or below its
- * anchor, advances it with the trunk tokens after that checkpoint through the
- * anchor, then takes its own tokens, updating the state and reading it with
- * each token's query; checkpoints are only read; the short causal
- * convolution follows the branch's ancestry. [SpecOPD paper page, Figure 13]:
- * GDN work includes that replay.
+ * Defines: [SpecOPD paper page, Figure 5] (GDN scoring of branches from stored
+ * trunk states): the trunk runs once and its FP32 state is stored every `chunk`
+ * tokens; a branch takes the last stored state at or before its anchor, runs
+ * the remaining trunk tokens up to the anchor on its own copy, then runs its
+ * own tokens, producing one output per token; the replay never writes a stored
+ * state, and each token's convolution window runs over its ancestors.
+ * [SpecOPD paper page, Figure 13]: the replayed trunk tokens count as GDN work.
  *
  * The pages do not write the recurrence out; this is the gated delta rule,
  * per head, with state S (D x D, value rows i, key columns j):
@@ -431,8 +443,8 @@ spec_status spec_gdn_replay_fwd(const spec_tree_layout *layout, int32_t n_heads,
  * spec_gdn_trunk_fwd -- the shared trunk pass of GDN scoring: the GDN outputs
  * of every trunk row and the checkpoints spec_gdn_replay_fwd reads.
  *
- * Defines: [SpecOPD paper page, Figure 5] (a shared trunk pass keeps an FP32
- * GDN state at every chunk-token boundary). Same recurrence, features and
+ * Defines: [SpecOPD paper page, Figure 5] (the one pass over the trunk that
+ * stores the FP32 GDN state every `chunk` tokens). Same recurrence, features and
  * argument meanings as spec_gdn_replay_fwd, along each tree's trunk from the
  * zero state: o is written for every trunk row, and slot c of d_ckpt (key-major
  * state, layout as for spec_gdn_replay_fwd) receives the state after trunk

@@ -3,13 +3,12 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Sources:
-  * [SpecOPD paper page, Figure 5]: branch-parallel scoring with linear
-    attention. A shared trunk pass keeps an FP32 GDN state at every C = 64
-    boundary. For a branch, a block copies the state of the checkpoint at or
-    below the anchor, advances it with the cached trunk features from there
-    through the anchor, then updates it with the branch's own tokens and reads
-    it with each token's query to give the GDN outputs. Checkpoints are never
-    written; the short causal convolution follows the branch's ancestry.
+  * [SpecOPD paper page, Figure 5]: GDN scoring of branches. One pass over the
+    trunk stores the FP32 state every C = 64 tokens; a branch loads the last
+    stored state at or before its anchor, runs the trunk tokens from there to
+    the anchor, then runs its own tokens and reads the state with each token's
+    query for its output. Stored states are never overwritten, and each
+    token's convolution window runs over its ancestors.
   * [SpecOPD paper page, Figure 13]: GDN work counts include that replay.
     The trunk pass here also gives every trunk token's output, which is what
     scoring the trunk needs.

@@ -176,6 +176,16 @@ def test_e2etv_noalloc_checks(tas):
     assert "scratch" in lib.spec_last_error().decode()
 
 
+def test_e2etv_status_checks(tas):
+    lib = tas.library()
+    L = _query_layout(tas)
+    v = ctypes.c_uint32(7)
+    assert lib.spec_e2etv_status(ctypes.byref(L), 151936, ctypes.c_void_p(0x1000), None, None) == 1
+    assert lib.spec_e2etv_status(None, 151936, ctypes.c_void_p(0x1000), ctypes.byref(v), None) == 1
+    assert lib.spec_e2etv_status(ctypes.byref(L), 0, ctypes.c_void_p(0x1000), ctypes.byref(v), None) == 1
+    assert v.value == 7
+
+
 def test_qsa_size_query_and_checks(tas):
     """spec_qsa_attn_fwd: size query and argument checks, no GPU touched."""
     lib = tas.library()

@@ -131,6 +131,19 @@ def test_e2etv_bf16_few_rows(width):
     _full_compare(case, z, y)
 
 
+def test_e2etv_status_word_after_calls():
+    """The status word the fused kernel raises on a timed-out wait reads 0 after normal calls."""
+    import torch
+    import tree_attention_spec_amd as tas
+    case = Case(small_config("gqa8b", trunk=300, branches=5, width=16, vocab=151936))
+    z, y = case.logits()
+    tree = _pack(case.s)
+    work = torch.empty(tas.e2etv_work_bytes(tree, 151936, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    zt, yt = to_device(z), to_device(y)
+    tas.spec_e2etv_fwd_bwd(tree, zt, yt, work=work)
+    assert tas.spec_e2etv_status(tree, 151936, work) == 0
+
+
 def test_e2etv_forward_only_and_determinism():
     import torch
     case = Case(small_config("gqa8b", trunk=300, branches=5, width=16, vocab=151936))

@@ -21,7 +21,7 @@ from ._lib import (LAYOUT_ARRAYS, SPEC_BF16, SPEC_F32, SPEC_MAX_BRANCH_LEN, Spec
 
 __all__ = ["spec_tree_pack", "spec_tree_pack_query", "spec_tree_attn_fwd", "spec_e2etv_fwd_bwd",
            "spec_e2etv_head_fwd_bwd", "e2etv_head_work_bytes", "spec_qsa_attn_fwd", "qsa_work_bytes",
-           "spec_e2etv_fwd_bwd_noalloc",
+           "spec_e2etv_fwd_bwd_noalloc", "spec_e2etv_status",
            "spec_gdn_trunk_fwd", "spec_gdn_replay_fwd", "gdn_checkpoint_slots", "gdn_trunk_work_bytes", "PackedTree", "SpecError", "library",
            "KernelTimer"]
 
@@ -262,6 +262,19 @@ def spec_e2etv_fwd_bwd(tree: PackedTree, draft: torch.Tensor, teacher: torch.Ten
                                            ptr(grad_out), ptr(work), ctypes.byref(nbytes),
                                            ctypes.c_void_p(_stream(dev))))
     return alpha_out, loss_out, grad_out
+
+
+def spec_e2etv_status(tree: PackedTree, vocab: int, work=None, device=None) -> int:
+    """Status word of the last E2E-TV call on `work` (None: the no-allocation array of the
+    current device), after waiting for the current stream: 0 when every bounded wait of
+    the team kernels was met."""
+    lib = library()
+    v = ctypes.c_uint32(0)
+    dev = work.device if work is not None else (device or torch.device("cuda", torch.cuda.current_device()))
+    _lib.check(lib, lib.spec_e2etv_status(ctypes.byref(tree.layout), int(vocab),
+                                          ctypes.c_void_p(work.data_ptr()) if work is not None else None,
+                                          ctypes.byref(v), ctypes.c_void_p(_stream(dev))))
+    return v.value
 
 
 def spec_e2etv_fwd_bwd_noalloc(tree: PackedTree, draft: torch.Tensor, teacher: torch.Tensor,

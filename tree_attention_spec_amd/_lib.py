@@ -86,6 +86,7 @@ LAYOUT_ARRAYS = {
 }
 
 EXPORTS = ["spec_tree_pack", "spec_tree_attn_fwd", "spec_e2etv_fwd_bwd", "spec_e2etv_fwd_bwd_noalloc",
+           "spec_e2etv_status",
            "spec_e2etv_head_fwd_bwd", "spec_qsa_attn_fwd",
            "spec_gdn_trunk_fwd",
            "spec_gdn_replay_fwd", "spec_status_string", "spec_last_error", "spec_abi_version",
@@ -115,6 +116,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_e2etv_fwd_bwd_noalloc.argtypes = [c.POINTER(spec_tree_layout), c.c_int64, c.c_int, c.c_void_p,
                                                c.c_void_p, c.c_float, c.c_void_p, c.c_void_p, c.c_void_p,
                                                c.c_void_p]
+    lib.spec_e2etv_status.restype = c.c_int
+    lib.spec_e2etv_status.argtypes = [c.POINTER(spec_tree_layout), c.c_int64, c.c_void_p,
+                                      c.POINTER(c.c_uint32), c.c_void_p]
     lib.spec_qsa_attn_fwd.restype = c.c_int
     lib.spec_qsa_attn_fwd.argtypes = [c.POINTER(spec_tree_layout), c.c_int32, c.c_int32, c.c_int32, c.c_int32,
                                       c.c_int32, c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,

@@ -164,6 +164,11 @@ extern "C" spec_status spec_tree_attn_fwd(const spec_tree_layout *layout, int32_
   if ((int64_t)layout->n_rows * hq * D > (int64_t)INT32_MAX * 8)
     return fail(SPEC_ERR_UNSUPPORTED, "tensor too large");
   const AttnWork w = attn_work(*layout, hkv, D, dtype);
+  // the register-staged kernels address one KV head's K and V through buffer
+  // descriptors whose byte ranges and offsets are 32-bit
+  if (!w.tiled && dtype == SPEC_BF16 && (int64_t)layout->n_rows * hkv * D * 2 >= ((int64_t)1 << 32))
+    return fail(SPEC_ERR_UNSUPPORTED, "K / V of %lld rows x %d heads x %d dims past 4 GiB (head dim 128 has no "
+                "such limit)", (long long)layout->n_rows, hkv, D);
   if (!d_work) {
     *work_bytes = w.total;
     return SPEC_OK;
@@ -396,6 +401,29 @@ extern "C" spec_status spec_e2etv_fwd_bwd_noalloc(const spec_tree_layout *layout
   hipStream_t s = static_cast<hipStream_t>(stream);
   prof_mark(s, "e2etv:begin");
   SPEC_HIP_TRY(launch_e2etv(*layout, vocab, dtype, d_draft, d_teacher, w, d_alpha, d_loss, d_grad, ws, s));
+  return SPEC_OK;
+}
+
+extern "C" spec_status spec_e2etv_status(const spec_tree_layout *layout, int64_t vocab, const void *d_work,
+                                         uint32_t *h_status, spec_stream stream) {
+  clear_error();
+  if (!layout || !h_status) return fail(SPEC_ERR_INVALID_ARG, "layout and h_status must be non-NULL");
+  if (layout->n_steps < 1) return fail(SPEC_ERR_INVALID_ARG, "the layout has no supervised steps");
+  if (vocab < 1 || vocab > (int64_t)INT32_MAX)
+    return fail(SPEC_ERR_INVALID_ARG, "vocab %lld out of range", (long long)vocab);
+  const void *base = d_work;
+  if (!base) {
+    void *p = nullptr;
+    spec_status st = scratch_address(&p);
+    if (st != SPEC_OK) return st;
+    base = p;
+  }
+  const E2etvWork w = e2etv_carve(const_cast<void *>(base), layout->n_steps, vocab);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  SPEC_HIP_TRY(hipMemcpyAsync(&v, w.status, sizeof(v), hipMemcpyDeviceToHost, s));
+  SPEC_HIP_TRY(hipStreamSynchronize(s));
+  *h_status = v;
   return SPEC_OK;
 }
 

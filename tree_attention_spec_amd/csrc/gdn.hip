@@ -1,13 +1,12 @@
 // Indexed GDN state replay for the branch rows of a packed proposal tree.
 //
-// [SpecOPD paper page, Figure 5]: a shared trunk pass keeps an FP32 GDN state
-// at every `chunk`-token boundary. For a branch, a block copies the state of
-// the checkpoint at or below the anchor into registers, advances it with the
-// trunk tokens after that checkpoint through the anchor, then takes the
-// branch's own tokens, updating the state and reading it with each token's
-// query. Checkpoints are only read; the short causal convolution follows the
-// branch's ancestry. [SpecOPD paper page, Figure 13]: GDN work includes that
-// replay.
+// [SpecOPD paper page, Figure 5]: the trunk runs once and its FP32 GDN state is
+// stored every `chunk` tokens. A branch loads the last stored state at or
+// before its anchor into registers, runs the trunk tokens between that state
+// and the anchor, then its own tokens, one output per token; stored states are
+// never written here, and each token's convolution window runs over its
+// ancestors. [SpecOPD paper page, Figure 13]: the replayed trunk tokens count as
+// GDN work.
 //
 // Recurrence (gated delta rule, per head; state S is D x D with value rows i
 // and key columns j):
