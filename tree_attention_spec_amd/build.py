@@ -63,8 +63,10 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     with ThreadPoolExecutor(min(len(SOURCES) + 1, os.cpu_count() or 1)) as ex:
         results = list(ex.map(compile_one, SOURCES + [PROBE_SOURCE]))
     for _, out in results:
-        if verbose and out.strip():
-            print(out)
+        # compiler warnings are always shown (the packed-fp32 host note is filtered in _run)
+        lines = [l for l in out.splitlines() if verbose or "warning" in l or "error" in l]
+        if lines:
+            print("\n".join(lines))
     objs = [o for o, _ in results]
     probe_obj = objs.pop()
     tmp = LIB + ".tmp"
