@@ -134,8 +134,11 @@ __device__ inline float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Two waves per SIMD where the LDS allows it (four or more waves per workgroup);
+// with one or two waves per workgroup the double-buffered tiles already cap a CU
+// at one wave per SIMD, so only that is asked for.
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void tree_attn_bf16_kernel(
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4 ? 2 : 1, 2))) void tree_attn_bf16_kernel(
     const AttnItem *__restrict__ items, int hkv, int group, int hsub,
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ kws, const __bf16 *__restrict__ v,
     __bf16 *__restrict__ out, const float2 *__restrict__ tab, const int32_t *__restrict__ row_pos,
@@ -367,7 +370,7 @@ struct alignas(16) TiledSmem {
 };
 
 template <int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void tree_attn_tiled_kernel(
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4 ? 2 : 1, 2))) void tree_attn_tiled_kernel(
     const AttnItem *__restrict__ items, int hkv, int group, int hsub,
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ kt, const __bf16 *__restrict__ vt,
     __bf16 *__restrict__ out, const float2 *__restrict__ tab, const int32_t *__restrict__ row_pos,
