@@ -355,7 +355,8 @@ spec_status spec_e2etv_fwd_bwd_noalloc(const spec_tree_layout *layout, int64_t v
  *   layout        from spec_tree_pack (uses n_steps, n_branches,
  *                 max_branch_len, step_off, step_pred_row).
  *   vocab         V >= 8, a multiple of 8.
- *   d_model       hidden size, a positive multiple of 64.
+ *   d_model       hidden size, a positive multiple of 64; the hidden states
+ *                 (N x d_model bf16) must stay under 2 GiB.
  *   draft_dtype   SPEC_BF16 or SPEC_F32: the dtype of d_draft.
  *   d_draft       [R, V] draft logits; NaN or -inf mean inactive support.
  *   d_hidden      [N, d_model] bf16 final hidden states of every packed row
@@ -369,8 +370,8 @@ spec_status spec_e2etv_fwd_bwd_noalloc(const spec_tree_layout *layout, int64_t v
  * overlap in time. Data preconditions (not checked; violations give NaN):
  * hidden and head finite, at least one active draft entry per row.
  * Errors: SPEC_ERR_INVALID_ARG, SPEC_ERR_UNSUPPORTED (vocab or d_model not a
- * multiple of 8 or 64, branches longer than 64 steps, draft dtype),
- * SPEC_ERR_WORKSPACE, SPEC_ERR_HIP.
+ * multiple of 8 or 64, hidden states of 2 GiB or more, branches longer than 64
+ * steps, draft dtype), SPEC_ERR_WORKSPACE, SPEC_ERR_HIP.
  */
 spec_status spec_e2etv_head_fwd_bwd(const spec_tree_layout *layout, int64_t vocab,
                                     int32_t d_model, spec_dtype draft_dtype, const void *d_draft,

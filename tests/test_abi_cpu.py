@@ -226,6 +226,9 @@ def test_e2etv_head_size_query_and_checks(tas):
     assert call(151932, 4096, 1) == 2             # vocab not a multiple of 8
     assert call(151936, 4000, 1) == 2             # d_model not a multiple of 64
     assert call(151936, 4096, 3) == 2             # unsupported draft dtype
+    assert L.n_rows * 135360 * 2 > 2 ** 31 - 1 > L.n_rows * 135296 * 2
+    assert call(151936, 135360, 1) == 2           # hidden states of 2 GiB or more
+    assert call(151936, 135296, 1) == 0
     assert call(151936, 4096, 1, float("inf")) == 1
     big = ctypes.c_size_t(1 << 40)
     # a workspace with a layout that has no device arrays is refused before any launch

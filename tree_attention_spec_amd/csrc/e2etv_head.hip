@@ -8,15 +8,16 @@
 //
 //   y[s, v] = <hidden[step_pred_row[s]], head[v]>   bf16 operands, float32 sums
 //
-// A workgroup (4 waves) owns a tile of 128 vocabulary entries x 128 steps and
-// runs the product over the hidden dimension in steps of 64 with
-// v_mfma_f32_32x32x16_bf16: vocabulary on the MFMA rows, steps on the
-// columns, so a lane's accumulators hold 32 vocabulary entries of two steps
+// A workgroup (4 waves, one per SIMD) owns a tile of 256 vocabulary entries x
+// 256 steps and runs the product over the hidden dimension in stages of 64
+// with v_mfma_f32_32x32x16_bf16: vocabulary on the MFMA rows, steps on the
+// columns, so a lane's accumulators hold 64 vocabulary entries of four steps
 // and every per-step reduction is in-lane plus one exchange with lane l ^ 32.
-// Wave w covers vocabulary half w & 1 and step half w >> 1 of the tile; both
-// operand tiles are double-buffered in LDS and the next step's tiles are
-// fetched into registers during the current step's products.
-//
+// Wave w covers vocabulary half w & 1 and step half w >> 1 of the tile (128 x
+// 128, accumulators in the matrix-core registers): each operand fragment read
+// from LDS feeds four MFMAs. Both operand stages are double-buffered in LDS and
+// filled by direct-to-LDS loads one stage ahead, in an XOR-swizzled layout that
+// the fragment reads take without bank conflicts.
 // The product runs twice, because alpha needs the teacher's normaliser before
 // any min(q, p) can be summed:
 //   pass 1   per (step, 64-entry vocabulary slice): the maximum and the sum of
@@ -36,20 +37,17 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int HT = 128;     // vocabulary entries, and steps, per workgroup tile
-constexpr int HK = 64;      // hidden dimensions per product step
-constexpr int HP = HK + 8;  // LDS row pitch in bf16 (144 B): a wave's 16-byte reads hit distinct banks
-constexpr int HS = 64;      // vocabulary entries per partial slice (one wave's width)
-constexpr int HGROUP = 8;   // tiles are walked in groups of 8 vocabulary x 8 step tiles
+constexpr int HT = 256;     // vocabulary entries, and steps, per workgroup tile
+constexpr int HK = 64;      // hidden dimensions per product stage
+constexpr int HS = 64;      // vocabulary entries per partial slice
+constexpr int HGROUP = 8;   // the walk takes tiles in groups of 8 vocabulary tiles x every step tile
+constexpr int HSTAGE = HT * HK;  // elements of one operand stage (32 KB)
 constexpr float kL2e = 1.4426950408889634f;
-constexpr int kWaitLgkm0 = 0xC07F;  // s_waitcnt lgkmcnt(0), other counters at their maxima
+constexpr int kHeadWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters at their maxima
 
-// Workgroup barrier for LDS traffic only: global loads in flight stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+// raw buffer descriptor over `bytes` bytes from `base` (reads past the end return zero)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 __device__ __forceinline__ float no_nan(float z) { return __builtin_isnan(z) ? -INFINITY : z; }
@@ -62,9 +60,14 @@ __device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2
   m = mm;
 }
 
+// One operand stage: 256 rows x 64 hidden dims. The 16-byte chunk c of row r
+// sits in slot 8 r + (c ^ swz(r)): 16 consecutive rows read at one chunk fall in
+// 16 distinct bank groups (and any aligned 8 of them in 8).
+__device__ __forceinline__ int head_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
 struct HeadLds {
-  __bf16 a[2][HT][HP];  // head rows (vocabulary entries)
-  __bf16 b[2][HT][HP];  // hidden rows (the steps' predecessor rows)
+  __bf16 a[2][HSTAGE];  // head rows (vocabulary entries)
+  __bf16 b[2][HSTAGE];  // hidden rows (the steps' predecessor rows)
 };
 
 struct HeadArgs {
@@ -72,7 +75,7 @@ struct HeadArgs {
   const int32_t *pred_row;
   const __bf16 *head;
   const void *draft;
-  int64_t R, V;
+  int64_t R, V, n_rows;
   int32_t d, n_vt, n_rt, n_tiles, per_xcd, n_slices;
   float4 *lse_part;  // pass 1 out: [R][n_slices] (max z', sum z', max y', sum y'), log2 units
   const float *lse_q2, *lse_p2;
@@ -103,11 +106,11 @@ template <> struct Draft4<float> {
 
 template <typename T, bool PASS2>
 __device__ __forceinline__ void head_tile(const HeadArgs &a) {
-  __shared__ HeadLds sm;
+  __shared__ __attribute__((aligned(16))) HeadLds sm;
   // Workgroups 8 apart run on one XCD; each XCD walks a contiguous run of the
-  // tile order, in which 64 consecutive tiles form a group of 8 vocabulary x 8
-  // step tiles, so the workgroups resident on an XCD share both operands'
-  // current slices in its L2.
+  // tile order, in which groups of 8 vocabulary tiles take every step tile
+  // (vocabulary fastest), so the 32 workgroups resident on an XCD share 8 head
+  // tiles and 4 hidden tiles in its L2 (groups of 2 and 4 were slower).
   const int t = (blockIdx.x % 8) * a.per_xcd + blockIdx.x / 8;
   if (t >= a.n_tiles) return;
   const int per_group = HGROUP * a.n_rt;
@@ -117,162 +120,183 @@ __device__ __forceinline__ void head_tile(const HeadArgs &a) {
   const int rt = (t % per_group) / gsize;
   const int64_t v0 = (int64_t)vt * HT, r0 = (int64_t)rt * HT;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS copy bases go to M0
   const int n = lane & 31, half = lane >> 5;
   const int wv = w & 1, wr = w >> 1;
 
-  // copies: thread tid moves 16 bytes at column 8 (tid % 8) of tile rows tid / 8 + 32 j;
-  // rows past the end of the vocabulary or the steps repeat the last one (never stored)
-  const int cc = (tid & 7) * 8;
-  const __bf16 *ga[4], *gb[4];
+  // Copies: wave w issues copies q = w + 4 i (i < 8) of each operand stage;
+  // copy q fills slots 64 q .. 64 q + 63, i.e. rows 8 q + lane / 8, and lane
+  // takes the chunk its slot holds. Rows past the vocabulary or the steps
+  // repeat the last one (never stored). The copies are buffer loads to LDS (the
+  // head tile's rows and the hidden rows are one buffer each, the stage a
+  // scalar offset): outstanding, they leave the LDS counter to the fragment
+  // reads, so a wait for one k-step's fragments does not wait for the next's.
+  const int cpy_c = (lane & 7) ^ (lane >> 3) ^ (w & 1);
+  const int64_t v_rows = min<int64_t>(a.V - v0, HT);
+  // the head tile's descriptor, in scalar registers (the compiler cannot see
+  // that v0 is the same in every lane)
+  const uint64_t abase = (uint64_t)(a.head + v0 * a.d);
+  const uint32_t alo = __builtin_amdgcn_readfirstlane((uint32_t)abase);
+  const uint32_t ahi = __builtin_amdgcn_readfirstlane((uint32_t)(abase >> 32));
+  const uint32_t abytes = __builtin_amdgcn_readfirstlane((uint32_t)(v_rows * a.d * 2));
+  const __amdgpu_buffer_rsrc_t rsa =
+      head_rsrc(reinterpret_cast<const void *>(((uint64_t)ahi << 32) | alo), abytes);
+  const __amdgpu_buffer_rsrc_t rsb = head_rsrc(a.hidden, (uint32_t)(a.n_rows * a.d * 2));
+  uint32_t oa[8], ob[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t v = min<int64_t>(v0 + tid / 8 + 32 * j, a.V - 1);
-    const int64_t r = min<int64_t>(r0 + tid / 8 + 32 * j, a.R - 1);
-    ga[j] = a.head + v * a.d + cc;
-    gb[j] = a.hidden + (int64_t)a.pred_row[r] * a.d + cc;
+  for (int i = 0; i < 8; ++i) {
+    const int row = 32 * i + 8 * w + (lane >> 3);
+    const int64_t vr = min<int64_t>(row, v_rows - 1);
+    const int64_t r = min<int64_t>(r0 + row, a.R - 1);
+    oa[i] = (uint32_t)((vr * a.d + 8 * cpy_c) * 2);
+    ob[i] = (uint32_t)(((int64_t)a.pred_row[r] * a.d + 8 * cpy_c) * 2);
   }
-  u32x4 ra[4], rb[4];
-#define SPEC_HEAD_FETCH1(j, kt)                                                 \
-  ra[j] = *reinterpret_cast<const u32x4 *>(ga[j] + (int64_t)(kt) * HK);         \
-  rb[j] = *reinterpret_cast<const u32x4 *>(gb[j] + (int64_t)(kt) * HK);
-#define SPEC_HEAD_FETCH(kt) \
-  { SPEC_HEAD_FETCH1(0, kt) SPEC_HEAD_FETCH1(1, kt) SPEC_HEAD_FETCH1(2, kt) SPEC_HEAD_FETCH1(3, kt) }
-#define SPEC_HEAD_STASH1(j, buf)                                                \
-  *reinterpret_cast<u32x4 *>(&sm.a[buf][tid / 8 + 32 * (j)][cc]) = ra[j];       \
-  *reinterpret_cast<u32x4 *>(&sm.b[buf][tid / 8 + 32 * (j)][cc]) = rb[j];
-#define SPEC_HEAD_STASH(buf) \
-  { SPEC_HEAD_STASH1(0, buf) SPEC_HEAD_STASH1(1, buf) SPEC_HEAD_STASH1(2, buf) SPEC_HEAD_STASH1(3, buf) }
-
-  // this lane's steps: r0 + 64 wr + 32 tr + n; its vocabulary entries of tile tv:
-  // vb(tv) + 8 g + 4 half + i (g, i < 4), vb(tv) = v0 + 64 wv + 32 tv
-  const T *draft = static_cast<const T *>(a.draft);
-  Draft4<T> dz[2][2][4];  // [tv][tr][g]
-
-  f32x16 acc[2][2];
+  auto copy_stage = [&](int kt, int buf) {
+    const uint32_t so = (uint32_t)kt * HK * 2;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 8; ++i) {
+      const int q = w + 4 * i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, &sm.a[buf][q * 512], 16, oa[i], so, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, &sm.b[buf][q * 512], 16, ob[i], so, 0, 0);
+    }
+  };
+
+  f32x16 acc[4][4];  // [vocabulary block i][step block j]
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+  // fragment rows 128 wv + 32 i + n (head) and 128 wr + 32 j + n (hidden): the
+  // swizzle depends on n only
+  const int swz = head_swz(n);
   const int nk = a.d / HK;
-  SPEC_HEAD_FETCH(0)
-  SPEC_HEAD_STASH(0)
+  copy_stage(0, 0);
+  __builtin_amdgcn_s_waitcnt(kHeadWaitVm0);
   __syncthreads();
 #pragma unroll 1
   for (int kt = 0; kt < nk; ++kt) {
     const int cb = kt & 1;
-    if (kt + 1 < nk) SPEC_HEAD_FETCH(kt + 1)
+    if (kt + 1 < nk) copy_stage(kt + 1, cb ^ 1);
+    __builtin_amdgcn_sched_barrier(0);  // the copies go out before this stage's products
+    // fragments of k-step ks + 1 are read before k-step ks's 16 MFMAs are
+    // issued (scheduling barriers keep the compiler from sinking the reads to
+    // their use): with one wave per SIMD nothing else covers the LDS latency
+    bf16x8 fa[2][4], fb[2][4];
+    auto read_frags = [&](int ks, bf16x8 (&xa)[4], bf16x8 (&xb)[4]) {
+      const int slot = (2 * ks + half) ^ swz;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xa[i] = *reinterpret_cast<const bf16x8 *>(&sm.a[cb][((128 * wv + 32 * i + n) * 8 + slot) * 8]);
+        xb[i] = *reinterpret_cast<const bf16x8 *>(&sm.b[cb][((128 * wr + 32 * i + n) * 8 + slot) * 8]);
+      }
+    };
+    read_frags(0, fa[0], fb[0]);
 #pragma unroll
     for (int ks = 0; ks < HK / 16; ++ks) {
-      const int kc = 16 * ks + 8 * half;
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(&sm.a[cb][64 * wv + n][kc]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(&sm.a[cb][64 * wv + 32 + n][kc]);
-      const bf16x8 b0 = *reinterpret_cast<const bf16x8 *>(&sm.b[cb][64 * wr + n][kc]);
-      const bf16x8 b1 = *reinterpret_cast<const bf16x8 *>(&sm.b[cb][64 * wr + 32 + n][kc]);
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
+      if (ks + 1 < HK / 16) read_frags(ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);  // the reads go out before this k-step's products
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < nk) SPEC_HEAD_STASH(cb ^ 1)
-    lds_barrier();
-  }
-#undef SPEC_HEAD_FETCH
-#undef SPEC_HEAD_FETCH1
-#undef SPEC_HEAD_STASH
-#undef SPEC_HEAD_STASH1
-
-  // the draft logits this lane pairs with its accumulators (issued after the
-  // products: the other resident workgroup keeps the MFMA pipe busy meanwhile)
-#pragma unroll
-  for (int tr = 0; tr < 2; ++tr) {
-    const int64_t r = min<int64_t>(r0 + 64 * wr + 32 * tr + n, a.R - 1);
-#pragma unroll
-    for (int tv = 0; tv < 2; ++tv)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t v = v0 + 64 * wv + 32 * tv + 8 * g + 4 * half;
-        if (v < a.V)
-          dz[tv][tr][g].load(draft + r * a.V + v);
-        else
-          dz[tv][tr][g].clear();
-      }
+    __builtin_amdgcn_s_waitcnt(kHeadWaitVm0);  // this wave's copies of the next stage landed
+    __syncthreads();
   }
 
-  // accumulator e of tile (tv, tr) is the teacher logit of vocabulary entry
-  // vb(tv) + 8 (e / 4) + 4 half + e % 4 for this lane's step of half tr
-  const int slice = 2 * vt + wv;
-  const bool slice_live = (int64_t)slice * HS < a.V;
+  // Epilogue. Accumulator e of block (i, j) is the teacher logit of vocabulary
+  // entry v0 + 128 wv + 32 i + 8 (e / 4) + 4 half + e % 4 for step
+  // r0 + 128 wr + 32 j + n; slice s of the wave's 128 entries is blocks 2s, 2s+1.
+  const T *draft = static_cast<const T *>(a.draft);
 #pragma unroll
-  for (int tr = 0; tr < 2; ++tr) {
-    const int64_t row = r0 + 64 * wr + 32 * tr + n;
-    const bool store = half == 0 && row < a.R && slice_live;
-    if (!PASS2) {
-      float my = -INFINITY, mz = -INFINITY;
+  for (int j = 0; j < 4; ++j) {
+    const int64_t row = r0 + 128 * wr + 32 * j + n;
+    const int64_t rc = row < a.R ? row : a.R - 1;
 #pragma unroll
-      for (int tv = 0; tv < 2; ++tv)
+    for (int sl = 0; sl < 2; ++sl) {
+      const int slice = (int)(v0 / HS) + 2 * wv + sl;
+      const bool slice_live = (int64_t)slice * HS < a.V;
+      const bool store = half == 0 && row < a.R && slice_live;
+      Draft4<T> dz[2][4];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const bool live = v0 + 64 * wv + 32 * tv + 8 * (e / 4) + 4 * half < a.V;
-          const float zz = no_nan(dz[tv][tr][e / 4][e % 4]) * kL2e;
-          my = fmaxf(my, live ? acc[tv][tr][e] * kL2e : -INFINITY);
-          mz = fmaxf(mz, zz);
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t v = v0 + 128 * wv + 32 * (2 * sl + ii) + 8 * g + 4 * half;
+          if (v < a.V)
+            dz[ii][g].load(draft + rc * a.V + v);
+          else
+            dz[ii][g].clear();
         }
-      my = fmaxf(my, __shfl_xor(my, 32));
-      mz = fmaxf(mz, __shfl_xor(mz, 32));
-      const float my0 = my == -INFINITY ? 0.f : my, mz0 = mz == -INFINITY ? 0.f : mz;
-      float sy = 0.f, sz = 0.f;
+      if (!PASS2) {
+        float my = -INFINITY, mz = -INFINITY;
 #pragma unroll
-      for (int tv = 0; tv < 2; ++tv)
+        for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const bool live = v0 + 64 * wv + 32 * tv + 8 * (e / 4) + 4 * half < a.V;
-          if (live) sy += __builtin_amdgcn_exp2f(fmaf(acc[tv][tr][e], kL2e, -my0));
-          sz += __builtin_amdgcn_exp2f(fmaf(no_nan(dz[tv][tr][e / 4][e % 4]), kL2e, -mz0));
-        }
-      sy += __shfl_xor(sy, 32);
-      sz += __shfl_xor(sz, 32);
-      if (store) a.lse_part[row * a.n_slices + slice] = make_float4(mz, sz, my, sy);
-    } else {
-      const int64_t rc = row < a.R ? row : a.R - 1;
-      const float lz = a.lse_q2[rc], ly = a.lse_p2[rc];
-      float al = 0.f, ss = 0.f;
+          for (int e = 0; e < 16; ++e) {
+            const bool live = v0 + 128 * wv + 32 * (2 * sl + ii) + 8 * (e / 4) + 4 * half < a.V;
+            const float zz = no_nan(dz[ii][e / 4][e % 4]) * kL2e;
+            my = fmaxf(my, live ? acc[2 * sl + ii][j][e] * kL2e : -INFINITY);
+            mz = fmaxf(mz, zz);
+          }
+        my = fmaxf(my, __shfl_xor(my, 32));
+        mz = fmaxf(mz, __shfl_xor(mz, 32));
+        const float my0 = my == -INFINITY ? 0.f : my, mz0 = mz == -INFINITY ? 0.f : mz;
+        float sy = 0.f, sz = 0.f;
 #pragma unroll
-      for (int tv = 0; tv < 2; ++tv) {
-        const int64_t vb = v0 + 64 * wv + 32 * tv;
-        uint32_t word = 0u;
+        for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const bool live = vb + 8 * (e / 4) + 4 * half < a.V;
-          const float zq = fmaf(no_nan(dz[tv][tr][e / 4][e % 4]), kL2e, -lz);  // log2 q
-          const float yp = fmaf(acc[tv][tr][e], kL2e, -ly);                    // log2 p
-          if (live) {
-            al += __builtin_amdgcn_exp2f(fminf(zq, yp));
-            if (zq < yp) {
-              ss += __builtin_amdgcn_exp2f(zq);
-              word |= 1u << (8 * (e / 4) + 4 * half + e % 4);
+          for (int e = 0; e < 16; ++e) {
+            const bool live = v0 + 128 * wv + 32 * (2 * sl + ii) + 8 * (e / 4) + 4 * half < a.V;
+            if (live) sy += __builtin_amdgcn_exp2f(fmaf(acc[2 * sl + ii][j][e], kL2e, -my0));
+            sz += __builtin_amdgcn_exp2f(fmaf(no_nan(dz[ii][e / 4][e % 4]), kL2e, -mz0));
+          }
+        sy += __shfl_xor(sy, 32);
+        sz += __shfl_xor(sz, 32);
+        if (store) a.lse_part[row * a.n_slices + slice] = make_float4(mz, sz, my, sy);
+      } else {
+        const float lz = a.lse_q2[rc], ly = a.lse_p2[rc];
+        float al = 0.f, ss = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          const int64_t vb = v0 + 128 * wv + 32 * (2 * sl + ii);
+          uint32_t word = 0u;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const bool live = vb + 8 * (e / 4) + 4 * half + e % 4 < a.V;
+            const float zq = fmaf(no_nan(dz[ii][e / 4][e % 4]), kL2e, -lz);  // log2 q
+            const float yp = fmaf(acc[2 * sl + ii][j][e], kL2e, -ly);         // log2 p
+            if (live) {
+              al += __builtin_amdgcn_exp2f(fminf(zq, yp));
+              if (zq < yp) {
+                ss += __builtin_amdgcn_exp2f(zq);
+                word |= 1u << (8 * (e / 4) + 4 * half + e % 4);
+              }
             }
           }
+          word |= __shfl_xor(word, 32);
+          if (store && vb < a.V) a.bits[row * a.bits_words + vb / 32] = word;
         }
-        word |= __shfl_xor(word, 32);
-        if (store && vb < a.V) a.bits[row * a.bits_words + vb / 32] = word;
+        al += __shfl_xor(al, 32);
+        ss += __shfl_xor(ss, 32);
+        if (store) a.tv_part[row * a.n_slices + slice] = make_float2(al, ss);
       }
-      al += __shfl_xor(al, 32);
-      ss += __shfl_xor(ss, 32);
-      if (store) a.tv_part[row * a.n_slices + slice] = make_float2(al, ss);
     }
   }
 }
 
 template <typename T>
-__global__ __launch_bounds__(256, 2) void e2etv_head_lse_kernel(HeadArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void e2etv_head_lse_kernel(HeadArgs a) {
   head_tile<T, false>(a);
 }
 template <typename T>
-__global__ __launch_bounds__(256, 2) void e2etv_head_tv_kernel(HeadArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void e2etv_head_tv_kernel(HeadArgs a) {
   head_tile<T, true>(a);
 }
 
@@ -377,6 +401,7 @@ hipError_t run_head(const spec_tree_layout &L, int64_t V, int32_t d, const void 
   a.head = static_cast<const __bf16 *>(head);
   a.draft = draft;
   a.R = R;
+  a.n_rows = L.n_rows;
   a.V = V;
   a.d = d;
   a.n_vt = (int32_t)((V + HT - 1) / HT);
