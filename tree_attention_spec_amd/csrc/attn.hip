@@ -386,7 +386,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
   const int hs = rest % hsub;
   const AttnItem it = items[rest / hsub];
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS copy bases go to M0
   const int n = lane & 31, half = lane >> 5;
   const int hl = hs * NW + w;
   const bool active = hl < group;  // wave-uniform
@@ -401,20 +402,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
   auto tile_index = [&](int t) { return t < n_trunk ? tt0 + t : bt0 + (t - n_trunk); };
 
   // copy tile t into `dst`: wave w issues copies w, w + NW, ... of the tile's
-  // 1 KB pieces (K pieces first, then V^T)
-  const __bf16 *kbase = kt + (int64_t)g * n_key_tiles * KT * D;
-  const __bf16 *vbase = vt + (int64_t)g * n_key_tiles * KT * D;
+  // 1 KB pieces (K pieces first, then V^T), as buffer loads to LDS (the KV
+  // head's tiles are one buffer, the piece's byte offset a scalar): outstanding,
+  // they leave the LDS counter to the fragment reads, which can then be issued
+  // ahead and waited for one at a time
+  const uint32_t head_bytes = (uint32_t)n_key_tiles * KT * D * 2;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kt + (int64_t)g * n_key_tiles * KT * D, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vt + (int64_t)g * n_key_tiles * KT * D, head_bytes);
+  const uint32_t lane_off = (uint32_t)lane * 16;
   auto copy_tile = [&](int t, TiledSmem &dst) {
-    const int64_t off = (int64_t)tile_index(t) * KT * D;
+    const uint32_t off = (uint32_t)tile_index(t) * (KT * D * 2);
     static_assert(CHUNKS % NW == 0, "each wave issues the same number of copies");
 #pragma unroll
     for (int i = 0; i < CHUNKS / NW; ++i) {
       const int j = w + NW * i;
       const bool isk = j < CHUNKS / 2;
       const int jj = isk ? j : j - CHUNKS / 2;
-      const __bf16 *src = (isk ? kbase : vbase) + off + jj * 512 + lane * 8;
       __bf16 *lds = (isk ? dst.k : dst.vt) + jj * 512;
-      __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isk ? rk : rv, lds, 16, lane_off, off + (uint32_t)jj * 1024, 0, 0);
     }
   };
 
@@ -478,13 +483,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
     const bool branch = t >= n_trunk;
     if (active) {
       f32x16 s0 = negm, s1 = negm;
+      // K fragments of step s + 1 are read before step s's MFMAs are issued
+      bf16x8 ka[2][2];
+      auto read_k = [&](int s, bf16x8 (&x)[2]) {
+        const int c = 2 * s + half;
+        x[0] = *reinterpret_cast<const bf16x8 *>(&cur.k[(n * 16 + (c ^ (n & 15))) * 8]);
+        x[1] = *reinterpret_cast<const bf16x8 *>(&cur.k[((32 + n) * 16 + (c ^ (n & 15))) * 8]);
+      };
+      read_k(0, ka[0]);
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const int c = 2 * s + half;
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(&cur.k[(n * 16 + (c ^ (n & 15))) * 8]);
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(&cur.k[((32 + n) * 16 + (c ^ (n & 15))) * 8]);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], s1, 0, 0, 0);
+        if (s + 1 < KS) read_k(s + 1, ka[(s + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s & 1][0], qf[s], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s & 1][1], qf[s], s1, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
       const bool need_mask = branch || k0 < it.tk0 || (k0 + KT > it.tfull);
       if (need_mask) {
@@ -542,14 +555,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
         pf[2 + (i >> 3)][i & 7] = (__bf16)p1;
       }
       l += ls0 + ls1;
+      // V^T fragments read one MFMA ahead of their use
+      auto read_v = [&](int x) {
+        const int kk = x / DT, dt = x % DT;
+        const int row = 32 * dt + n, c = 2 * kk + half;
+        return *reinterpret_cast<const bf16x8 *>(&cur.vt[(row * 8 + (c ^ vt_swizzle(row))) * 8]);
+      };
+      bf16x8 va[2];
+      va[0] = read_v(0);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int row = 32 * dt + n, c = 2 * kk + half;
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&cur.vt[(row * 8 + (c ^ vt_swizzle(row))) * 8]);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk], o[dt], 0, 0, 0);
-        }
+      for (int x = 0; x < 4 * DT; ++x) {
+        if (x + 1 < 4 * DT) va[(x + 1) & 1] = read_v(x + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        o[x % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[x & 1], pf[x / DT], o[x % DT], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of tile t + 1 landed
     __syncthreads();
