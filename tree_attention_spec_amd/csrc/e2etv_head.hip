@@ -8,16 +8,16 @@
 //
 //   y[s, v] = <hidden[step_pred_row[s]], head[v]>   bf16 operands, float32 sums
 //
-// A workgroup (4 waves, one per SIMD) owns a tile of 256 vocabulary entries x
-// 256 steps and runs the product over the hidden dimension in stages of 64
-// with v_mfma_f32_32x32x16_bf16: vocabulary on the MFMA rows, steps on the
-// columns, so a lane's accumulators hold 64 vocabulary entries of four steps
-// and every per-step reduction is in-lane plus one exchange with lane l ^ 32.
-// Wave w covers vocabulary half w & 1 and step half w >> 1 of the tile (128 x
-// 128, accumulators in the matrix-core registers): each operand fragment read
-// from LDS feeds four MFMAs. Both operand stages are double-buffered in LDS and
-// filled by direct-to-LDS loads one stage ahead, in an XOR-swizzled layout that
-// the fragment reads take without bank conflicts.
+// A workgroup (8 waves, two per SIMD, one workgroup per CU) owns a tile of 256
+// vocabulary entries x 256 steps and runs the product over the hidden dimension
+// in stages of 64 with v_mfma_f32_32x32x16_bf16: vocabulary on the MFMA rows,
+// steps on the columns, so a lane's accumulators hold 64 vocabulary entries of
+// two steps and every per-step reduction is in-lane plus one exchange with lane
+// l ^ 32. Wave w covers vocabulary half w & 1 and step quarter w >> 1 of the
+// tile (128 x 64): each fragment read from LDS feeds two or four MFMAs. Both
+// operand stages are double-buffered in LDS and filled by buffer loads to LDS
+// one stage ahead, in an XOR-swizzled layout that the fragment reads take
+// without bank conflicts.
 // The product runs twice, because alpha needs the teacher's normaliser before
 // any min(q, p) can be summed:
 //   pass 1   per (step, 64-entry vocabulary slice): the maximum and the sum of
@@ -110,7 +110,7 @@ __device__ __forceinline__ void head_tile(const HeadArgs &a) {
   // Workgroups 8 apart run on one XCD; each XCD walks a contiguous run of the
   // tile order, in which groups of 8 vocabulary tiles take every step tile
   // (vocabulary fastest), so the 32 workgroups resident on an XCD share 8 head
-  // tiles and 4 hidden tiles in its L2 (groups of 2 and 4 were slower).
+  // tiles and 4 hidden tiles in its L2.
   const int t = (blockIdx.x % 8) * a.per_xcd + blockIdx.x / 8;
   if (t >= a.n_tiles) return;
   const int per_group = HGROUP * a.n_rt;
@@ -123,9 +123,9 @@ __device__ __forceinline__ void head_tile(const HeadArgs &a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS copy bases go to M0
   const int n = lane & 31, half = lane >> 5;
-  const int wv = w & 1, wr = w >> 1;
+  const int wv = w & 1, wr = w >> 1;  // vocabulary half, step quarter
 
-  // Copies: wave w issues copies q = w + 4 i (i < 8) of each operand stage;
+  // Copies: wave w issues copies q = w + 8 i (i < 4) of each operand stage;
   // copy q fills slots 64 q .. 64 q + 63, i.e. rows 8 q + lane / 8, and lane
   // takes the chunk its slot holds. Rows past the vocabulary or the steps
   // repeat the last one (never stored). The copies are buffer loads to LDS (the
@@ -143,10 +143,10 @@ __device__ __forceinline__ void head_tile(const HeadArgs &a) {
   const __amdgpu_buffer_rsrc_t rsa =
       head_rsrc(reinterpret_cast<const void *>(((uint64_t)ahi << 32) | alo), abytes);
   const __amdgpu_buffer_rsrc_t rsb = head_rsrc(a.hidden, (uint32_t)(a.n_rows * a.d * 2));
-  uint32_t oa[8], ob[8];
+  uint32_t oa[4], ob[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = 32 * i + 8 * w + (lane >> 3);
+  for (int i = 0; i < 4; ++i) {
+    const int row = 64 * i + 8 * w + (lane >> 3);
     const int64_t vr = min<int64_t>(row, v_rows - 1);
     const int64_t r = min<int64_t>(r0 + row, a.R - 1);
     oa[i] = (uint32_t)((vr * a.d + 8 * cpy_c) * 2);
@@ -155,22 +155,22 @@ __device__ __forceinline__ void head_tile(const HeadArgs &a) {
   auto copy_stage = [&](int kt, int buf) {
     const uint32_t so = (uint32_t)kt * HK * 2;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = w + 4 * i;
+    for (int i = 0; i < 4; ++i) {
+      const int q = w + 8 * i;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, &sm.a[buf][q * 512], 16, oa[i], so, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, &sm.b[buf][q * 512], 16, ob[i], so, 0, 0);
     }
   };
 
-  f32x16 acc[4][4];  // [vocabulary block i][step block j]
+  f32x16 acc[4][2];  // [vocabulary block i][step block j]
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // fragment rows 128 wv + 32 i + n (head) and 128 wr + 32 j + n (hidden): the
+  // fragment rows 128 wv + 32 i + n (head) and 64 wr + 32 j + n (hidden): the
   // swizzle depends on n only
   const int swz = head_swz(n);
   const int nk = a.d / HK;
@@ -182,17 +182,18 @@ __device__ __forceinline__ void head_tile(const HeadArgs &a) {
     const int cb = kt & 1;
     if (kt + 1 < nk) copy_stage(kt + 1, cb ^ 1);
     __builtin_amdgcn_sched_barrier(0);  // the copies go out before this stage's products
-    // fragments of k-step ks + 1 are read before k-step ks's 16 MFMAs are
+    // fragments of k-step ks + 1 are read before k-step ks's 8 MFMAs are
     // issued (scheduling barriers keep the compiler from sinking the reads to
-    // their use): with one wave per SIMD nothing else covers the LDS latency
-    bf16x8 fa[2][4], fb[2][4];
-    auto read_frags = [&](int ks, bf16x8 (&xa)[4], bf16x8 (&xb)[4]) {
+    // their use), so their LDS latency overlaps the products
+    bf16x8 fa[2][4], fb[2][2];
+    auto read_frags = [&](int ks, bf16x8 (&xa)[4], bf16x8 (&xb)[2]) {
       const int slot = (2 * ks + half) ^ swz;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i)
         xa[i] = *reinterpret_cast<const bf16x8 *>(&sm.a[cb][((128 * wv + 32 * i + n) * 8 + slot) * 8]);
-        xb[i] = *reinterpret_cast<const bf16x8 *>(&sm.b[cb][((128 * wr + 32 * i + n) * 8 + slot) * 8]);
-      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        xb[j] = *reinterpret_cast<const bf16x8 *>(&sm.b[cb][((64 * wr + 32 * j + n) * 8 + slot) * 8]);
     };
     read_frags(0, fa[0], fb[0]);
 #pragma unroll
@@ -202,7 +203,7 @@ __device__ __forceinline__ void head_tile(const HeadArgs &a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -212,11 +213,11 @@ __device__ __forceinline__ void head_tile(const HeadArgs &a) {
 
   // Epilogue. Accumulator e of block (i, j) is the teacher logit of vocabulary
   // entry v0 + 128 wv + 32 i + 8 (e / 4) + 4 half + e % 4 for step
-  // r0 + 128 wr + 32 j + n; slice s of the wave's 128 entries is blocks 2s, 2s+1.
+  // r0 + 64 wr + 32 j + n; slice s of the wave's 128 entries is blocks 2s, 2s+1.
   const T *draft = static_cast<const T *>(a.draft);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t row = r0 + 128 * wr + 32 * j + n;
+  for (int j = 0; j < 2; ++j) {
+    const int64_t row = r0 + 64 * wr + 32 * j + n;
     const int64_t rc = row < a.R ? row : a.R - 1;
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl) {
@@ -292,11 +293,11 @@ __device__ __forceinline__ void head_tile(const HeadArgs &a) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void e2etv_head_lse_kernel(HeadArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void e2etv_head_lse_kernel(HeadArgs a) {
   head_tile<T, false>(a);
 }
 template <typename T>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void e2etv_head_tv_kernel(HeadArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void e2etv_head_tv_kernel(HeadArgs a) {
   head_tile<T, true>(a);
 }
 
@@ -419,7 +420,7 @@ hipError_t run_head(const spec_tree_layout &L, int64_t V, int32_t d, const void 
   a.bits_words = o.bits_row / 4;
   const dim3 grid((unsigned)(8 * (int64_t)a.per_xcd));
 
-  hipLaunchKernelGGL((e2etv_head_lse_kernel<T>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((e2etv_head_lse_kernel<T>), grid, dim3(512), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   prof_mark(s, "e2etv_head_lse");
@@ -428,7 +429,7 @@ hipError_t run_head(const spec_tree_layout &L, int64_t V, int32_t d, const void 
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   prof_mark(s, "e2etv_head_merge");
-  hipLaunchKernelGGL((e2etv_head_tv_kernel<T>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((e2etv_head_tv_kernel<T>), grid, dim3(512), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   prof_mark(s, "e2etv_head_tv");
