@@ -188,7 +188,9 @@ spec_status spec_tree_pack(int32_t n_trees, const int32_t *h_trunk_len,
  *   d_work        workspace of *work_bytes bytes, or NULL for a size query.
  * Data precondition (not checked): Q, K, V are finite.
  * Errors: SPEC_ERR_INVALID_ARG, SPEC_ERR_UNSUPPORTED (head_dim / dtype / GQA
- * ratio outside the kernels), SPEC_ERR_WORKSPACE, SPEC_ERR_HIP.
+ * ratio outside the kernels; bf16 K / V past 4 GiB: all heads for head dims 32
+ * and 64, one KV head's rows rounded up to 64 for head dim 128),
+ * SPEC_ERR_WORKSPACE, SPEC_ERR_HIP.
  */
 spec_status spec_tree_attn_fwd(const spec_tree_layout *layout, int32_t n_heads_q,
                                int32_t n_heads_kv, int32_t head_dim, spec_dtype dtype,

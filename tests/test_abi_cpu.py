@@ -135,6 +135,14 @@ def test_attention_size_query_and_checks(tas):
     assert call(32, 8, 128, 5, 10000.0) == 2      # unsupported dtype
     assert call(32, 8, 128, 1, -1.0) == 1         # bad RoPE base
     assert call(32, 8, 128, 0, 10000.0) == 0      # float32 path
+    # bf16 K / V tiles of one KV head must fit the 4 GiB a buffer descriptor spans
+    from tree_attention_spec_amd import _lib
+    big = _lib.spec_tree_layout.from_buffer_copy(L)
+    huge = lambda rows: (setattr(big, "n_rows", rows), lib.spec_tree_attn_fwd(
+        ctypes.byref(big), 1, 1, 128, 1, None, None, None, 10000.0, 0.0, None, None, None,
+        ctypes.byref(size), None))[1]
+    assert huge((1 << 24) - 64) == 0
+    assert huge(1 << 24) == 2
 
 
 def test_e2etv_size_query_and_checks(tas):

@@ -164,11 +164,15 @@ extern "C" spec_status spec_tree_attn_fwd(const spec_tree_layout *layout, int32_
   if ((int64_t)layout->n_rows * hq * D > (int64_t)INT32_MAX * 8)
     return fail(SPEC_ERR_UNSUPPORTED, "tensor too large");
   const AttnWork w = attn_work(*layout, hkv, D, dtype);
-  // the register-staged kernels address one KV head's K and V through buffer
-  // descriptors whose byte ranges and offsets are 32-bit
-  if (!w.tiled && dtype == SPEC_BF16 && (int64_t)layout->n_rows * hkv * D * 2 >= ((int64_t)1 << 32))
-    return fail(SPEC_ERR_UNSUPPORTED, "K / V of %lld rows x %d heads x %d dims past 4 GiB (head dim 128 has no "
-                "such limit)", (long long)layout->n_rows, hkv, D);
+  // the bf16 kernels address K and V through buffer descriptors whose byte
+  // ranges and offsets are 32-bit: all heads' rows for the register-staged
+  // kernels, one KV head's 64-key tiles for the tiled kernel
+  if (dtype == SPEC_BF16) {
+    const int64_t span = w.tiled ? (layout->n_rows + 63) / 64 * 64 * D * 2 : layout->n_rows * hkv * D * 2;
+    if (span >= ((int64_t)1 << 32))
+      return fail(SPEC_ERR_UNSUPPORTED, "K / V of %lld rows x %d heads x %d dims past the 4 GiB a buffer "
+                  "descriptor spans", (long long)layout->n_rows, hkv, D);
+  }
   if (!d_work) {
     *work_bytes = w.total;
     return SPEC_OK;
