@@ -357,8 +357,8 @@ spec_status spec_e2etv_fwd_bwd_noalloc(const spec_tree_layout *layout, int64_t v
  *   layout        from spec_tree_pack (uses n_steps, n_branches,
  *                 max_branch_len, step_off, step_pred_row).
  *   vocab         V >= 8, a multiple of 8.
- *   d_model       hidden size, a positive multiple of 64; the hidden states
- *                 (N x d_model bf16) must stay under 2 GiB.
+ *   d_model       hidden size, a positive multiple of 64, at most 2^22; the
+ *                 hidden states (N x d_model bf16) must stay under 2 GiB.
  *   draft_dtype   SPEC_BF16 or SPEC_F32: the dtype of d_draft.
  *   d_draft       [R, V] draft logits; NaN or -inf mean inactive support.
  *   d_hidden      [N, d_model] bf16 final hidden states of every packed row

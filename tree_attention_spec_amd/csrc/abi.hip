@@ -450,8 +450,10 @@ extern "C" spec_status spec_e2etv_head_fwd_bwd(const spec_tree_layout *layout, i
   if (vocab % 8 != 0 || d_model % 64 != 0)
     return fail(SPEC_ERR_UNSUPPORTED, "vocab (%lld) must be a multiple of 8 and d_model (%d) of 64",
                 (long long)vocab, (int)d_model);
-  if ((uint64_t)layout->n_rows * (uint64_t)d_model * 2u > (uint64_t)INT32_MAX)
-    return fail(SPEC_ERR_UNSUPPORTED, "hidden states of %lld rows x %d exceed 2 GiB",
+  // the head kernels address the hidden states, and each 256-row tile of the
+  // head, through buffer descriptors
+  if ((uint64_t)layout->n_rows * (uint64_t)d_model * 2u > (uint64_t)INT32_MAX || d_model > (1 << 22))
+    return fail(SPEC_ERR_UNSUPPORTED, "hidden states of %lld rows x %d exceed 2 GiB, or d_model past 2^22",
                 (long long)layout->n_rows, (int)d_model);
   if (layout->max_branch_len > 64)
     return fail(SPEC_ERR_UNSUPPORTED, "branches of %d steps (at most 64)", (int)layout->max_branch_len);
