@@ -65,9 +65,14 @@ typedef enum spec_status {
   SPEC_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
 } spec_status;
 
+/* Callers may pass any 32-bit value as a spec_dtype (the library refuses the
+ * ones it does not know): the two range markers make every int32 a value of the
+ * enumeration, so an unknown code is an error return and never undefined. */
 typedef enum spec_dtype {
   SPEC_F32 = 0,  /* IEEE binary32 */
-  SPEC_BF16 = 1  /* bfloat16 (upper half of a binary32) */
+  SPEC_BF16 = 1, /* bfloat16 (upper half of a binary32) */
+  SPEC_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  SPEC_DTYPE_RANGE_MAX_ = 2147483647
 } spec_dtype;
 
 typedef void *spec_stream; /* a hipStream_t */

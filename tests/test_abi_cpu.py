@@ -12,7 +12,7 @@ from specgen import CONFIGS, gen_structure
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "spec_tree.h")
-LIB = os.path.join(ROOT, "tree_attention_spec_amd", "libspec_tree.so")
+LIB = os.environ.get("SPEC_TREE_LIBRARY") or os.path.join(ROOT, "tree_attention_spec_amd", "libspec_tree.so")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB),
                                 reason="libspec_tree.so not built (run __graft_entry__.build())")

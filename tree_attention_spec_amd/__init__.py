@@ -11,6 +11,7 @@ every step of the path runs in the library's HIP kernels.
 from __future__ import annotations
 
 import ctypes
+import os
 
 import numpy as np
 import torch  # loads the HIP runtime the library binds to; keep before the library
@@ -29,10 +30,12 @@ _LIB = None
 
 
 def library() -> ctypes.CDLL:
-    """The loaded libspec_tree.so (raises ImportError if it is not built)."""
+    """The loaded libspec_tree.so (raises ImportError if it is not built). The
+    SPEC_TREE_LIBRARY environment variable names another build of the same library
+    (the CPU tests use it for the host-sanitized build)."""
     global _LIB
     if _LIB is None:
-        _LIB = _lib.load()
+        _LIB = _lib.load(os.environ.get("SPEC_TREE_LIBRARY") or _lib.LIB_PATH)
     return _LIB
 
 

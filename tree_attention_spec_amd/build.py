@@ -78,5 +78,45 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     return LIB
 
 
+# Host-side sanitizers for the CPU tests: AddressSanitizer and UBSan apply to the
+# host code only (argument checks, size queries, the pack plan); device code is
+# built as usual.
+HOST_SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+HOST_SAN_LIB = os.path.join(BUILD, "hostsan", "libspec_tree_hostsan.so")
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime that a host-sanitized library needs preloaded."""
+    import glob
+    cands = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not cands:
+        raise RuntimeError("clang AddressSanitizer runtime not found under /opt/rocm/lib/llvm")
+    return cands[-1]
+
+
+def build_host_sanitized() -> str:
+    """libspec_tree with host code under ASan + UBSan, in _build/hostsan/ (not the product)."""
+    cc = hipcc()
+    out_dir = os.path.dirname(HOST_SAN_LIB)
+    os.makedirs(out_dir, exist_ok=True)
+    flags = ["-O1", "-g"] + COMMON[1:] + DEVICE_FLAGS + HOST_SAN
+
+    def compile_one(src):
+        obj = os.path.join(out_dir, src.replace(".hip", ".o"))
+        _run([cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
+        return obj
+
+    with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    tmp = HOST_SAN_LIB + ".tmp"
+    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *HOST_SAN, *objs, "-o", tmp])
+    os.replace(tmp, HOST_SAN_LIB)
+    return HOST_SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--host-sanitized" in sys.argv:
+        print(build_host_sanitized())
+    else:
+        print(build(verbose="-v" in sys.argv))
