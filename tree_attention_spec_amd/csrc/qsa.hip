@@ -254,6 +254,15 @@ __global__ __launch_bounds__(64 * kQsaWaves) void qsa_attn_kernel(
   auto half = [&](int tl, int h, int lo, int hi) {
     const __bf16 *kp = kbase + (int64_t)tl * kKeyTile * D;
     const __bf16 *vp = vbase + (int64_t)tl * kKeyTile * D;
+    // the V^T fragments go out with the K fragments: both loads of a half are in
+    // flight together
+    bf16x8 vfr[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = 16 * dt + (lane & 15);
+      const int c = 4 * h + qd;
+      vfr[dt] = *reinterpret_cast<const bf16x8 *>(vp + (d * 8 + (c ^ vt_swizzle(d))) * 8);
+    }
     f32x4 s[2];
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
@@ -302,12 +311,7 @@ __global__ __launch_bounds__(64 * kQsaWaves) void qsa_attn_kernel(
     }
     // O^T[dims][heads] += V^T[dims][keys] P^T[keys][heads], k-slot 8 qd + i = key half_key(h, qd, i)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = 16 * dt + (lane & 15);
-      const int c = 4 * h + qd;
-      const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(vp + (d * 8 + (c ^ vt_swizzle(d))) * 8);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[dt], 0, 0, 0);
-    }
+    for (int dt = 0; dt < DT; ++dt) o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr[dt], pf, o[dt], 0, 0, 0);
   };
 
   // every 32-key half that meets packed rows [lo, hi)
