@@ -18,7 +18,8 @@
 // Three kernels after the RoPE table and the K / V^T tile pre-pass of the full
 // attention path (rope.hip):
 //   qsa_keys_kernel    the group keys: every complete trunk group of each tree
-//                      once, and for each branch the groups that hold its
+//                      once (stored dim-major, a tree's groups contiguous per
+//                      dim), and for each branch the groups that hold its
 //                      tokens (at most ceil((W_b - 1)/G)), one wave per key
 //   qsa_select_kernel  one wave per (row, KV head), a workgroup per KV head and
 //                      4 rows: scores of every complete
@@ -54,8 +55,8 @@ __global__ __launch_bounds__(64 * kQsaWaves) void qsa_keys_kernel(
     const __bf16 *__restrict__ ki, int32_t hkv, int32_t di, int32_t G, const int32_t *__restrict__ tree_off,
     const int32_t *__restrict__ tree_len, int32_t n_trees, int32_t max_tg, const int32_t *__restrict__ branch_tree,
     const int32_t *__restrict__ branch_anchor, const int32_t *__restrict__ branch_len,
-    const int32_t *__restrict__ branch_off, int32_t n_branches, int32_t max_bg, float *__restrict__ trunk_keys,
-    float *__restrict__ branch_keys) {
+    const int32_t *__restrict__ branch_off, int32_t n_branches, int32_t max_bg, int32_t tg_stride,
+    float *__restrict__ trunk_keys, float *__restrict__ branch_keys) {
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * kQsaWaves + (threadIdx.x >> 6);
   const int64_t n_trunk_items = (int64_t)n_trees * max_tg;
@@ -65,6 +66,7 @@ __global__ __launch_bounds__(64 * kQsaWaves) void qsa_keys_kernel(
   const int64_t slot = item / hkv;
   int base, anchor, boff, j;
   float *dst;
+  int64_t dstride;  // floats between consecutive dims of this key
   if (slot < n_trunk_items) {
     const int t = (int)(slot / max_tg);
     j = (int)(slot % max_tg);
@@ -72,7 +74,8 @@ __global__ __launch_bounds__(64 * kQsaWaves) void qsa_keys_kernel(
     base = tree_off[t];
     anchor = INT32_MAX;
     boff = 0;
-    dst = trunk_keys + (slot * hkv + g) * di;
+    dst = trunk_keys + ((int64_t)t * hkv + g) * di * tg_stride + j;  // dim-major, groups contiguous
+    dstride = tg_stride;
   } else {
     const int64_t bs = slot - n_trunk_items;
     const int b = (int)(bs / max_bg), s = (int)(bs % max_bg);
@@ -83,6 +86,7 @@ __global__ __launch_bounds__(64 * kQsaWaves) void qsa_keys_kernel(
     anchor = a;
     boff = branch_off[b];
     dst = branch_keys + (bs * hkv + g) * di;
+    dstride = 1;
   }
   for (int d = lane; d < di; d += 64) {
     float acc = 0.f;
@@ -91,7 +95,7 @@ __global__ __launch_bounds__(64 * kQsaWaves) void qsa_keys_kernel(
       const int row = p <= anchor ? base + p : boff + (p - anchor - 1);
       acc += bf(ki[((int64_t)row * hkv + g) * di + d]);
     }
-    dst[d] = acc / (float)G;
+    dst[d * dstride] = acc / (float)G;
   }
 }
 
@@ -112,7 +116,7 @@ __device__ inline int wave_min_i(int x) {
 __global__ __launch_bounds__(64 * kQsaWaves) void qsa_select_kernel(
     const __bf16 *__restrict__ qi, int32_t hkv, int32_t di, int32_t G, int32_t top_k, int64_t n_rows,
     const int32_t *__restrict__ row_tree, const int32_t *__restrict__ row_branch,
-    const int32_t *__restrict__ row_anchor, const int32_t *__restrict__ row_pos, int32_t max_tg, int32_t max_bg,
+    const int32_t *__restrict__ row_anchor, const int32_t *__restrict__ row_pos, int32_t tg_stride, int32_t max_bg,
     const float *__restrict__ trunk_keys, const float *__restrict__ branch_keys, int32_t *__restrict__ sel) {
   __shared__ float qs[kQsaWaves][256];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -136,16 +140,14 @@ __global__ __launch_bounds__(64 * kQsaWaves) void qsa_select_kernel(
     const int j = lane + 64 * s;
     sc[s] = -INFINITY;
     if (j < n_c) {
-      const float *key = j < jb ? trunk_keys + (((int64_t)tree * max_tg + j) * hkv + g) * di
-                                : branch_keys + (((int64_t)b * max_bg + (j - jb)) * hkv + g) * di;
+      // trunk keys are dim-major with the groups contiguous, so the lanes of a
+      // wave (consecutive groups) read one dim of 64 keys in one coalesced load
+      const bool trunk = j < jb;
+      const float *key = trunk ? trunk_keys + ((int64_t)tree * hkv + g) * di * tg_stride + j
+                               : branch_keys + (((int64_t)b * max_bg + (j - jb)) * hkv + g) * di;
+      const int64_t ks = trunk ? tg_stride : 1;
       float acc = 0.f;
-      for (int d = 0; d < di; d += 4) {
-        const float4 k4 = *reinterpret_cast<const float4 *>(key + d);
-        acc = fmaf(qs[wv][d], k4.x, acc);
-        acc = fmaf(qs[wv][d + 1], k4.y, acc);
-        acc = fmaf(qs[wv][d + 2], k4.z, acc);
-        acc = fmaf(qs[wv][d + 3], k4.w, acc);
-      }
+      for (int d = 0; d < di; ++d) acc = fmaf(qs[wv][d], key[d * ks], acc);
       sc[s] = acc;
     }
   }
@@ -384,10 +386,15 @@ __global__ __launch_bounds__(64 * kQsaWaves) void qsa_attn_kernel(
 
 }  // namespace
 
+// trunk keys [tree][Hkv][DI][groups padded to a multiple of 64], then branch keys
+// [branch][its groups][Hkv][DI]
+static int64_t trunk_group_stride(const spec_tree_layout &L, int32_t G) {
+  return (L.max_trunk_len / G + 63) / 64 * 64;
+}
+
 size_t qsa_keys_floats(const spec_tree_layout &L, int32_t hkv, int32_t di, int32_t G) {
-  const int64_t max_tg = L.max_trunk_len / G;
   const int64_t max_bg = L.max_branch_len > 1 ? (L.max_branch_len - 1 + G - 1) / G : 0;
-  return (size_t)((int64_t)L.n_trees * max_tg + (int64_t)L.n_branches * max_bg) * hkv * di;
+  return (size_t)((int64_t)L.n_trees * trunk_group_stride(L, G) + (int64_t)L.n_branches * max_bg) * hkv * di;
 }
 
 hipError_t launch_qsa(const spec_tree_layout &L, int32_t hq, int32_t hkv, int32_t di, int32_t G,
@@ -396,14 +403,15 @@ hipError_t launch_qsa(const spec_tree_layout &L, int32_t hq, int32_t hkv, int32_
                       void *out, hipStream_t s) {
   const int32_t max_tg = L.max_trunk_len / G;
   const int32_t max_bg = L.max_branch_len > 1 ? (L.max_branch_len - 1 + G - 1) / G : 0;
+  const int32_t tg_stride = (int32_t)trunk_group_stride(L, G);
   float *trunk_keys = keys;
-  float *branch_keys = keys + (int64_t)L.n_trees * max_tg * hkv * di;
+  float *branch_keys = keys + (int64_t)L.n_trees * tg_stride * hkv * di;
   const int64_t key_items = ((int64_t)L.n_trees * max_tg + (int64_t)L.n_branches * max_bg) * hkv;
   if (key_items > 0) {
     hipLaunchKernelGGL(qsa_keys_kernel, dim3((unsigned)((key_items + kQsaWaves - 1) / kQsaWaves)),
                        dim3(64 * kQsaWaves), 0, s, static_cast<const __bf16 *>(ki), hkv, di, G, L.tree_off,
                        L.tree_trunk_len, L.n_trees, max_tg, L.branch_tree, L.branch_anchor, L.branch_len,
-                       L.branch_off, L.n_branches, max_bg, trunk_keys, branch_keys);
+                       L.branch_off, L.n_branches, max_bg, tg_stride, trunk_keys, branch_keys);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -412,7 +420,7 @@ hipError_t launch_qsa(const spec_tree_layout &L, int32_t hq, int32_t hkv, int32_
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)blocks;
   hipLaunchKernelGGL(qsa_select_kernel, dim3(grid), dim3(64 * kQsaWaves), 0, s, static_cast<const __bf16 *>(qi),
-                     hkv, di, G, top_k, L.n_rows, L.row_tree, L.row_branch, L.row_anchor, L.row_pos, max_tg,
+                     hkv, di, G, top_k, L.n_rows, L.row_tree, L.row_branch, L.row_anchor, L.row_pos, tg_stride,
                      max_bg, trunk_keys, branch_keys, sel);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
