@@ -289,10 +289,17 @@ spec_status spec_qsa_attn_fwd(const spec_tree_layout *layout, int32_t n_heads_q,
  *   d_work        workspace of *work_bytes bytes, or NULL for a size query.
  * Data preconditions (not checked; violations give NaN): teacher finite, at
  * least one active draft entry per row.
- * For bf16 logits with V a multiple of 8 the work runs as one cooperative
- * kernel whose workgroups wait on each other through bounded polls; if a poll
- * ever times out (it cannot while the kernel is resident on the device as a
- * whole) alpha and the loss come back NaN and spec_e2etv_status reports it.
+ * For bf16 logits the work runs as one cooperative kernel (8 bytes of memory
+ * traffic per logit element) when V is a multiple of 8 and at most 245,760 (a
+ * team of at most 16 workgroups splits each row, 15,360 entries apiece), the
+ * longest branch is at most one step longer than the number of teams resident
+ * on the device (25 on MI355X for V = 151,936) and no team holds more than
+ * 2,048 rows. Otherwise,
+ * and for float32 logits, three kernels give the same results at about 10
+ * bytes per element. The cooperative kernel's workgroups wait on each other
+ * through bounded polls; if a poll ever times out (it cannot while the kernel
+ * is resident on the device as a whole) alpha and the loss come back NaN and
+ * spec_e2etv_status reports it.
  * Calls that share a workspace must not overlap in time.
  * Errors: SPEC_ERR_INVALID_ARG, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP.
  */
