@@ -52,6 +52,9 @@ SMALL = [
     # head dim 128 with GQA groups 1 and 3 (one and four waves per workgroup, a partial head slice)
     dict(tag="s_d128_g1", base="gqa8b", trunk=230, branches=12, width=9, hq=2, hkv=2, head_dim=128),
     dict(tag="s_d128_g3", base="gqa8b", n_trees=3, trunk=90, branches=5, width=11, hq=6, hkv=2, head_dim=128),
+    # GQA group 16 (two workgroups of eight waves per block) and 5 (a partial second slice)
+    dict(tag="s_d128_g16", base="stress", trunk=200, branches=9, width=16, hq=32, hkv=2, head_dim=128),
+    dict(tag="s_d128_g5", base="gqa8b", trunk=170, branches=7, width=12, hq=10, hkv=2, head_dim=128),
 ]
 
 

@@ -242,3 +242,24 @@ def test_e2etv_long_branches_multipass():
     assert case.lay["max_branch_len"] > 16
     z, y = case.logits()
     _full_compare(case, z, y)
+
+
+def test_e2etv_branch_lengths_at_path_limits():
+    """Branches of 1, 26, 27 and 64 steps (the ABI maximum) in one tree, V = 151,936 bf16:
+    the fused cooperative path takes a branch of at most one step more than its team
+    count (25 on MI355X at this vocabulary), the three-kernel path the rest; every row
+    matches the oracle either way."""
+    import numpy as np
+    say("e2etv parity: branch lengths 1, 26, 27, 64")
+    s = dict(trunk_len=np.array([300], np.int32), n_branches=np.array([4], np.int32),
+             anchors=np.array([20, 150, 151, 299], np.int32), branch_len=np.array([1, 26, 27, 64], np.int32))
+    case = Case(small_config("gqa8b", vocab=151936), structure=s)
+    assert case.lay["max_branch_len"] == 64
+    z, y = case.logits()
+    _full_compare(case, z, y)
+    for w in (26, 27):
+        s1 = dict(trunk_len=np.array([300], np.int32), n_branches=np.array([2], np.int32),
+                  anchors=np.array([40, 200], np.int32), branch_len=np.array([w, 3], np.int32))
+        c1 = Case(small_config("gqa8b", vocab=151936), structure=s1)
+        z1, y1 = c1.logits()
+        _full_compare(c1, z1, y1)
