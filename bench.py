@@ -693,7 +693,9 @@ def ceilings(args):
     """Achievable rates on this GPU for the two roofline bounds, from the probe library
     (tree_attention_spec_amd/libspec_probe.so): HBM streams of the shapes the E2E-TV
     kernel moves (read-only, write-only, and two bf16 reads to one float32 write per
-    element) with and without non-temporal loads and stores, and chains of bf16 MFMAs."""
+    element) with and without non-temporal loads and stores, chains of bf16 MFMAs, and
+    the same MFMAs fed from LDS at the tree attention's 1 KB of fragment reads per MFMA
+    (and at 1/2, 1/4 of that, and reads alone)."""
     import ctypes
     import torch
     path = os.path.join(ROOT, "tree_attention_spec_amd", "libspec_probe.so")
@@ -706,6 +708,7 @@ def ceilings(args):
     lib.spec_probe_mixed.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p, c.c_int64, c.c_int, c.c_int, c.c_int,
                                      c.c_int, c.c_void_p]
     lib.spec_probe_mfma.argtypes = [c.c_void_p, c.c_int, c.c_int, c.c_void_p]
+    lib.spec_probe_mfma_lds.argtypes = [c.c_void_p, c.c_int, c.c_int, c.c_int, c.c_void_p]
     dev = torch.device("cuda:0")
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     stream = torch.cuda.current_stream(dev)
@@ -749,18 +752,35 @@ def ceilings(args):
     assert torch.equal(out[idx], a[idx].float() - b[idx].float())
     del a, b, out
     iters = 2048
+    msink = torch.zeros(cus * 8, dtype=torch.float32, device=dev)  # one float per workgroup
     for waves_per_simd in (2, 4, 8):
         blocks = cus * waves_per_simd          # 4 waves per workgroup, one per SIMD
         flop = float(blocks) * 4 * 4 * iters * 32 * 32 * 16 * 2
-        ms = timed(lambda: lib.spec_probe_mfma(P(sink), blocks, iters, sp), reps=5)
+        ms = timed(lambda: lib.spec_probe_mfma(P(msink), blocks, iters, sp), reps=5)
         res["mfma"]["bf16 32x32x16, %d waves/SIMD" % waves_per_simd] = {"flop": flop, "ms": ms,
                                                                         "TFLOP/s": flop / ms / 1e9}
+    # MFMAs fed from LDS: a fresh 1 KB A fragment every `reuse` MFMAs (1: the tree
+    # attention's K and V^T fragments), or LDS reads alone (reuse 0)
+    res["lds"] = {}
+    iters = 4096
+    for waves_per_simd in (1, 2):
+        blocks = cus * waves_per_simd
+        for reuse in (0, 1, 2, 4):
+            lds_bytes = float(blocks) * 4 * 8 * iters * 1024
+            flop = float(blocks) * 4 * 8 * iters * reuse * 32 * 32 * 16 * 2
+            ms = timed(lambda: lib.spec_probe_mfma_lds(P(msink), blocks, iters, reuse, sp), reps=5)
+            key = ("LDS reads only" if reuse == 0 else "bf16 32x32x16, 1 KB LDS fragment per %d MFMA" % reuse)
+            res["lds"]["%s, %d waves/SIMD" % (key, waves_per_simd)] = {
+                "flop": flop, "lds_bytes": lds_bytes, "ms": ms, "TFLOP/s": flop / ms / 1e9,
+                "LDS GB/s": lds_bytes / ms / 1e6, "LDS B/clk/CU at 2.4 GHz": lds_bytes / (ms * 1e-3) / cus / 2.4e9}
     best = lambda d, key, pre: max((v[key], k) for k, v in d.items() if k.startswith(pre))
     res["summary"] = {
         "read_GBs": best(res["streams"], "GB/s", "read"),
         "write_GBs": best(res["streams"], "GB/s", "write"),
         "mixed_GBs": best(res["streams"], "GB/s", "mixed"),
         "mfma_bf16_TFLOPs": best(res["mfma"], "TFLOP/s", "bf16"),
+        "mfma_lds_1KB_per_mfma_TFLOPs": best(res["lds"], "TFLOP/s", "bf16 32x32x16, 1 KB LDS fragment per 1 "),
+        "lds_read_GBs": best(res["lds"], "LDS GB/s", "LDS reads only"),
         "datasheet": {"hbm_GBs": PEAK_HBM_GBS, "bf16_TFLOPs": PEAK_BF16_TFLOPS},
     }
     return res

@@ -9,6 +9,10 @@
 //                     element (4 bytes read : 4 bytes written, the mix of the
 //                     E2E-TV forward and backward over bf16 logits)
 //   spec_probe_mfma   chains of v_mfma_f32_32x32x16_bf16 on register operands
+//   spec_probe_mfma_lds the same MFMAs with a fresh 1 KB A fragment read from LDS
+//                     every `reuse` of them (reuse 1 is the tree attention's
+//                     dataflow: each K or V^T fragment feeds one MFMA); reuse 0
+//                     only reads, for the LDS read rate
 // Loads and stores can be marked non-temporal (the nt cache policy).
 #include <hip/hip_runtime.h>
 
@@ -131,6 +135,57 @@ __global__ __launch_bounds__(kThreads) void probe_mfma_kernel(float *__restrict_
   if (t == 1.2345f) out[blockIdx.x] = t;
 }
 
+// A 32 KB LDS buffer of 32 fragments (1 KB each, lane l holding bytes 16l..16l+15:
+// a conflict-free ds_read_b128); a wave reads 8 of them per iteration, the next
+// iteration's 8 issued before this one's are used.
+template <int REUSE>
+__global__ __launch_bounds__(kThreads) void probe_mfma_lds_kernel(float *__restrict__ out, int iters) {
+  constexpr int NF = 32;
+  __shared__ u32x4 buf[NF * 64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int i = tid; i < NF * 64; i += kThreads) {
+    const uint32_t v = 0x3f803f80u ^ ((uint32_t)i & 0x00070007u);  // bf16 values near 1
+    buf[i] = u32x4{v, v, v, v};
+  }
+  __syncthreads();
+  bf16x8 b;
+  const float sb = (float)(lane & 7) * 0.125f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) b[j] = (__bf16)(sb - j);
+  f32x16 c[4] = {};
+  u32x4 fa[8], fb[8];
+  auto rd = [&](int it, u32x4 (&f)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = buf[((it * 8 + j) & (NF - 1)) * 64 + lane];
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto use = [&](const u32x4 (&f)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if constexpr (REUSE == 0) {
+        asm volatile("" ::"v"(f[j]));
+      } else {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, f[j]);
+#pragma unroll
+        for (int r = 0; r < REUSE; ++r)
+          c[(j * REUSE + r) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[(j * REUSE + r) & 3], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  rd(0, fa);
+  for (int it = 0; it < iters; it += 2) {
+    rd(it + 1, fb);
+    use(fa);
+    rd(it + 2, fa);
+    use(fb);
+  }
+  float t = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) t += c[0][j] + c[1][j] + c[2][j] + c[3][j];
+  if (t == 1.2345f) out[blockIdx.x] = t;
+}
+
 int grid_for(int64_t n, int cap) {
   const int64_t g = (n + kThreads - 1) / kThreads;
   return (int)(g < cap ? (g < 1 ? 1 : g) : cap);
@@ -193,6 +248,22 @@ int spec_probe_mixed(const void *a, const void *b, void *out, int64_t n, int nt_
 int spec_probe_mfma(void *out, int blocks, int iters, void *stream) {
   hipLaunchKernelGGL(probe_mfma_kernel, dim3(blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
                      (float *)out, iters);
+  return (int)hipGetLastError();
+}
+
+// `blocks` workgroups of 4 waves; each wave reads 8 * iters 1 KB LDS fragments
+// (iters even) and runs `reuse` MFMAs of 32x32x16 on each (reuse 0, 1, 2 or 4).
+int spec_probe_mfma_lds(void *out, int blocks, int iters, int reuse, void *stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float *o = (float *)out;
+  if (iters < 2 || (iters & 1)) return (int)hipErrorInvalidValue;
+  switch (reuse) {
+    case 0: hipLaunchKernelGGL(probe_mfma_lds_kernel<0>, dim3(blocks), dim3(kThreads), 0, s, o, iters); break;
+    case 1: hipLaunchKernelGGL(probe_mfma_lds_kernel<1>, dim3(blocks), dim3(kThreads), 0, s, o, iters); break;
+    case 2: hipLaunchKernelGGL(probe_mfma_lds_kernel<2>, dim3(blocks), dim3(kThreads), 0, s, o, iters); break;
+    case 4: hipLaunchKernelGGL(probe_mfma_lds_kernel<4>, dim3(blocks), dim3(kThreads), 0, s, o, iters); break;
+    default: return (int)hipErrorInvalidValue;
+  }
   return (int)hipGetLastError();
 }
 
