@@ -25,7 +25,11 @@
 // query's two visible intervals. Rows of Q are rotated in registers on load.
 // Head dims 32 and 64 stage K and V through registers (tree_attn_bf16_kernel);
 // head dim 128 copies 64-key tiles that a pre-pass laid out in the fragments'
-// LDS order straight into LDS (tree_attn_tiled_kernel, below).
+// LDS order straight into LDS (tree_attn_tiled_kernel, below). The tiled kernel
+// forms the exponentials before any maximum, against the current reference, and
+// forms the tile maximum only when a partial sum shows a probability above
+// 2^8 (or the reference is still unset): the decisions, and so the outputs, are
+// those of the maximum-first order, with the maxima left out of the usual tile.
 //
 // fp32 path: one wavefront per (row, head) walks the visible keys in order with
 // an exact float32 online softmax (no MFMA); it serves float32 inputs.
@@ -358,16 +362,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
 // pre-pass exactly as the MFMA fragments read them), so staging takes no
 // registers and no VALU work. Key tiles are aligned to multiples of 64 in the
 // packed order; keys outside a query's visible ranges are masked as before.
-// The copy of tile t+1 is issued before tile t is computed, into the other of
-// two LDS buffers; one wait and one barrier per tile.
+// Tile t's work is S(t) = K(t) Q^T, then its exponentials with the previous
+// tile's O += V(t-1) P(t-1) issued between them (one MFMA, two exponentials,
+// ...), so the matrix core runs while the VALU works. K(t+1) and V(t) are
+// copied during tile t into the other K buffer and the V buffer that P V(t-2)
+// has finished with: two buffers of each, one wait and one barrier per tile.
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima), as an
 // immediate the compiler's own wait bookkeeping sees
 constexpr int kWaitVm0 = 0x0F70;
-
-struct alignas(16) TiledSmem {
-  __bf16 k[KT * 128];   // slot r*16 + (c ^ (r & 15)) holds dims 8c..8c+7 of key r
-  __bf16 vt[128 * KT];  // slot d*8 + (c ^ vt_swizzle(d)) holds positions 8c..8c+7 of dim d
-};
+constexpr float kLazyLimit = 256.f;  // 2^kLazyMax
+static_assert(kLazyMax == 8.f && kLazyLimit == 256.f, "kLazyLimit is 2^kLazyMax");
 
 template <int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4 ? 2 : 1, 2))) void tree_attn_tiled_kernel(
@@ -377,8 +381,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
     const int32_t *__restrict__ row_trunk_hi, const int32_t *__restrict__ row_branch_lo,
     int32_t n_key_tiles, int hq, float sl2) {
   constexpr int D = 128, KS = D / 16, DT = D / 32;
-  constexpr int CHUNKS = 2 * KT * D * 2 / 1024;  // 1 KB copies per tile (K and V)
-  __shared__ TiledSmem smA, smB;
+  constexpr int PIECES = KT * D * 2 / 1024;  // 1 KB copies per K (or V^T) tile
+  static_assert(PIECES % NW == 0, "each wave issues the same number of copies");
+  // K tiles: slot r*16 + (c ^ (r & 15)) holds dims 8c..8c+7 of key r; V^T tiles:
+  // slot d*8 + (c ^ vt_swizzle(d)) holds positions 8c..8c+7 of dim d. Four arrays,
+  // so the compiler can see that no fragment read touches a buffer being filled.
+  __shared__ __attribute__((aligned(16))) __bf16 kb0[KT * D], kb1[KT * D], vb0[D * KT], vb1[D * KT];
 
   const int bid = blockIdx.x;
   const int g = bid % hkv;
@@ -401,25 +409,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
   const int n_tiles = n_trunk + (bt1 - bt0);
   auto tile_index = [&](int t) { return t < n_trunk ? tt0 + t : bt0 + (t - n_trunk); };
 
-  // copy tile t into `dst`: wave w issues copies w, w + NW, ... of the tile's
-  // 1 KB pieces (K pieces first, then V^T), as buffer loads to LDS (the KV
-  // head's tiles are one buffer, the piece's byte offset a scalar): outstanding,
-  // they leave the LDS counter to the fragment reads, which can then be issued
-  // ahead and waited for one at a time
+  // copy the K (or V^T) half of tile t into `dst`: wave w issues the 1 KB pieces
+  // w, w + NW, ... as buffer loads to LDS (the KV head's tiles are one buffer, the
+  // piece's byte offset a scalar): outstanding, they leave the LDS counter to the
+  // fragment reads, which can then be issued ahead and waited for one at a time
   const uint32_t head_bytes = (uint32_t)n_key_tiles * KT * D * 2;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kt + (int64_t)g * n_key_tiles * KT * D, head_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vt + (int64_t)g * n_key_tiles * KT * D, head_bytes);
   const uint32_t lane_off = (uint32_t)lane * 16;
-  auto copy_tile = [&](int t, TiledSmem &dst) {
+  auto copy_k = [&](int t, __bf16 *dst) {
     const uint32_t off = (uint32_t)tile_index(t) * (KT * D * 2);
-    static_assert(CHUNKS % NW == 0, "each wave issues the same number of copies");
 #pragma unroll
-    for (int i = 0; i < CHUNKS / NW; ++i) {
+    for (int i = 0; i < PIECES / NW; ++i) {
       const int j = w + NW * i;
-      const bool isk = j < CHUNKS / 2;
-      const int jj = isk ? j : j - CHUNKS / 2;
-      __bf16 *lds = (isk ? dst.k : dst.vt) + jj * 512;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(isk ? rk : rv, lds, 16, lane_off, off + (uint32_t)jj * 1024, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst + j * 512, 16, lane_off, off + (uint32_t)j * 1024, 0, 0);
+    }
+  };
+  auto copy_v = [&](int t, __bf16 *dst) {
+    const uint32_t off = (uint32_t)tile_index(t) * (KT * D * 2);
+#pragma unroll
+    for (int i = 0; i < PIECES / NW; ++i) {
+      const int j = w + NW * i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst + j * 512, 16, lane_off, off + (uint32_t)j * 1024, 0, 0);
     }
   };
 
@@ -427,7 +438,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
   const int pos = row_pos[qrow];
   int thi = row_trunk_hi[qrow];
   int blo = row_branch_lo[qrow];
-  if (n_tiles > 0) copy_tile(0, smA);
+  if (n_tiles > 0) copy_k(0, kb0);
 
   bf16x8 qf[KS];
   {
@@ -472,12 +483,67 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
   f32x16 negm;
 #pragma unroll
   for (int i = 0; i < 16; ++i) negm[i] = 0.f;
+  bf16x8 pp[4];  // the previous tile's probabilities
 
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
 
-  auto body = [&](int t, const TiledSmem &cur, TiledSmem &next) {
-    if (t + 1 < n_tiles) copy_tile(t + 1, next);
+  auto read_v = [&](const __bf16 *vs, int x) {
+    const int kk = x / DT, dt = x % DT;
+    const int row = 32 * dt + n, c = 2 * kk + half;
+    return *reinterpret_cast<const bf16x8 *>(&vs[(row * 8 + (c ^ vt_swizzle(row))) * 8]);
+  };
+  // O^T += V^T P^T over one tile, V^T fragments read one MFMA ahead
+  auto pv = [&](const __bf16 *vs, const bf16x8 (&p)[4]) {
+    bf16x8 va[2];
+    va[0] = read_v(vs, 0);
+#pragma unroll
+    for (int x = 0; x < 4 * DT; ++x) {
+      if (x + 1 < 4 * DT) va[(x + 1) & 1] = read_v(vs, x + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      o[x % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[x & 1], p[x / DT], o[x % DT], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // probability of score i (0..31: s0 then s1) into pf, added to its half's sum;
+  // the sums run over i in order
+  auto prob = [&](const f32x16 &s0, const f32x16 &s1, int i, bf16x8 (&pf)[4], float &ls0, float &ls1) {
+    const float p = __builtin_amdgcn_exp2f(i < 16 ? s0[i & 15] : s1[i & 15]);
+    if (i < 16)
+      ls0 += p;
+    else
+      ls1 += p;
+    pf[i >> 3][i & 7] = (__bf16)p;
+  };
+  auto exps = [&](const f32x16 &s0, const f32x16 &s1, bf16x8 (&pf)[4], float &ls0, float &ls1) {
+    ls0 = 0.f;
+    ls1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) prob(s0, s1, i, pf, ls0, ls1);
+  };
+  // the same exponentials with the previous tile's product between them: one
+  // MFMA (its V^T fragment read one ahead), then two exponentials
+  auto exps_pv = [&](const __bf16 *vs, const f32x16 &s0, const f32x16 &s1, bf16x8 (&pf)[4], float &ls0,
+                     float &ls1) {
+    ls0 = 0.f;
+    ls1 = 0.f;
+    bf16x8 va[2];
+    va[0] = read_v(vs, 0);
+#pragma unroll
+    for (int x = 0; x < 4 * DT; ++x) {
+      if (x + 1 < 4 * DT) va[(x + 1) & 1] = read_v(vs, x + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      o[x % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[x & 1], pp[x / DT], o[x % DT], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      prob(s0, s1, 2 * x, pf, ls0, ls1);
+      prob(s0, s1, 2 * x + 1, pf, ls0, ls1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  auto body = [&](int t, const __bf16 *kcur, __bf16 *knext, const __bf16 *vprev, __bf16 *vnext, bool first) {
+    if (t + 1 < n_tiles) copy_k(t + 1, knext);
+    copy_v(t, vnext);
     __builtin_amdgcn_sched_barrier(0);  // the copies go out before this tile's work
     const int k0 = tile_index(t) * KT;
     const bool branch = t >= n_trunk;
@@ -487,8 +553,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
       bf16x8 ka[2][2];
       auto read_k = [&](int s, bf16x8 (&x)[2]) {
         const int c = 2 * s + half;
-        x[0] = *reinterpret_cast<const bf16x8 *>(&cur.k[(n * 16 + (c ^ (n & 15))) * 8]);
-        x[1] = *reinterpret_cast<const bf16x8 *>(&cur.k[((32 + n) * 16 + (c ^ (n & 15))) * 8]);
+        x[0] = *reinterpret_cast<const bf16x8 *>(&kcur[(n * 16 + (c ^ (n & 15))) * 8]);
+        x[1] = *reinterpret_cast<const bf16x8 *>(&kcur[((32 + n) * 16 + (c ^ (n & 15))) * 8]);
       };
       read_k(0, ka[0]);
 #pragma unroll
@@ -511,72 +577,64 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
           s1[i] = (uint32_t)(o0 + 32) <= span ? s1[i] : -INFINITY;
         }
       }
-      auto max3 = [](float x, float y, float z) { return fmaxf(fmaxf(x, y), z); };
-      float ma[5], mb[5];
+      // Exponentials against the current reference m first (the previous tile's
+      // P V between them, so it is accumulated at the old reference). The
+      // reference moves only when a score exceeds it by more than kLazyMax, i.e.
+      // when some probability exceeds 2^kLazyMax, and then one of the lane's two
+      // partial sums does too; only then (and while m is unset) is the tile's
+      // maximum formed, O and l rescaled and the exponentials redone.
+      bf16x8 pf[4];
+      float ls0, ls1;
+      if (first)
+        exps(s0, s1, pf, ls0, ls1);
+      else
+        exps_pv(vprev, s0, s1, pf, ls0, ls1);
+      if (__any(fmaxf(ls0, ls1) > kLazyLimit || m == -INFINITY)) {
+        auto max3 = [](float x, float y, float z) { return fmaxf(fmaxf(x, y), z); };
+        float ma[5], mb[5];
 #pragma unroll
-      for (int k = 0; k < 5; ++k) {
-        ma[k] = max3(s0[3 * k], s0[3 * k + 1], s0[3 * k + 2]);
-        mb[k] = max3(s1[3 * k], s1[3 * k + 1], s1[3 * k + 2]);
-      }
-      const float mc = max3(s0[15], s1[15], ma[0]);
-      const float md = max3(ma[1], ma[2], ma[3]), me = max3(ma[4], mb[0], mb[1]), mf = max3(mb[2], mb[3], mb[4]);
-      const float m_use = m == -INFINITY ? 0.f : m;
-      const float mx = pair_max(fmaxf(max3(mc, md, me), mf)) + m_use;
-      if (__any(mx > m + kLazyMax)) {
-        const float m_new = mx > m + kLazyMax ? mx : m;
-        const float corr = m_new == m ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
-        l *= corr;
+        for (int k = 0; k < 5; ++k) {
+          ma[k] = max3(s0[3 * k], s0[3 * k + 1], s0[3 * k + 2]);
+          mb[k] = max3(s1[3 * k], s1[3 * k + 1], s1[3 * k + 2]);
+        }
+        const float mc = max3(s0[15], s1[15], ma[0]);
+        const float md = max3(ma[1], ma[2], ma[3]), me = max3(ma[4], mb[0], mb[1]), mf = max3(mb[2], mb[3], mb[4]);
+        const float m_use = m == -INFINITY ? 0.f : m;
+        const float mx = pair_max(fmaxf(max3(mc, md, me), mf)) + m_use;
+        if (__any(mx > m + kLazyMax)) {
+          const float m_new = mx > m + kLazyMax ? mx : m;
+          const float corr = m_new == m ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+          l *= corr;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+          for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) o[dt][i] *= corr;
-        m = m_new;
-        const float m_use2 = m == -INFINITY ? 0.f : m;
-        const float d = m_use - m_use2;
+            for (int i = 0; i < 16; ++i) o[dt][i] *= corr;
+          m = m_new;
+          const float m_use2 = m == -INFINITY ? 0.f : m;
+          const float d = m_use - m_use2;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          s0[i] += d;
-          s1[i] += d;
-          negm[i] = -m_use2;
+          for (int i = 0; i < 16; ++i) {
+            s0[i] += d;
+            s1[i] += d;
+            negm[i] = -m_use2;
+          }
+          exps(s0, s1, pf, ls0, ls1);
         }
       }
-      float ls0 = 0.f, ls1 = 0.f;
-      bf16x8 pf[4];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p0 = __builtin_amdgcn_exp2f(s0[i]);
-        ls0 += p0;
-        pf[i >> 3][i & 7] = (__bf16)p0;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p1 = __builtin_amdgcn_exp2f(s1[i]);
-        ls1 += p1;
-        pf[2 + (i >> 3)][i & 7] = (__bf16)p1;
-      }
       l += ls0 + ls1;
-      // V^T fragments read one MFMA ahead of their use
-      auto read_v = [&](int x) {
-        const int kk = x / DT, dt = x % DT;
-        const int row = 32 * dt + n, c = 2 * kk + half;
-        return *reinterpret_cast<const bf16x8 *>(&cur.vt[(row * 8 + (c ^ vt_swizzle(row))) * 8]);
-      };
-      bf16x8 va[2];
-      va[0] = read_v(0);
 #pragma unroll
-      for (int x = 0; x < 4 * DT; ++x) {
-        if (x + 1 < 4 * DT) va[(x + 1) & 1] = read_v(x + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        o[x % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[x & 1], pf[x / DT], o[x % DT], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int kk = 0; kk < 4; ++kk) pp[kk] = pf[kk];
     }
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of tile t + 1 landed
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of K(t + 1) and V(t) landed
     __syncthreads();
   };
-  for (int t = 0; t < n_tiles; t += 2) {
-    body(t, smA, smB);
-    if (t + 1 < n_tiles) body(t + 1, smB, smA);
+  if (n_tiles > 0) {
+    body(0, kb0, kb1, vb1, vb0, true);
+    for (int t = 1; t < n_tiles; t += 2) {
+      body(t, kb1, kb0, vb0, vb1, false);
+      if (t + 1 < n_tiles) body(t + 1, kb0, kb1, vb1, vb0, false);
+    }
+    if (active) pv((n_tiles - 1) & 1 ? vb1 : vb0, pp);
   }
 
   const float inv = 1.f / pair_sum(l);
