@@ -773,6 +773,19 @@ def ceilings(args):
             res["lds"]["%s, %d waves/SIMD" % (key, waves_per_simd)] = {
                 "flop": flop, "lds_bytes": lds_bytes, "ms": ms, "TFLOP/s": flop / ms / 1e9,
                 "LDS GB/s": lds_bytes / ms / 1e6, "LDS B/clk/CU at 2.4 GHz": lds_bytes / (ms * 1e-3) / cus / 2.4e9}
+    # a library bf16 GEMM (torch.matmul, i.e. hipBLASLt) of the fused head's product
+    # shape, hidden [4096 x 4096] times head^T [4096 x 151,936]: the rate a plain
+    # product of that shape reaches, for the head's roofline (operands contiguous)
+    res["library_gemm"] = {}
+    g = torch.Generator(device=dev).manual_seed(7)
+    for (mm, kk, nn) in ((4096, 4096, 151936),):
+        a = torch.randn(mm, kk, device=dev, generator=g).to(torch.bfloat16)
+        b = torch.randn(kk, nn, device=dev, generator=g).to(torch.bfloat16)
+        flop = 2.0 * mm * kk * nn
+        ms = timed(lambda: (torch.matmul(a, b), 0)[1], reps=5)
+        res["library_gemm"]["bf16 %dx%dx%d torch.matmul" % (mm, kk, nn)] = {"flop": flop, "ms": ms,
+                                                                           "TFLOP/s": flop / ms / 1e9}
+        del a, b
     best = lambda d, key, pre: max((v[key], k) for k, v in d.items() if k.startswith(pre))
     res["summary"] = {
         "read_GBs": best(res["streams"], "GB/s", "read"),
@@ -781,6 +794,7 @@ def ceilings(args):
         "mfma_bf16_TFLOPs": best(res["mfma"], "TFLOP/s", "bf16"),
         "mfma_lds_1KB_per_mfma_TFLOPs": best(res["lds"], "TFLOP/s", "bf16 32x32x16, 1 KB LDS fragment per 1 "),
         "lds_read_GBs": best(res["lds"], "LDS GB/s", "LDS reads only"),
+        "library_gemm_head_shape_TFLOPs": best(res["library_gemm"], "TFLOP/s", "bf16"),
         "datasheet": {"hbm_GBs": PEAK_HBM_GBS, "bf16_TFLOPs": PEAK_BF16_TFLOPS},
     }
     return res
