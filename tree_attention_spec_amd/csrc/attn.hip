@@ -522,18 +522,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
     for (int i = 0; i < 32; ++i) prob(s0, s1, i, pf, ls0, ls1);
   };
   // the same exponentials with the previous tile's product between them: one
-  // MFMA (its V^T fragment read one ahead), then two exponentials
+  // MFMA (its V^T fragment read three MFMAs ahead), then two exponentials
   auto exps_pv = [&](const __bf16 *vs, const f32x16 &s0, const f32x16 &s1, bf16x8 (&pf)[4], float &ls0,
                      float &ls1) {
     ls0 = 0.f;
     ls1 = 0.f;
-    bf16x8 va[2];
-    va[0] = read_v(vs, 0);
+    constexpr int AH = 3;
+    bf16x8 va[AH + 1];
+#pragma unroll
+    for (int x = 0; x < AH; ++x) va[x] = read_v(vs, x);
 #pragma unroll
     for (int x = 0; x < 4 * DT; ++x) {
-      if (x + 1 < 4 * DT) va[(x + 1) & 1] = read_v(vs, x + 1);
+      if (x + AH < 4 * DT) va[(x + AH) % (AH + 1)] = read_v(vs, x + AH);
       __builtin_amdgcn_sched_barrier(0);
-      o[x % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[x & 1], pp[x / DT], o[x % DT], 0, 0, 0);
+      o[x % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[x % (AH + 1)], pp[x / DT], o[x % DT], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       prob(s0, s1, 2 * x, pf, ls0, ls1);
       prob(s0, s1, 2 * x + 1, pf, ls0, ls1);
