@@ -86,14 +86,28 @@ def sample_rows(lay, k: int, seed: int = 0) -> np.ndarray:
     return np.array(sorted(p for p in picks if 0 <= p < N), dtype=np.int64)
 
 
-def check_grad_rows(g_gpu, g_ref, q, p, rtol=GRAD_RTOL):
-    """Normwise per-row gradient check, skipping near-tie elements. Returns (worst, n_skipped)."""
+S_ULPS = 2.0 ** -20        # absolute error allowed in the float32 S a gradient row is formed from
+
+
+def check_grad_rows(g_gpu, g_ref, q, p, c=None, rtol=GRAD_RTOL):
+    """Normwise per-row gradient check, skipping near-tie elements. Returns (worst, n_skipped).
+
+    The gradient of a row is c q (1[q < p] - S). The kernels form S as a float32 sum of
+    float32 exponentials, so S carries an absolute error of a few float32 ulps of 1, and
+    the in-set coefficient c (1 - S) an absolute error of about |c| times that. When S
+    lies within ~1e-4 of 1 (a draft whose mass sits almost entirely where the teacher is
+    more confident: seen with three-token vocabularies, never on the workloads, where
+    1 - S >= 0.54) the whole row is of that size. With the row coefficients `c` given,
+    a row's scale is therefore at least S_ULPS / rtol * |c| * max_u q_u: the error
+    allowed is at least S_ULPS |c| max q, eight float32 ulps of 1."""
     with np.errstate(divide="ignore", invalid="ignore"):
         lq, lp = np.log(q), np.log(p)
     tie = np.abs(lq - lp) <= TIE_MARGIN
     worst = 0.0
     for r in range(g_ref.shape[0]):
         scale = np.abs(g_ref[r]).max()
+        if c is not None:
+            scale = max(scale, S_ULPS / rtol * abs(float(c[r])) * float(np.max(q[r])))
         err = np.abs(np.where(tie[r], 0.0, g_gpu[r] - g_ref[r])).max()
         rel = err / scale if scale > 0 else err
         worst = max(worst, rel)

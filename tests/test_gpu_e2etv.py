@@ -34,7 +34,7 @@ def _full_compare(case, z, y, inv_norm=None):
     ga, gl, gg = from_device(a), float(l.item()), from_device(g)
     arel = np.max(np.abs(ga - alpha) / np.maximum(alpha, 1e-30))
     lerr = abs(gl - L)
-    gw, nt = check_grad_rows(gg, gref, q, p)
+    gw, nt = check_grad_rows(gg, gref, q, p, c)
     say("  alpha rel %.2e, L %.8f vs %.8f, grad rel %.2e (%d near-ties skipped)" % (arel, gl, L, gw, nt))
     assert arel <= ALPHA_RTOL
     assert lerr <= max(LOSS_RTOL * abs(L), LOSS_ATOL)
@@ -203,7 +203,7 @@ def test_e2etv_workload_full(name):
     _, S, _, _, q, p = e2etv_row_stats_ref(zs.astype(np.float64), ys.astype(np.float64))
     gref = e2etv_grad_ref(q, p, S, c_all[rows])
     gg = from_device(g[torch.from_numpy(rows).cuda()])
-    gw, nt = check_grad_rows(gg, gref, q, p)
+    gw, nt = check_grad_rows(gg, gref, q, p, c_all[rows])
     say("  %d alphas: max rel %.2e; L %.7f vs oracle %.7f; %d grad rows rel %.2e (%d near-ties)"
         % (R, arel, l.item(), L, len(rows), gw, nt))
     assert arel <= ALPHA_RTOL

@@ -37,10 +37,11 @@ def _compare(case, d, V, **kw):
     y = head_logits_ref(case.lay, widen(hidden), widen(head))
     alpha, S, _, _, q, p = e2etv_row_stats_ref(widen(draft), y)
     L = e2etv_loss_ref(alpha, case.lay["step_off"])
-    gref = e2etv_grad_ref(q, p, S, e2etv_coef_ref(alpha, case.lay["step_off"]))
+    c = e2etv_coef_ref(alpha, case.lay["step_off"])
+    gref = e2etv_grad_ref(q, p, S, c)
     ga, gl, gg = from_device(a), float(l.item()), from_device(g)
     arel = np.max(np.abs(ga - alpha) / np.maximum(alpha, 1e-30))
-    gw, nt = check_grad_rows(gg, gref, q, p)
+    gw, nt = check_grad_rows(gg, gref, q, p, c)
     say("  R %d V %d d %d: alpha rel %.2e, L %.8f vs %.8f, grad rel %.2e (%d near-ties)"
         % (case.R, V, d, arel, gl, L, gw, nt))
     assert arel <= ALPHA_RTOL
@@ -154,7 +155,7 @@ def test_head_gqa8b_full():
     _, S, _, _, q, p = e2etv_row_stats_ref(z, y)
     c = e2etv_coef_ref(alpha, case.lay["step_off"])[rows]
     gref = e2etv_grad_ref(q, p, S, c)
-    gw, nt = check_grad_rows(from_device(g[torch.from_numpy(rows).cuda()]), gref, q, p)
+    gw, nt = check_grad_rows(from_device(g[torch.from_numpy(rows).cuda()]), gref, q, p, c)
     say("  %d alphas: max rel %.2e; L %.7f vs oracle %.7f; %d grad rows rel %.2e (%d near-ties)"
         % (R, arel, l.item(), L, len(rows), gw, nt))
     assert arel <= ALPHA_RTOL

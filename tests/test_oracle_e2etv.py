@@ -3,7 +3,7 @@ invariants and central finite differences."""
 import numpy as np
 import pytest
 
-from oracle import e2etv_coef_ref, e2etv_loss_ref, e2etv_ref, e2etv_row_stats_ref
+from oracle import e2etv_coef_ref, e2etv_grad_ref, e2etv_loss_ref, e2etv_ref, e2etv_row_stats_ref
 from specgen import bf16_bits_to_f32, f32_to_bf16_bits, gen_logits, get_config
 
 
@@ -184,3 +184,31 @@ def test_low_precision_inputs_are_promoted():
     p32 /= p32.sum(1, keepdims=True, dtype=np.float32)
     a32 = np.minimum(q32, p32).sum(1, dtype=np.float32)
     np.testing.assert_allclose(a32, a64, rtol=1e-5)
+
+
+def test_gradient_check_bound():
+    """The GPU tests' gradient check (test infrastructure): a few float32 ulps of error in
+    the S a row is formed from pass only through the |c| max q floor, which a real error
+    (a wrong coefficient, a flipped indicator) does not reach."""
+    from _util import check_grad_rows
+    q = np.array([[1 - 2e-5, 1.5e-5, 5e-6]])          # draft almost certain of token 0
+    p = np.array([[1 - 1e-6, 5e-7, 5e-7]])            # teacher more so: only token 0 has q < p
+    S = np.array([q[0, 0]])
+    c = np.array([-0.3])
+    g = e2etv_grad_ref(q, p, S, c)
+    assert np.abs(g).max() < 1e-4 * abs(c[0])          # a row of size |c| (1 - S)
+    g_ulps = e2etv_grad_ref(q, p, S + 4 * 2.0 ** -24, c)   # S off by four float32 ulps of 1
+    assert check_grad_rows(g_ulps, g, q, p)[0] > 1e-4      # fails the plain normwise bound
+    assert check_grad_rows(g_ulps, g, q, p, c)[0] <= 1e-4  # within the floor
+    g_off = e2etv_grad_ref(q, p, S + 1e-5, c)              # S off by ~80 ulps
+    assert check_grad_rows(g_off, g, q, p, c)[0] > 1e-4
+    flip = g.copy()
+    flip[0, 1] = -flip[0, 1] + c[0] * q[0, 1]               # token 1 taken as inside {q < p}
+    assert check_grad_rows(flip, g, q, p, c)[0] > 1e-4
+    q2 = np.array([[0.5, 0.3, 0.2]])
+    p2 = np.array([[0.2, 0.5, 0.3]])
+    S2 = np.array([0.5])
+    g2 = e2etv_grad_ref(q2, p2, S2, c)
+    assert check_grad_rows(e2etv_grad_ref(q2, p2, S2 + 1e-3, c), g2, q2, p2, c)[0] > 1e-4
+    assert check_grad_rows(e2etv_grad_ref(q2, p2, S2, 1.01 * c), g2, q2, p2, c)[0] > 1e-4  # 1% in c
+    assert check_grad_rows(e2etv_grad_ref(q2, p2, S2 + 4 * 2.0 ** -24, c), g2, q2, p2, c)[0] <= 1e-4
