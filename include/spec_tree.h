@@ -128,7 +128,9 @@ typedef struct spec_tree_layout {
   int32_t *step_branch;     /* branch of the step */
   int32_t *step_pred_row;   /* packed row whose output predicts the step's sample */
   int32_t *step_sample_row; /* packed row of the sample y_{b,i}; -1 for the terminal sample */
-  /* library-internal attention schedule [n_attn_items * 8] */
+  /* library-internal attention schedule: n_attn_items query blocks of 8 int32,
+     then the same blocks in groups of four, (n_attn_items + 3) / 4 + 2 * n_trees
+     groups of 4 * 8 int32 */
   int32_t *attn_items;
 } spec_tree_layout;
 

@@ -22,9 +22,40 @@ def _pack_gpu(s):
     return tree, {k: v.cpu().numpy() for k, v in tree.arrays().items()}
 
 
+def _check_groups(lay, it, groups):
+    """The grouped schedule holds every block once, four to a group: consecutive blocks
+    (in row order) of one tree's trunk rows or of one tree's branch rows, empty blocks
+    padding a group's end, groups longest first (by their longest block), then empty
+    groups."""
+    n_trees = len(lay["tree_off"]) - 1
+    assert groups.shape == (((len(it) + 3) // 4 + 2 * n_trees) * 4, 8)
+    g = groups.reshape(-1, 4, 8)
+    seen = []
+    prev_cost = None
+    done = False
+    for grp in g:
+        real = [b for b in grp if b[1] > b[0]]
+        assert all(not b.any() for b in grp[len(real):])          # padding at the end, all zero
+        if not real:
+            done = True
+            continue
+        assert not done                                           # empty groups only at the end
+        for a, b in zip(real, real[1:]):
+            assert b[0] == a[1]                                   # consecutive rows
+            assert b[2] == a[2]                                   # one tree
+            assert (b[5] < b[6]) == (a[5] < a[6])                 # one kind: trunk or branch rows
+        cost = max(int(b[7]) for b in real)
+        assert prev_cost is None or cost <= prev_cost
+        prev_cost = cost
+        seen.extend(tuple(b) for b in real)
+    assert sorted(seen) == sorted(tuple(b) for b in it)
+
+
 def _check_items(lay, items):
     """The attention schedule covers every row once and every visible key of its rows."""
-    it = items.reshape(-1, 8)
+    n_items = lay["_n_attn_items"]
+    it = items[:n_items * 8].reshape(-1, 8)
+    _check_groups(lay, it, items[n_items * 8:].reshape(-1, 8))
     N = lay["n_rows"]
     seen = np.zeros(N, np.int64)
     for q0, q1, tk0, tk1, tfull, bk0, bk1, cost in it:
@@ -52,7 +83,7 @@ def _compare(s, tag):
     assert tree.max_branch_len == ref["max_branch_len"] and tree.max_pos == ref["max_pos"]
     for k in COMPARED:
         assert np.array_equal(got[k], ref[k]), k
-    _check_items(ref, got["attn_items"])
+    _check_items(dict(ref, _n_attn_items=tree.n_attn_items), got["attn_items"])
 
 
 def test_pack_hand_worked(golden):

@@ -82,7 +82,8 @@ LAYOUT_ARRAYS = {
     "step_branch": lambda L: L.n_steps,
     "step_pred_row": lambda L: L.n_steps,
     "step_sample_row": lambda L: L.n_steps,
-    "attn_items": lambda L: L.n_attn_items * 8,
+    # the blocks, then the same blocks in groups of four ((n + 3) // 4 + 2 * n_trees groups)
+    "attn_items": lambda L: (L.n_attn_items + 4 * ((L.n_attn_items + 3) // 4 + 2 * L.n_trees)) * 8,
 }
 
 EXPORTS = ["spec_tree_pack", "spec_tree_attn_fwd", "spec_e2etv_fwd_bwd", "spec_e2etv_fwd_bwd_noalloc",

@@ -373,16 +373,24 @@ constexpr int kWaitVm0 = 0x0F70;
 constexpr float kLazyLimit = 256.f;  // 2^kLazyMax
 static_assert(kLazyMax == 8.f && kLazyLimit == 256.f, "kLazyLimit is 2^kLazyMax");
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4 ? 2 : 1, 2))) void tree_attn_tiled_kernel(
-    const AttnItem *__restrict__ items, int hkv, int group, int hsub,
+// NW query heads of one KV head (one wave each) for NB query blocks: NB = 1 takes
+// one block of the longest-first list; NB > 1 (one or two query heads per KV head)
+// takes NB blocks of a group (consecutive blocks of one tree's trunk or branch
+// rows), so that each staged tile serves NW * NB waves. The tiles then cover the
+// union of the blocks' key ranges, and a wave's own masks discard the keys its
+// rows do not see.
+template <int NW, int NB>
+__global__ __launch_bounds__(NW * NB * 64) __attribute__((amdgpu_waves_per_eu(NW * NB >= 4 ? 2 : 1, 2))) void tree_attn_tiled_kernel(
+    const AttnItem *__restrict__ items, int n_items, int hkv, int group, int hsub,
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ kt, const __bf16 *__restrict__ vt,
     __bf16 *__restrict__ out, const float2 *__restrict__ tab, const int32_t *__restrict__ row_pos,
     const int32_t *__restrict__ row_trunk_hi, const int32_t *__restrict__ row_branch_lo,
     int32_t n_key_tiles, int hq, float sl2) {
   constexpr int D = 128, KS = D / 16, DT = D / 32;
+  constexpr int NWAVE = NW * NB;
   constexpr int PIECES = KT * D * 2 / 1024;  // 1 KB copies per K (or V^T) tile
-  static_assert(PIECES % NW == 0, "each wave issues the same number of copies");
+  static_assert(PIECES % NWAVE == 0, "each wave issues the same number of copies");
+  static_assert(kAttnGroup % NB == 0, "a workgroup takes whole slices of a group");
   // K tiles: slot r*16 + (c ^ (r & 15)) holds dims 8c..8c+7 of key r; V^T tiles:
   // slot d*8 + (c ^ vt_swizzle(d)) holds positions 8c..8c+7 of dim d. Four arrays,
   // so the compiler can see that no fragment read touches a buffer being filled.
@@ -391,26 +399,54 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
   const int bid = blockIdx.x;
   const int g = bid % hkv;
   const int rest = bid / hkv;
-  const int hs = rest % hsub;
-  const AttnItem it = items[rest / hsub];
-
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS copy bases go to M0
   const int n = lane & 31, half = lane >> 5;
-  const int hl = hs * NW + w;
-  const bool active = hl < group;  // wave-uniform
+  const AttnItem *blocks;  // this workgroup's NB blocks
+  int hs = 0;
+  if constexpr (NB == 1) {
+    hs = rest % hsub;
+    blocks = items + rest / hsub;
+  } else {
+    constexpr int PER = kAttnGroup / NB;  // workgroups per group
+    blocks = items + n_items + (int64_t)(rest / PER) * kAttnGroup + (rest % PER) * NB;
+  }
+  const AttnItem it = blocks[w / NW];
+  const bool rows = it.q1 > it.q0;  // false for a group's padding
+  const int hl = hs * NW + w % NW;
+  const bool active = hl < group && rows;  // wave-uniform
   const int h = g * group + (active ? hl : 0);
-  const int qrow = min(it.q0 + n, it.q1 - 1);
+  const int qrow = rows ? min(it.q0 + n, it.q1 - 1) : 0;
 
-  // 64-aligned key tiles: trunk tiles cover [tk0, tk1), then branch tiles [bk0, bk1)
-  const int tt0 = it.tk0 / KT, tt1 = it.tk1 > it.tk0 ? (it.tk1 - 1) / KT + 1 : tt0;
-  const int bt0 = it.bk0 / KT, bt1 = it.bk1 > it.bk0 ? (it.bk1 - 1) / KT + 1 : bt0;
+  // 64-aligned key tiles over the union of the blocks' ranges: trunk tiles cover
+  // [tk0, tk1), then branch tiles [bk0, bk1)
+  int tt0 = 0, tt1 = 0, bt0 = 0, bt1 = 0;
+  {
+    bool any_t = false, any_b = false;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const AttnItem x = blocks[b];
+      if (x.q1 <= x.q0) continue;
+      if (x.tk1 > x.tk0) {
+        const int a0 = x.tk0 / KT, a1 = (x.tk1 - 1) / KT + 1;
+        tt0 = any_t ? min(tt0, a0) : a0;
+        tt1 = any_t ? max(tt1, a1) : a1;
+        any_t = true;
+      }
+      if (x.bk1 > x.bk0) {
+        const int a0 = x.bk0 / KT, a1 = (x.bk1 - 1) / KT + 1;
+        bt0 = any_b ? min(bt0, a0) : a0;
+        bt1 = any_b ? max(bt1, a1) : a1;
+        any_b = true;
+      }
+    }
+  }
   const int n_trunk = tt1 - tt0;
   const int n_tiles = n_trunk + (bt1 - bt0);
   auto tile_index = [&](int t) { return t < n_trunk ? tt0 + t : bt0 + (t - n_trunk); };
 
   // copy the K (or V^T) half of tile t into `dst`: wave w issues the 1 KB pieces
-  // w, w + NW, ... as buffer loads to LDS (the KV head's tiles are one buffer, the
+  // w, w + NWAVE, ... as buffer loads to LDS (the KV head's tiles are one buffer, the
   // piece's byte offset a scalar): outstanding, they leave the LDS counter to the
   // fragment reads, which can then be issued ahead and waited for one at a time
   const uint32_t head_bytes = (uint32_t)n_key_tiles * KT * D * 2;
@@ -420,16 +456,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 4
   auto copy_k = [&](int t, __bf16 *dst) {
     const uint32_t off = (uint32_t)tile_index(t) * (KT * D * 2);
 #pragma unroll
-    for (int i = 0; i < PIECES / NW; ++i) {
-      const int j = w + NW * i;
+    for (int i = 0; i < PIECES / NWAVE; ++i) {
+      const int j = w + NWAVE * i;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst + j * 512, 16, lane_off, off + (uint32_t)j * 1024, 0, 0);
     }
   };
   auto copy_v = [&](int t, __bf16 *dst) {
     const uint32_t off = (uint32_t)tile_index(t) * (KT * D * 2);
 #pragma unroll
-    for (int i = 0; i < PIECES / NW; ++i) {
-      const int j = w + NW * i;
+    for (int i = 0; i < PIECES / NWAVE; ++i) {
+      const int j = w + NWAVE * i;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst + j * 512, 16, lane_off, off + (uint32_t)j * 1024, 0, 0);
     }
   };
@@ -745,18 +781,21 @@ hipError_t launch_bf16_d(const spec_tree_layout &L, int hq, int hkv, const void 
   return launch_bf16<D, 1>(L, hq, hkv, q, kws, v, tab, scale, out, s);
 }
 
-template <int NW>
+template <int NW, int NB>
 hipError_t launch_tiled(const spec_tree_layout &L, int hq, int hkv, const void *q, const void *kt,
                         const void *vt, const float2 *tab, float scale, void *out, hipStream_t s) {
   const int group = hq / hkv;
   const int hsub = (group + NW - 1) / NW;
-  const int64_t nblk = (int64_t)L.n_attn_items * hkv * hsub;
+  if (NB > 1 && hsub != 1) return hipErrorInvalidValue;
+  const int64_t units = NB == 1 ? (int64_t)L.n_attn_items * hsub
+                                : attn_group_count(L.n_attn_items, L.n_trees) * (kAttnGroup / NB);
+  const int64_t nblk = L.n_attn_items > 0 ? units * hkv : 0;
   if (nblk == 0) return hipSuccess;
   if (nblk > INT32_MAX) return hipErrorInvalidValue;
   const int32_t n_key_tiles = (int32_t)((L.n_rows + KT - 1) / KT);
   const float sl2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((tree_attn_tiled_kernel<NW>), dim3((unsigned)nblk), dim3(NW * 64), 0, s,
-                     reinterpret_cast<const AttnItem *>(L.attn_items), hkv, group, hsub,
+  hipLaunchKernelGGL((tree_attn_tiled_kernel<NW, NB>), dim3((unsigned)nblk), dim3(NW * NB * 64), 0, s,
+                     reinterpret_cast<const AttnItem *>(L.attn_items), L.n_attn_items, hkv, group, hsub,
                      static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(kt),
                      static_cast<const __bf16 *>(vt), static_cast<__bf16 *>(out), tab, L.row_pos,
                      L.row_trunk_hi, L.row_branch_lo, n_key_tiles, hq, sl2);
@@ -780,10 +819,10 @@ hipError_t launch_tree_attn_tiled(const spec_tree_layout &L, int32_t hq, int32_t
                                   const void *kt, const void *vt, const float2 *tab, float scale,
                                   void *out, hipStream_t s) {
   const int group = hq / hkv;
-  if (group >= 8) return launch_tiled<8>(L, hq, hkv, q, kt, vt, tab, scale, out, s);
-  if (group >= 3) return launch_tiled<4>(L, hq, hkv, q, kt, vt, tab, scale, out, s);
-  if (group == 2) return launch_tiled<2>(L, hq, hkv, q, kt, vt, tab, scale, out, s);
-  return launch_tiled<1>(L, hq, hkv, q, kt, vt, tab, scale, out, s);
+  if (group >= 8) return launch_tiled<8, 1>(L, hq, hkv, q, kt, vt, tab, scale, out, s);
+  if (group >= 3) return launch_tiled<4, 1>(L, hq, hkv, q, kt, vt, tab, scale, out, s);
+  if (group == 2) return launch_tiled<2, 2>(L, hq, hkv, q, kt, vt, tab, scale, out, s);
+  return launch_tiled<1, 4>(L, hq, hkv, q, kt, vt, tab, scale, out, s);
 }
 
 hipError_t launch_tree_attn(const spec_tree_layout &L, int32_t hq, int32_t hkv, int32_t D,

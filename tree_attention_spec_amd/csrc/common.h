@@ -39,6 +39,17 @@ struct AttnItem {
 static_assert(sizeof(AttnItem) == 32, "AttnItem is 8 int32");
 constexpr int kAttnBlockRows = 32;
 constexpr int kAttnItemInts = 8;
+// The same blocks grouped kAttnGroup at a time, for the tiled attention with one
+// or two query heads per KV head (whose workgroups then take several blocks of one
+// KV head and share each K/V tile among them): a group holds consecutive blocks of
+// one tree's trunk rows or of one tree's branch rows, in row order, padded with
+// empty blocks (q0 == q1 == 0); groups are ordered longest first and padded to
+// attn_group_count groups with empty ones. They follow the n_attn_items blocks in
+// the layout's attn_items.
+constexpr int kAttnGroup = 4;
+__host__ __device__ inline int64_t attn_group_count(int64_t n_items, int64_t n_trees) {
+  return (n_items + kAttnGroup - 1) / kAttnGroup + 2 * n_trees;
+}
 
 // ---------------------------------------------------------------- launchers (per TU)
 hipError_t launch_pack_expand(const spec_tree_layout &L, const int32_t *d_tree_len, int32_t max_trunk,

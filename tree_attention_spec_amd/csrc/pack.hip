@@ -7,6 +7,7 @@
 // [SpecOPD notes page, "Equations"]: the anchor row predicts y_{b,1}, the row
 // of y_{b,i-1} predicts y_{b,i}; y_{b,i} sits at semantic position a_b + i.
 #include <algorithm>
+#include <array>
 #include <cstring>
 #include <cstdarg>
 #include <cstdio>
@@ -109,6 +110,7 @@ struct Plan {
   std::vector<int32_t> tree_off, tree_len, branch_tree, branch_anchor, branch_len, branch_off,
       step_off, branch_order;
   std::vector<AttnItem> items;
+  std::vector<AttnItem> groups;  // attn_group_count groups of kAttnGroup blocks
 };
 
 // Query blocks for the attention kernel, longest first. Trunk blocks take 32
@@ -116,6 +118,21 @@ struct Plan {
 // tree (branches are anchor-sorted, so a block's anchors are close together).
 void plan_attention(Plan &p) {
   const int BR = kAttnBlockRows;
+  // groups of up to kAttnGroup consecutive blocks of one tree's trunk or branch rows
+  std::vector<std::pair<int32_t, std::array<AttnItem, kAttnGroup>>> groups;  // (cost, blocks)
+  size_t run = 0;  // first block of the current run of one tree's trunk or branch rows
+  auto close_run = [&]() {
+    for (size_t i = run; i < p.items.size(); i += kAttnGroup) {
+      std::array<AttnItem, kAttnGroup> g{};
+      int32_t cost = 0;
+      for (size_t j = 0; j < (size_t)kAttnGroup && i + j < p.items.size(); ++j) {
+        g[j] = p.items[i + j];
+        cost = std::max(cost, g[j].cost);
+      }
+      groups.emplace_back(cost, g);
+    }
+    run = p.items.size();
+  };
   int k = 0;  // position in packed branch order
   for (int t = 0; t < p.n_trees; ++t) {
     const int off = p.tree_off[t], T = p.tree_len[t];
@@ -130,6 +147,7 @@ void plan_attention(Plan &p) {
       it.cost = it.tk1 - it.tk0;
       p.items.push_back(it);
     }
+    close_run();
     // branches of tree t in packed order: branch_order[k .. k_end)
     int k_end = k;
     while (k_end < p.B && p.branch_tree[p.branch_order[k_end]] == t) ++k_end;
@@ -156,10 +174,17 @@ void plan_attention(Plan &p) {
       it.cost = (it.tk1 - it.tk0) + (it.bk1 - it.bk0);
       p.items.push_back(it);
     }
+    close_run();
     k = k_end;
   }
   std::stable_sort(p.items.begin(), p.items.end(),
                    [](const AttnItem &a, const AttnItem &b) { return a.cost > b.cost; });
+  std::stable_sort(groups.begin(), groups.end(),
+                   [](const auto &a, const auto &b) { return a.first > b.first; });
+  const int64_t n_groups = attn_group_count((int64_t)p.items.size(), p.n_trees);
+  p.groups.assign((size_t)n_groups * kAttnGroup, AttnItem{});
+  for (size_t i = 0; i < groups.size(); ++i)
+    for (int j = 0; j < kAttnGroup; ++j) p.groups[i * kAttnGroup + j] = groups[i].second[j];
 }
 
 spec_status make_plan(int32_t n_trees, const int32_t *h_trunk_len, const int32_t *h_n_branches,
@@ -264,7 +289,7 @@ Carve carve(const Plan &p) {
   c.off_branch_off = take(p.B);
   c.off_step_off = take(p.B + 1);
   c.off_branch_order = take(p.B);
-  c.off_items = take(p.items.size() * kAttnItemInts);
+  c.off_items = take((p.items.size() + p.groups.size()) * kAttnItemInts);
   c.head_bytes = o;
   for (auto &r : c.off_rows) r = take(p.N);
   for (auto &s : c.off_steps) s = take(p.R);
@@ -342,6 +367,7 @@ extern "C" spec_status spec_tree_pack(int32_t n_trees, const int32_t *h_trunk_le
   put(c.off_step_off, p.step_off.data(), p.step_off.size() * 4);
   put(c.off_branch_order, p.branch_order.data(), p.branch_order.size() * 4);
   put(c.off_items, p.items.data(), p.items.size() * sizeof(AttnItem));
+  put(c.off_items + p.items.size() * sizeof(AttnItem), p.groups.data(), p.groups.size() * sizeof(AttnItem));
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   prof_mark(s, "pack:begin");
